@@ -1,0 +1,232 @@
+"""Benchmark of cascade verify attention on one MI355X.
+
+One step = one cascade_verify_attn call (pass A over every request's prefix,
+pass B over every branch's drafts, LSE merge) over the whole batch of the
+headline workload: B=32 requests, Hq=32, Hkv=8, d=128, prefix L=2000,
+topk=4 branches of S=5 draft tokens, 16-token pages in random physical order.
+Inputs are synthetic (seeded N(0,1) values rounded to bf16) and resident in
+HBM before timing starts.
+
+Protocol: W warm-up steps, then K timed steps.  Before every timed step a
+1 GiB buffer is overwritten (outside the timed interval) so that neither L2
+nor the 256 MB Infinity Cache still holds the 265 MB of KV; each step is
+timed with HIP events on the stream it is launched on.  The same protocol
+times naive expansion (the baseline) on the same inputs.
+
+Prints one JSON line.  value = KV GB/s = cascade KV bytes / step time, where
+cascade KV bytes = sum_i (L_i + sum_j S_j) * Hkv * d * 2 (K and V) * 2 bytes.
+"""
+
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0
+METRIC = "cascade verify attn: KV GB/s (% HBM peak) + query tok/s vs naive expand"
+CSRC = os.path.join(ROOT, "cascade_attention_tree_amd", "csrc")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "verify_headline_traffic.json")
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    for name in sorted(os.listdir(CSRC)):
+        with open(os.path.join(CSRC, name), "rb") as f:
+            h.update(name.encode())
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def workload_bytes(wl):
+    Hkv, d = wl.num_kv_heads, wl.head_dim
+    per_tok = Hkv * d * 2 * 2
+    L = wl.cache_seqlens.astype(np.int64)
+    S = np.diff(wl.branch_qo_indptr.astype(np.int64))
+    req_of = wl.request_of_branch()
+    kv_cascade = int((L.sum() + S.sum()) * per_tok)
+    kv_naive = int(sum(L[req_of[j]] + S[j] for j in range(S.shape[0])) * per_tok)
+    R, Hq = wl.total_rows, wl.num_qo_heads
+    q_bytes = R * Hq * d * 2
+    o_bytes = R * Hq * d * 2 + R * Hq * 4   # bf16 output + fp32 LSE
+    return kv_cascade, kv_naive, q_bytes, o_bytes
+
+
+def time_steps(fn, steps, warmup, flush, torch):
+    """Per-step event times (ms) under the cold protocol, plus the wall time of
+    the K timed steps bracketed by device synchronisation."""
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    starts = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+    ends = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for k in range(steps):
+        flush()
+        starts[k].record(stream)
+        fn()
+        ends[k].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms = np.array([s.elapsed_time(e) for s, e in zip(starts, ends)])
+    return ms, wall
+
+
+def time_warm(fn, steps, torch):
+    """Back-to-back steps without flushing (context only)."""
+    stream = torch.cuda.current_stream()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    a.record(stream)
+    for _ in range(steps):
+        fn()
+    b.record(stream)
+    torch.cuda.synchronize()
+    return a.elapsed_time(b) / steps
+
+
+def cpu_baseline(wl, kv_bytes, budget_s):
+    """The fp64 oracle (pass A, pass B, merge for every row) on the host, on one
+    thread, repeated over the full batch until `budget_s` of work is done."""
+    from oracle import cascade_oracle as O
+    try:
+        from threadpoolctl import threadpool_limits
+        limiter = threadpool_limits(limits=1)
+    except Exception:  # pragma: no cover - threadpoolctl is installed here
+        limiter = None
+    reps, t0 = 0, time.perf_counter()
+    while True:
+        O.cascade(wl)
+        reps += 1
+        if time.perf_counter() - t0 >= budget_s:
+            break
+    dt = (time.perf_counter() - t0) / reps
+    if limiter is not None:
+        limiter.unregister() if hasattr(limiter, "unregister") else None
+    return {"value": kv_bytes / dt / 1e9, "unit": "GB/s", "cores": 1, "kind": "oracle",
+            "sample": f"full headline batch ({wl.total_rows} rows x {wl.num_qo_heads} heads), "
+                      f"{reps} repetitions, {dt:.2f} s each, numpy/BLAS limited to 1 thread",
+            "query_tok_per_s": wl.total_rows / dt}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--only-verify", action="store_true", help="time only the fused verify call")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}); "
+              "the path runs on a single MI355X here and has no multi-GPU leg.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    from cascade_attention_tree_amd import binding as B
+    from cascade_attention_tree_amd import workload as W
+
+    print("bench: generating headline workload", file=sys.stderr, flush=True)
+    wl = W.headline()
+    kv_casc, kv_naive, q_bytes, o_bytes = workload_bytes(wl)
+    x = B.to_device(wl, "cuda")
+    o = torch.empty(wl.q.shape, dtype=torch.bfloat16, device="cuda")
+    lse = torch.empty(wl.q.shape[:2], dtype=torch.float32, device="cuda")
+    ws = B.workspace_for(x)
+    flush_buf = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
+
+    def flush():
+        flush_buf.zero_()
+
+    def verify():
+        B.cascade_verify_attn(x, o=o, lse=lse, workspace=ws)
+
+    def naive():
+        B.naive_expand(x, o=o, lse=lse)
+
+    oa = torch.empty(wl.q.shape, dtype=torch.float32, device="cuda")
+    la = torch.empty(wl.q.shape[:2], dtype=torch.float32, device="cuda")
+    ob, lb = torch.empty_like(oa), torch.empty_like(la)
+
+    def three_call():
+        B.cascade_prefix_attn(x, o_a=oa, lse_a=la, workspace=ws)
+        B.cascade_draft_attn(x, o_b=ob, lse_b=lb)
+        B.merge_state(oa, la, ob, lb, out_dtype=torch.bfloat16, o=o, lse=lse)
+
+    print("bench: timing cascade_verify_attn", file=sys.stderr, flush=True)
+    ms, wall = time_steps(verify, args.steps, args.warmup, flush, torch)
+    t_ms = float(np.mean(ms))
+    warm_ms = time_warm(verify, args.steps, torch)
+    extra = {}
+    if not args.only_verify:
+        print("bench: timing naive_expand", file=sys.stderr, flush=True)
+        ms_n, _ = time_steps(naive, args.steps, args.warmup, flush, torch)
+        print("bench: timing prefix + draft + merge (three calls)", file=sys.stderr, flush=True)
+        ms_3, _ = time_steps(three_call, args.steps, args.warmup, flush, torch)
+        t_naive = float(np.mean(ms_n))
+        extra = {
+            "naive": {"ms": t_naive, "median_ms": float(np.median(ms_n)),
+                      "kv_GBps_algorithmic": kv_naive / (t_naive * 1e-3) / 1e9,
+                      "kv_bytes": kv_naive},
+            "speedup_vs_naive": t_naive / t_ms,
+            "three_call_ms": float(np.mean(ms_3)),
+        }
+    kv_gbs = kv_casc / (t_ms * 1e-3) / 1e9
+    compulsory = kv_casc + q_bytes + o_bytes
+    traffic = None
+    if os.path.exists(TRAFFIC_FILE):
+        with open(TRAFFIC_FILE) as f:
+            tr = json.load(f)
+        if tr.get("kernel_hash") == kernel_source_hash():
+            traffic = tr.get("bytes_per_launch")
+    line = {
+        "metric": METRIC,
+        "value": kv_gbs,
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": t_ms,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": "headline verify: B=32, Hq=32, Hkv=8, d=128, L=2000, topk=4, S=5, "
+                               "page 16, random page table, bf16 in, bf16 out",
+                   "global_batch": wl.batch_size, "query_tokens": wl.total_rows,
+                   "kv_bytes_cascade": kv_casc, "protocol": "cold (1 GiB overwrite between steps)"},
+        "pct_hbm_peak": 100.0 * kv_gbs / HBM_PEAK_GBS,
+        "query_tok_per_s": wl.total_rows / (t_ms * 1e-3),
+        "median_ms": float(np.median(ms)), "p10_ms": float(np.percentile(ms, 10)),
+        "p90_ms": float(np.percentile(ms, 90)),
+        "warm_ms_per_step": warm_ms,
+        "wall_s_timed_region": wall,
+        "roofline": {"bound": "hbm", "achieved": compulsory / (t_ms * 1e-3) / 1e9,
+                     "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": compulsory / (t_ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
+                     "traffic": traffic,
+                     "kernel": "attn_kernel<128, 5, verify> (one launch per step)",
+                     "algorithmic_bytes_per_launch": compulsory},
+    }
+    line.update(extra)
+    if not args.no_cpu_baseline:
+        print("bench: timing the CPU oracle", file=sys.stderr, flush=True)
+        line["cpu_baseline"] = cpu_baseline(wl, kv_casc, args.cpu_seconds)
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,293 @@
+"""ctypes binding of libcascade_attn.so.
+
+Argument marshalling only: every step of the attention path runs in the
+library's HIP kernels.  torch tensors serve as device memory and streams.
+Functions carry the names of the C entry points they call.  The library is
+loaded on first use; if it is missing every call raises.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+from dataclasses import dataclass
+from typing import Optional
+
+import numpy as np
+import torch
+
+from . import workload as _wl
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libcascade_attn.so")
+
+CASCADE_OK = 0
+CASCADE_ERR_NULL = 1
+CASCADE_ERR_SHAPE = 2
+CASCADE_ERR_UNSUPPORTED = 3
+CASCADE_ERR_WORKSPACE = 4
+CASCADE_ERR_HIP = 5
+CASCADE_F32 = 0
+CASCADE_BF16 = 1
+
+EXPORTED = (
+    "cascade_workspace_size", "cascade_prefix_attn", "cascade_draft_attn", "merge_state",
+    "cascade_verify_attn", "naive_expand", "cascade_status_string", "cascade_last_error",
+    "cascade_debug_gather", "cascade_debug_mask", "cascade_device_error",
+)
+
+
+class PagedKV(ctypes.Structure):
+    _fields_ = [("k", ctypes.c_void_p), ("v", ctypes.c_void_p),
+                ("num_pages", ctypes.c_int32), ("page_size", ctypes.c_int32),
+                ("num_kv_heads", ctypes.c_int32), ("head_dim", ctypes.c_int32),
+                ("page_stride", ctypes.c_int64), ("token_stride", ctypes.c_int64),
+                ("head_stride", ctypes.c_int64)]
+
+
+class Query(ctypes.Structure):
+    _fields_ = [("q", ctypes.c_void_p), ("row_stride", ctypes.c_int64),
+                ("head_stride", ctypes.c_int64), ("num_qo_heads", ctypes.c_int32),
+                ("total_rows", ctypes.c_int32), ("sm_scale", ctypes.c_float)]
+
+
+class Tree(ctypes.Structure):
+    _fields_ = [("batch_size", ctypes.c_int32), ("num_branches", ctypes.c_int32),
+                ("page_table", ctypes.c_void_p), ("page_table_stride", ctypes.c_int32),
+                ("cache_seqlens", ctypes.c_void_p), ("req_branch_indptr", ctypes.c_void_p),
+                ("branch_qo_indptr", ctypes.c_void_p), ("draft_page_table", ctypes.c_void_p),
+                ("draft_page_table_stride", ctypes.c_int32), ("draft_start", ctypes.c_void_p),
+                ("max_prefix_len", ctypes.c_int32), ("max_request_rows", ctypes.c_int32),
+                ("max_draft_len", ctypes.c_int32)]
+
+
+class CascadeError(RuntimeError):
+    def __init__(self, status: int, message: str):
+        super().__init__(f"status {status}: {message}")
+        self.status = status
+
+
+_LIB = None
+
+
+def lib() -> ctypes.CDLL:
+    global _LIB
+    if _LIB is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is not built (run __graft_entry__.build())")
+        L = ctypes.CDLL(LIB_PATH)
+        P = ctypes.POINTER
+        st = ctypes.c_int
+        vp = ctypes.c_void_p
+        L.cascade_workspace_size.argtypes = [P(Query), P(PagedKV), P(Tree)]
+        L.cascade_workspace_size.restype = ctypes.c_size_t
+        L.cascade_prefix_attn.argtypes = [P(Query), P(PagedKV), P(Tree), vp, vp, vp, ctypes.c_size_t, vp]
+        L.cascade_prefix_attn.restype = st
+        L.cascade_draft_attn.argtypes = [P(Query), P(PagedKV), P(Tree), vp, vp, vp]
+        L.cascade_draft_attn.restype = st
+        L.merge_state.argtypes = [vp, vp, vp, vp, ctypes.c_int64, ctypes.c_int32, ctypes.c_int32,
+                                  vp, ctypes.c_int, vp, vp]
+        L.merge_state.restype = st
+        L.cascade_verify_attn.argtypes = [P(Query), P(PagedKV), P(Tree), vp, ctypes.c_int, vp, vp,
+                                          ctypes.c_size_t, vp]
+        L.cascade_verify_attn.restype = st
+        L.naive_expand.argtypes = [P(Query), P(PagedKV), P(Tree), vp, ctypes.c_int, vp, vp]
+        L.naive_expand.restype = st
+        L.cascade_status_string.argtypes = [ctypes.c_int]
+        L.cascade_status_string.restype = ctypes.c_char_p
+        L.cascade_last_error.argtypes = []
+        L.cascade_last_error.restype = ctypes.c_char_p
+        L.cascade_debug_gather.argtypes = [P(PagedKV), P(Tree), ctypes.c_int32, ctypes.c_int32,
+                                           ctypes.c_int32, vp, vp, vp]
+        L.cascade_debug_gather.restype = st
+        L.cascade_debug_mask.argtypes = [P(Tree), ctypes.c_int32, vp, ctypes.c_int32, vp]
+        L.cascade_debug_mask.restype = st
+        L.cascade_device_error.argtypes = [P(ctypes.c_int32), ctypes.c_int32]
+        L.cascade_device_error.restype = st
+        _LIB = L
+    return _LIB
+
+
+def _check(status: int) -> None:
+    if status != CASCADE_OK:
+        raise CascadeError(status, lib().cascade_last_error().decode())
+
+
+def _ptr(t: Optional[torch.Tensor]) -> Optional[int]:
+    return None if t is None else t.data_ptr()
+
+
+def _stream(stream) -> Optional[int]:
+    if stream is None:
+        return torch.cuda.current_stream().cuda_stream
+    return stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
+
+
+# ---------------------------------------------------------------------------
+# Device-side inputs
+# ---------------------------------------------------------------------------
+
+@dataclass
+class DeviceInputs:
+    """A workload's arrays on the GPU, plus the C structs that point at them."""
+    q: torch.Tensor            # bf16 [R, Hq, d]
+    k_pool: torch.Tensor       # bf16 [pages, P, Hkv, d]
+    v_pool: torch.Tensor
+    page_table: torch.Tensor   # int32
+    cache_seqlens: torch.Tensor
+    req_branch_indptr: torch.Tensor
+    branch_qo_indptr: torch.Tensor
+    draft_page_table: torch.Tensor
+    draft_start: torch.Tensor
+    query: Query
+    kv: PagedKV
+    tree: Tree
+
+    @property
+    def total_rows(self) -> int:
+        return int(self.query.total_rows)
+
+
+def _bf16_tensor(x: np.ndarray, device) -> torch.Tensor:
+    bits = _wl.bf16_bits(x).view(np.int16)
+    return torch.from_numpy(bits).to(device).view(torch.bfloat16)
+
+
+def make_structs(q, k_pool, v_pool, page_table, cache_seqlens, req_branch_indptr,
+                 branch_qo_indptr, draft_page_table, draft_start, sm_scale,
+                 max_prefix_len, max_request_rows, max_draft_len):
+    R, Hq, d = q.shape
+    num_pages, P, Hkv, _ = k_pool.shape
+    query = Query(q.data_ptr(), q.stride(0), q.stride(1), Hq, R, float(sm_scale))
+    kv = PagedKV(k_pool.data_ptr(), v_pool.data_ptr(), num_pages, P, Hkv, d,
+                 k_pool.stride(0), k_pool.stride(1), k_pool.stride(2))
+    tree = Tree(int(cache_seqlens.shape[0]), int(branch_qo_indptr.shape[0] - 1),
+                page_table.data_ptr(), page_table.stride(0), cache_seqlens.data_ptr(),
+                req_branch_indptr.data_ptr(), branch_qo_indptr.data_ptr(),
+                draft_page_table.data_ptr(), draft_page_table.stride(0),
+                _ptr(draft_start), int(max_prefix_len), int(max_request_rows), int(max_draft_len))
+    return query, kv, tree
+
+
+def to_device(wl: "_wl.Workload", device="cuda") -> DeviceInputs:
+    """Uploads a workload (bf16 values, int32 tables) and builds its C structs."""
+    i32 = lambda a: torch.from_numpy(np.ascontiguousarray(a, np.int32)).to(device)
+    q = _bf16_tensor(wl.q, device)
+    k = _bf16_tensor(wl.k_pool, device)
+    v = _bf16_tensor(wl.v_pool, device)
+    pt, cs, rb = i32(wl.page_table), i32(wl.cache_seqlens), i32(wl.req_branch_indptr)
+    qo, dpt, ds = i32(wl.branch_qo_indptr), i32(wl.draft_page_table), i32(wl.draft_start)
+    query, kv, tree = make_structs(q, k, v, pt, cs, rb, qo, dpt, ds, wl.sm_scale,
+                                   wl.max_prefix_len(), wl.max_rows_per_request(),
+                                   wl.max_draft_len())
+    return DeviceInputs(q, k, v, pt, cs, rb, qo, dpt, ds, query, kv, tree)
+
+
+# ---------------------------------------------------------------------------
+# Entry points
+# ---------------------------------------------------------------------------
+
+def cascade_workspace_size(x: DeviceInputs) -> int:
+    return int(lib().cascade_workspace_size(ctypes.byref(x.query), ctypes.byref(x.kv),
+                                            ctypes.byref(x.tree)))
+
+
+def workspace_for(x: DeviceInputs) -> Optional[torch.Tensor]:
+    n = cascade_workspace_size(x)
+    return torch.empty(n, dtype=torch.uint8, device=x.q.device) if n else None
+
+
+def _out_shape(x: DeviceInputs):
+    R, Hq, d = x.q.shape
+    return (R, Hq, d), (R, Hq)
+
+
+def cascade_prefix_attn(x: DeviceInputs, o_a=None, lse_a=None, workspace=None, stream=None):
+    """Pass A.  Returns (o_A float32 [R, Hq, d], LSE_A float32 [R, Hq])."""
+    so, sl = _out_shape(x)
+    o_a = torch.empty(so, dtype=torch.float32, device=x.q.device) if o_a is None else o_a
+    lse_a = torch.empty(sl, dtype=torch.float32, device=x.q.device) if lse_a is None else lse_a
+    if workspace is None:
+        workspace = workspace_for(x)
+    nbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(lib().cascade_prefix_attn(ctypes.byref(x.query), ctypes.byref(x.kv), ctypes.byref(x.tree),
+                                     o_a.data_ptr(), lse_a.data_ptr(), _ptr(workspace), nbytes,
+                                     _stream(stream)))
+    return o_a, lse_a
+
+
+def cascade_draft_attn(x: DeviceInputs, o_b=None, lse_b=None, stream=None):
+    """Pass B.  Returns (o_B float32 [R, Hq, d], LSE_B float32 [R, Hq])."""
+    so, sl = _out_shape(x)
+    o_b = torch.empty(so, dtype=torch.float32, device=x.q.device) if o_b is None else o_b
+    lse_b = torch.empty(sl, dtype=torch.float32, device=x.q.device) if lse_b is None else lse_b
+    _check(lib().cascade_draft_attn(ctypes.byref(x.query), ctypes.byref(x.kv), ctypes.byref(x.tree),
+                                    o_b.data_ptr(), lse_b.data_ptr(), _stream(stream)))
+    return o_b, lse_b
+
+
+def merge_state(o_a, lse_a, o_b, lse_b, out_dtype=torch.float32, o=None, lse=None, stream=None):
+    """LSE merge of two states; o_* float32 [..., H, d], lse_* float32 [..., H]."""
+    assert o_a.shape == o_b.shape and lse_a.shape == lse_b.shape
+    assert o_a.dtype == torch.float32 and lse_a.dtype == torch.float32
+    for t in (o_a, lse_a, o_b, lse_b):
+        assert t.is_contiguous()
+    H, d = o_a.shape[-2], o_a.shape[-1]
+    rows = o_a.numel() // (H * d)
+    o = torch.empty(o_a.shape, dtype=out_dtype, device=o_a.device) if o is None else o
+    lse = torch.empty(lse_a.shape, dtype=torch.float32, device=o_a.device) if lse is None else lse
+    _check(lib().merge_state(o_a.data_ptr(), lse_a.data_ptr(), o_b.data_ptr(), lse_b.data_ptr(),
+                             rows, H, d, o.data_ptr(),
+                             CASCADE_BF16 if out_dtype == torch.bfloat16 else CASCADE_F32,
+                             _ptr(lse), _stream(stream)))
+    return o, lse
+
+
+def cascade_verify_attn(x: DeviceInputs, out_dtype=torch.float32, o=None, lse=None, workspace=None,
+                        stream=None, want_lse=True):
+    """Pass A + pass B + merge.  Returns (o [R, Hq, d], LSE float32 [R, Hq] or None)."""
+    so, sl = _out_shape(x)
+    o = torch.empty(so, dtype=out_dtype, device=x.q.device) if o is None else o
+    if lse is None and want_lse:
+        lse = torch.empty(sl, dtype=torch.float32, device=x.q.device)
+    if workspace is None:
+        workspace = workspace_for(x)
+    nbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(lib().cascade_verify_attn(ctypes.byref(x.query), ctypes.byref(x.kv), ctypes.byref(x.tree),
+                                     o.data_ptr(),
+                                     CASCADE_BF16 if o.dtype == torch.bfloat16 else CASCADE_F32,
+                                     _ptr(lse), _ptr(workspace), nbytes, _stream(stream)))
+    return o, lse
+
+
+def naive_expand(x: DeviceInputs, out_dtype=torch.float32, o=None, lse=None, stream=None,
+                 want_lse=True):
+    """Baseline: one softmax per branch over prefix + own drafts."""
+    so, sl = _out_shape(x)
+    o = torch.empty(so, dtype=out_dtype, device=x.q.device) if o is None else o
+    if lse is None and want_lse:
+        lse = torch.empty(sl, dtype=torch.float32, device=x.q.device)
+    _check(lib().naive_expand(ctypes.byref(x.query), ctypes.byref(x.kv), ctypes.byref(x.tree),
+                              o.data_ptr(), CASCADE_BF16 if o.dtype == torch.bfloat16 else CASCADE_F32,
+                              _ptr(lse), _stream(stream)))
+    return o, lse
+
+
+def cascade_debug_gather(x: DeviceInputs, which: int, index: int, kv_head: int, count: int):
+    d = x.q.shape[2]
+    k = torch.empty((max(count, 1), d), dtype=torch.bfloat16, device=x.q.device)
+    v = torch.empty_like(k)
+    _check(lib().cascade_debug_gather(ctypes.byref(x.kv), ctypes.byref(x.tree), which, index,
+                                      kv_head, k.data_ptr(), v.data_ptr(), _stream(None)))
+    return k[:count], v[:count]
+
+
+def cascade_debug_mask(x: DeviceInputs, branch: int, rows: int, cols: int):
+    m = torch.zeros((max(rows, 1), max(cols, 1)), dtype=torch.uint8, device=x.q.device)
+    _check(lib().cascade_debug_mask(ctypes.byref(x.tree), branch, m.data_ptr(), cols, _stream(None)))
+    return m[:rows, :cols]
+
+
+def cascade_device_error(clear: bool = True) -> int:
+    v = ctypes.c_int32(0)
+    _check(lib().cascade_device_error(ctypes.byref(v), 1 if clear else 0))
+    return int(v.value)

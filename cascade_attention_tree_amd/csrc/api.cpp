@@ -1,0 +1,473 @@
+// C entry points of libcascade_attn.so: argument checks (all on the host,
+// before any HIP call), launch planning, and dispatch to the kernels.
+#include <hip/hip_runtime_api.h>
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdint>
+#include <cstdio>
+#include <string>
+
+#include "../../include/cascade_attn.h"
+#include "launch.h"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+cascade_status fail(cascade_status s, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return s;
+}
+
+cascade_status hip_fail(hipError_t e, const char* what) {
+  return fail(CASCADE_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+bool is_pow2(int64_t x) { return x > 0 && (x & (x - 1)) == 0; }
+
+int ilog2(int x) {
+  int r = 0;
+  while ((1 << r) < x) ++r;
+  return r;
+}
+
+int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+// Work items wanted per launch before the prefix is split (one per CU of an
+// MI355X), and the bounds on keys per split.
+constexpr int kTargetItems = 256;
+constexpr int kMinSplitKeys = 256;
+constexpr int kMaxSplitKeys = 4096;
+constexpr int kMaxRowBlocks = 5;
+
+struct Plan {
+  int group = 1;
+  int rb = 1;        // 16-row blocks per chunk
+  int n_chunks = 1;  // row chunks per (segment, kv head)
+  int n_splits = 1;  // key splits of the prefix
+  int split_len = 32;
+  int64_t items = 0;  // segments * kv heads * chunks
+};
+
+void plan_rows(Plan& p, int64_t rows_per_segment) {
+  const int64_t blocks = rows_per_segment > 0 ? cdiv(rows_per_segment, 16) : 1;
+  p.rb = (int)(blocks < kMaxRowBlocks ? blocks : kMaxRowBlocks);
+  p.n_chunks = (int)(rows_per_segment > 0 ? cdiv(rows_per_segment, 16 * p.rb) : 1);
+}
+
+void plan_splits(Plan& p, int max_len) {
+  const int len = max_len > 0 ? max_len : 1;
+  int64_t n = 1;
+  if (len > 2 * kMinSplitKeys && p.items < kTargetItems) {
+    n = cdiv(kTargetItems, p.items);
+    const int64_t cap = cdiv(len, kMinSplitKeys);
+    if (n > cap) n = cap;
+  }
+  if (cdiv(len, n) > kMaxSplitKeys) n = cdiv(len, kMaxSplitKeys);
+  p.split_len = (int)(cdiv(cdiv(len, n), 32) * 32);
+  p.n_splits = (int)cdiv(len, p.split_len);
+}
+
+cascade_status check_kv(const cascade_paged_kv* kv) {
+  if (!kv) return fail(CASCADE_ERR_NULL, "kv is NULL");
+  if (!kv->k || !kv->v) return fail(CASCADE_ERR_NULL, "kv->k or kv->v is NULL");
+  if (kv->num_kv_heads <= 0) return fail(CASCADE_ERR_SHAPE, "num_kv_heads must be > 0");
+  if (kv->num_pages <= 0) return fail(CASCADE_ERR_SHAPE, "num_pages must be > 0");
+  if (kv->head_dim != 64 && kv->head_dim != 128)
+    return fail(CASCADE_ERR_UNSUPPORTED, "head_dim %d not supported (64 or 128)", kv->head_dim);
+  if (!is_pow2(kv->page_size) || kv->page_size < 16 || kv->page_size > 4096)
+    return fail(CASCADE_ERR_UNSUPPORTED, "page_size %d not supported (power of two in [16, 4096])",
+                kv->page_size);
+  if (kv->page_stride < 0 || kv->token_stride < 0 || kv->head_stride < 0)
+    return fail(CASCADE_ERR_SHAPE, "kv strides must be >= 0");
+  if (kv->page_stride % 8 || kv->token_stride % 8 || kv->head_stride % 8)
+    return fail(CASCADE_ERR_UNSUPPORTED, "kv strides must be multiples of 8 elements");
+  if (!aligned16(kv->k) || !aligned16(kv->v))
+    return fail(CASCADE_ERR_UNSUPPORTED, "kv->k and kv->v must be 16-byte aligned");
+  return CASCADE_OK;
+}
+
+cascade_status check_query(const cascade_query* q, const cascade_paged_kv* kv) {
+  if (!q) return fail(CASCADE_ERR_NULL, "q is NULL");
+  if (!q->q && q->total_rows > 0) return fail(CASCADE_ERR_NULL, "q->q is NULL");
+  if (q->num_qo_heads <= 0) return fail(CASCADE_ERR_SHAPE, "num_qo_heads must be > 0");
+  if (q->num_qo_heads % kv->num_kv_heads)
+    return fail(CASCADE_ERR_SHAPE, "num_qo_heads (%d) must be a multiple of num_kv_heads (%d)",
+                q->num_qo_heads, kv->num_kv_heads);
+  if (q->total_rows < 0) return fail(CASCADE_ERR_SHAPE, "total_rows must be >= 0");
+  if (q->row_stride < 0 || q->head_stride < 0) return fail(CASCADE_ERR_SHAPE, "q strides must be >= 0");
+  if (q->row_stride % 8 || q->head_stride % 8)
+    return fail(CASCADE_ERR_UNSUPPORTED, "q strides must be multiples of 8 elements");
+  if (q->q && !aligned16(q->q)) return fail(CASCADE_ERR_UNSUPPORTED, "q must be 16-byte aligned");
+  if (!std::isfinite(q->sm_scale)) return fail(CASCADE_ERR_SHAPE, "sm_scale must be finite");
+  return CASCADE_OK;
+}
+
+cascade_status check_tree(const cascade_tree* t, const cascade_paged_kv* kv) {
+  if (!t) return fail(CASCADE_ERR_NULL, "tree is NULL");
+  if (t->batch_size < 0 || t->num_branches < 0) return fail(CASCADE_ERR_SHAPE, "negative batch_size/num_branches");
+  if (t->max_prefix_len < 0 || t->max_request_rows < 0 || t->max_draft_len < 0)
+    return fail(CASCADE_ERR_SHAPE, "negative maxima in tree");
+  if (t->batch_size > 0) {
+    if (!t->cache_seqlens || !t->req_branch_indptr || !t->branch_qo_indptr)
+      return fail(CASCADE_ERR_NULL, "cache_seqlens, req_branch_indptr and branch_qo_indptr are required");
+    if (t->max_prefix_len > 0 && !t->page_table) return fail(CASCADE_ERR_NULL, "page_table is NULL");
+    if (t->num_branches < t->batch_size)
+      return fail(CASCADE_ERR_SHAPE, "num_branches (%d) < batch_size (%d)", t->num_branches, t->batch_size);
+  }
+  if (t->num_branches > 0 && t->batch_size == 0)
+    return fail(CASCADE_ERR_SHAPE, "branches without requests (batch_size = 0)");
+  if (t->num_branches > 0 && !t->draft_page_table) return fail(CASCADE_ERR_NULL, "draft_page_table is NULL");
+  if (t->page_table_stride < 0 || t->draft_page_table_stride < 0)
+    return fail(CASCADE_ERR_SHAPE, "negative block-table stride");
+  if ((int64_t)t->page_table_stride * kv->page_size < t->max_prefix_len)
+    return fail(CASCADE_ERR_SHAPE, "page_table_stride * page_size (%lld) < max_prefix_len (%d)",
+                (long long)t->page_table_stride * kv->page_size, t->max_prefix_len);
+  if (t->num_branches > 0 && t->draft_start == nullptr &&
+      (int64_t)t->draft_page_table_stride * kv->page_size < t->max_draft_len)
+    return fail(CASCADE_ERR_SHAPE, "draft_page_table_stride * page_size < max_draft_len");
+  return CASCADE_OK;
+}
+
+cascade_status check_all(const cascade_query* q, const cascade_paged_kv* kv, const cascade_tree* t) {
+  cascade_status s = check_kv(kv);
+  if (s != CASCADE_OK) return s;
+  if ((s = check_query(q, kv)) != CASCADE_OK) return s;
+  if ((s = check_tree(t, kv)) != CASCADE_OK) return s;
+  return CASCADE_OK;
+}
+
+casc::AttnArgs make_args(const cascade_query* q, const cascade_paged_kv* kv, const cascade_tree* t,
+                         const Plan& p) {
+  casc::AttnArgs a{};
+  a.q = static_cast<const uint16_t*>(q->q);
+  a.q_row_stride = q->row_stride;
+  a.q_head_stride = q->head_stride;
+  a.num_qo_heads = q->num_qo_heads;
+  a.group = p.group;
+  a.total_rows = q->total_rows;
+  a.scale_log2 = q->sm_scale * 1.4426950408889634f;
+  a.kv.k = static_cast<const uint16_t*>(kv->k);
+  a.kv.v = static_cast<const uint16_t*>(kv->v);
+  a.kv.page_stride = kv->page_stride;
+  a.kv.token_stride = kv->token_stride;
+  a.kv.head_stride = kv->head_stride;
+  a.kv.num_pages = kv->num_pages;
+  a.kv.log2_page = ilog2(kv->page_size);
+  a.num_kv_heads = kv->num_kv_heads;
+  a.batch_size = t->batch_size;
+  a.page_table = t->page_table;
+  a.page_table_stride = t->page_table_stride;
+  a.cache_seqlens = t->cache_seqlens;
+  a.req_branch_indptr = t->req_branch_indptr;
+  a.branch_qo_indptr = t->branch_qo_indptr;
+  a.draft_page_table = t->draft_page_table;
+  a.draft_page_table_stride = t->draft_page_table_stride;
+  a.draft_start = t->draft_start;
+  a.n_chunks = p.n_chunks;
+  a.grid_splits = 1;
+  a.n_splits = p.n_splits;
+  a.split_len = p.split_len;
+  return a;
+}
+
+// Plan of the per-request launches (pass A, pass B, verify).
+Plan plan_request(const cascade_query* q, const cascade_paged_kv* kv, const cascade_tree* t) {
+  Plan p;
+  p.group = q->num_qo_heads / kv->num_kv_heads;
+  plan_rows(p, (int64_t)t->max_request_rows * p.group);
+  p.items = (int64_t)t->batch_size * kv->num_kv_heads * p.n_chunks;
+  plan_splits(p, t->max_prefix_len);
+  return p;
+}
+
+struct WsLayout {
+  size_t bytes = 0;
+  size_t lse_off = 0;
+};
+
+WsLayout ws_layout(const cascade_query* q, const cascade_paged_kv* kv, const Plan& p) {
+  WsLayout w;
+  if (p.n_splits <= 1) return w;
+  const size_t plane = (size_t)q->total_rows * q->num_qo_heads;
+  const size_t o_bytes = (size_t)p.n_splits * plane * kv->head_dim * sizeof(float);
+  w.lse_off = (o_bytes + 255) / 256 * 256;
+  w.bytes = w.lse_off + (size_t)p.n_splits * plane * sizeof(float);
+  return w;
+}
+
+hipError_t launch(int mode, int head_dim, int rb, const casc::AttnArgs& a, int64_t grid, hipStream_t s) {
+  if (grid <= 0) return hipSuccess;
+  if (head_dim == 64) return casc::launch_attn_d64(mode, rb, a, (int)grid, s);
+  return casc::launch_attn_d128(mode, rb, a, (int)grid, s);
+}
+
+cascade_status check_grid(int64_t grid) {
+  if (grid > INT32_MAX) return fail(CASCADE_ERR_SHAPE, "launch too large (%lld work items)", (long long)grid);
+  return CASCADE_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* cascade_status_string(cascade_status s) {
+  switch (s) {
+    case CASCADE_OK: return "ok";
+    case CASCADE_ERR_NULL: return "null pointer";
+    case CASCADE_ERR_SHAPE: return "inconsistent shape";
+    case CASCADE_ERR_UNSUPPORTED: return "unsupported configuration";
+    case CASCADE_ERR_WORKSPACE: return "workspace too small";
+    case CASCADE_ERR_HIP: return "HIP runtime error";
+  }
+  return "unknown status";
+}
+
+const char* cascade_last_error(void) { return g_last_error.c_str(); }
+
+size_t cascade_workspace_size(const cascade_query* q, const cascade_paged_kv* kv, const cascade_tree* t) {
+  if (check_all(q, kv, t) != CASCADE_OK) return 0;
+  return ws_layout(q, kv, plan_request(q, kv, t)).bytes;
+}
+
+cascade_status cascade_prefix_attn(const cascade_query* q, const cascade_paged_kv* kv,
+                                   const cascade_tree* t, float* o_a, float* lse_a, void* ws,
+                                   size_t ws_bytes, void* stream) {
+  cascade_status st = check_all(q, kv, t);
+  if (st != CASCADE_OK) return st;
+  if (q->total_rows > 0 && (!o_a || !lse_a)) return fail(CASCADE_ERR_NULL, "o_a and lse_a are required");
+  if (o_a && !aligned16(o_a)) return fail(CASCADE_ERR_UNSUPPORTED, "o_a must be 16-byte aligned");
+  const Plan p = plan_request(q, kv, t);
+  const WsLayout wl = ws_layout(q, kv, p);
+  if (wl.bytes > 0 && (!ws || ws_bytes < wl.bytes))
+    return fail(CASCADE_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", wl.bytes, ws ? ws_bytes : 0);
+  if (ws && !aligned16(ws)) return fail(CASCADE_ERR_UNSUPPORTED, "workspace must be 16-byte aligned");
+  if ((st = check_grid(p.items * p.n_splits)) != CASCADE_OK) return st;
+  if (q->total_rows == 0 || t->batch_size == 0) return CASCADE_OK;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  casc::AttnArgs a = make_args(q, kv, t, p);
+  a.o = o_a;
+  a.o_bf16 = 0;
+  a.lse = lse_a;
+  hipError_t e;
+  if (p.n_splits > 1) {
+    a.ws_o = static_cast<float*>(ws);
+    a.ws_lse = reinterpret_cast<float*>(static_cast<char*>(ws) + wl.lse_off);
+    a.grid_splits = p.n_splits;
+    e = launch(casc::kModePrefix, kv->head_dim, p.rb, a, p.items * p.n_splits, s);
+    if (e != hipSuccess) return hip_fail(e, "prefix pass launch");
+    a.grid_splits = 1;
+    e = launch(casc::kModePrefixFinish, kv->head_dim, p.rb, a, p.items, s);
+    if (e != hipSuccess) return hip_fail(e, "prefix split merge launch");
+  } else {
+    e = launch(casc::kModePrefix, kv->head_dim, p.rb, a, p.items, s);
+    if (e != hipSuccess) return hip_fail(e, "prefix pass launch");
+  }
+  return CASCADE_OK;
+}
+
+cascade_status cascade_draft_attn(const cascade_query* q, const cascade_paged_kv* kv,
+                                  const cascade_tree* t, float* o_b, float* lse_b, void* stream) {
+  cascade_status st = check_all(q, kv, t);
+  if (st != CASCADE_OK) return st;
+  if (q->total_rows > 0 && (!o_b || !lse_b)) return fail(CASCADE_ERR_NULL, "o_b and lse_b are required");
+  if (o_b && !aligned16(o_b)) return fail(CASCADE_ERR_UNSUPPORTED, "o_b must be 16-byte aligned");
+  Plan p = plan_request(q, kv, t);
+  p.n_splits = 1;
+  if ((st = check_grid(p.items)) != CASCADE_OK) return st;
+  if (q->total_rows == 0 || t->batch_size == 0) return CASCADE_OK;
+  casc::AttnArgs a = make_args(q, kv, t, p);
+  a.o = o_b;
+  a.o_bf16 = 0;
+  a.lse = lse_b;
+  const hipError_t e = launch(casc::kModeDraft, kv->head_dim, p.rb, a, p.items, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "draft pass launch");
+  return CASCADE_OK;
+}
+
+cascade_status merge_state(const float* o_a, const float* lse_a, const float* o_b, const float* lse_b,
+                           int64_t num_rows, int32_t num_heads, int32_t head_dim, void* o,
+                           cascade_dtype o_dtype, float* lse, void* stream) {
+  if (num_rows < 0 || num_heads < 0 || head_dim <= 0) return fail(CASCADE_ERR_SHAPE, "bad merge shape");
+  if (head_dim % 4) return fail(CASCADE_ERR_UNSUPPORTED, "head_dim must be a multiple of 4");
+  if (o_dtype != CASCADE_F32 && o_dtype != CASCADE_BF16) return fail(CASCADE_ERR_UNSUPPORTED, "bad o_dtype");
+  if (num_rows == 0 || num_heads == 0) return CASCADE_OK;
+  if (!o_a || !lse_a || !o_b || !lse_b || !o) return fail(CASCADE_ERR_NULL, "merge_state input or output is NULL");
+  if (!aligned16(o_a) || !aligned16(o_b) || !aligned16(o))
+    return fail(CASCADE_ERR_UNSUPPORTED, "o_a, o_b and o must be 16-byte aligned");
+  casc::MergeArgs a{};
+  a.o_a = o_a;
+  a.lse_a = lse_a;
+  a.o_b = o_b;
+  a.lse_b = lse_b;
+  a.rows = num_rows * num_heads;
+  a.head_dim = head_dim;
+  a.o = o;
+  a.o_bf16 = o_dtype == CASCADE_BF16;
+  a.lse = lse;
+  const hipError_t e = casc::launch_merge(a, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "merge_state launch");
+  return CASCADE_OK;
+}
+
+cascade_status cascade_verify_attn(const cascade_query* q, const cascade_paged_kv* kv,
+                                   const cascade_tree* t, void* o, cascade_dtype o_dtype, float* lse,
+                                   void* ws, size_t ws_bytes, void* stream) {
+  cascade_status st = check_all(q, kv, t);
+  if (st != CASCADE_OK) return st;
+  if (o_dtype != CASCADE_F32 && o_dtype != CASCADE_BF16) return fail(CASCADE_ERR_UNSUPPORTED, "bad o_dtype");
+  if (q->total_rows > 0 && !o) return fail(CASCADE_ERR_NULL, "o is NULL");
+  if (o && !aligned16(o)) return fail(CASCADE_ERR_UNSUPPORTED, "o must be 16-byte aligned");
+  const Plan p = plan_request(q, kv, t);
+  const WsLayout wl = ws_layout(q, kv, p);
+  if (wl.bytes > 0 && (!ws || ws_bytes < wl.bytes))
+    return fail(CASCADE_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", wl.bytes, ws ? ws_bytes : 0);
+  if (ws && !aligned16(ws)) return fail(CASCADE_ERR_UNSUPPORTED, "workspace must be 16-byte aligned");
+  if ((st = check_grid(p.items * p.n_splits)) != CASCADE_OK) return st;
+  if (q->total_rows == 0 || t->batch_size == 0) return CASCADE_OK;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  casc::AttnArgs a = make_args(q, kv, t, p);
+  a.o = o;
+  a.o_bf16 = o_dtype == CASCADE_BF16;
+  a.lse = lse;
+  hipError_t e;
+  if (p.n_splits > 1) {
+    a.ws_o = static_cast<float*>(ws);
+    a.ws_lse = reinterpret_cast<float*>(static_cast<char*>(ws) + wl.lse_off);
+    a.grid_splits = p.n_splits;
+    e = launch(casc::kModeVerify, kv->head_dim, p.rb, a, p.items * p.n_splits, s);
+    if (e != hipSuccess) return hip_fail(e, "verify prefix launch");
+    a.grid_splits = 1;
+    e = launch(casc::kModeVerifyFinish, kv->head_dim, p.rb, a, p.items, s);
+    if (e != hipSuccess) return hip_fail(e, "verify merge launch");
+  } else {
+    e = launch(casc::kModeVerify, kv->head_dim, p.rb, a, p.items, s);
+    if (e != hipSuccess) return hip_fail(e, "verify launch");
+  }
+  return CASCADE_OK;
+}
+
+cascade_status naive_expand(const cascade_query* q, const cascade_paged_kv* kv, const cascade_tree* t,
+                            void* o, cascade_dtype o_dtype, float* lse, void* stream) {
+  cascade_status st = check_all(q, kv, t);
+  if (st != CASCADE_OK) return st;
+  if (o_dtype != CASCADE_F32 && o_dtype != CASCADE_BF16) return fail(CASCADE_ERR_UNSUPPORTED, "bad o_dtype");
+  if (q->total_rows > 0 && !o) return fail(CASCADE_ERR_NULL, "o is NULL");
+  if (o && !aligned16(o)) return fail(CASCADE_ERR_UNSUPPORTED, "o must be 16-byte aligned");
+  Plan p;
+  p.group = q->num_qo_heads / kv->num_kv_heads;
+  plan_rows(p, (int64_t)t->max_draft_len * p.group);
+  p.items = (int64_t)t->num_branches * kv->num_kv_heads * p.n_chunks;
+  p.n_splits = 1;
+  p.split_len = 32;
+  if ((st = check_grid(p.items)) != CASCADE_OK) return st;
+  if (q->total_rows == 0 || t->num_branches == 0) return CASCADE_OK;
+  casc::AttnArgs a = make_args(q, kv, t, p);
+  a.o = o;
+  a.o_bf16 = o_dtype == CASCADE_BF16;
+  a.lse = lse;
+  const hipError_t e = launch(casc::kModeNaive, kv->head_dim, p.rb, a, p.items, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "naive expand launch");
+  return CASCADE_OK;
+}
+
+cascade_status cascade_debug_gather(const cascade_paged_kv* kv, const cascade_tree* t, int32_t which,
+                                    int32_t index, int32_t kv_head, void* k_out, void* v_out, void* stream) {
+  cascade_status st = check_kv(kv);
+  if (st != CASCADE_OK) return st;
+  if (!t) return fail(CASCADE_ERR_NULL, "tree is NULL");
+  if (which != 0 && which != 1) return fail(CASCADE_ERR_SHAPE, "which must be 0 (prefix) or 1 (draft)");
+  if (kv_head < 0 || kv_head >= kv->num_kv_heads) return fail(CASCADE_ERR_SHAPE, "kv_head out of range");
+  if (which == 0 && (index < 0 || index >= t->batch_size)) return fail(CASCADE_ERR_SHAPE, "request out of range");
+  if (which == 1 && (index < 0 || index >= t->num_branches)) return fail(CASCADE_ERR_SHAPE, "branch out of range");
+  if (which == 0 && (!t->page_table || !t->cache_seqlens)) return fail(CASCADE_ERR_NULL, "page_table is NULL");
+  if (which == 1 && (!t->draft_page_table || !t->branch_qo_indptr)) return fail(CASCADE_ERR_NULL, "draft tables are NULL");
+  if (!k_out || !v_out) return fail(CASCADE_ERR_NULL, "k_out / v_out is NULL");
+  if (!aligned16(k_out) || !aligned16(v_out)) return fail(CASCADE_ERR_UNSUPPORTED, "outputs must be 16-byte aligned");
+  // The token count lives on the device: fetch it (this hook synchronises).
+  int32_t count = 0;
+  hipError_t e;
+  if (which == 0) {
+    e = hipMemcpy(&count, t->cache_seqlens + index, sizeof(int32_t), hipMemcpyDeviceToHost);
+  } else {
+    int32_t ends[2];
+    e = hipMemcpy(ends, t->branch_qo_indptr + index, 2 * sizeof(int32_t), hipMemcpyDeviceToHost);
+    count = ends[1] - ends[0];
+  }
+  if (e != hipSuccess) return hip_fail(e, "reading sequence length");
+  if (count < 0) return fail(CASCADE_ERR_SHAPE, "negative sequence length");
+  casc::DebugArgs a{};
+  a.kv.k = static_cast<const uint16_t*>(kv->k);
+  a.kv.v = static_cast<const uint16_t*>(kv->v);
+  a.kv.page_stride = kv->page_stride;
+  a.kv.token_stride = kv->token_stride;
+  a.kv.head_stride = kv->head_stride;
+  a.kv.num_pages = kv->num_pages;
+  a.kv.log2_page = ilog2(kv->page_size);
+  a.head_dim = kv->head_dim;
+  a.batch_size = t->batch_size;
+  a.page_table = t->page_table;
+  a.page_table_stride = t->page_table_stride;
+  a.cache_seqlens = t->cache_seqlens;
+  a.req_branch_indptr = t->req_branch_indptr;
+  a.branch_qo_indptr = t->branch_qo_indptr;
+  a.draft_page_table = t->draft_page_table;
+  a.draft_page_table_stride = t->draft_page_table_stride;
+  a.draft_start = t->draft_start;
+  a.which = which;
+  a.index = index;
+  a.kv_head = kv_head;
+  a.count = count;
+  a.k_out = static_cast<uint16_t*>(k_out);
+  a.v_out = static_cast<uint16_t*>(v_out);
+  e = casc::launch_debug_gather(a, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "debug gather launch");
+  return CASCADE_OK;
+}
+
+cascade_status cascade_debug_mask(const cascade_tree* t, int32_t branch, uint8_t* mask_out,
+                                  int32_t mask_cols, void* stream) {
+  if (!t) return fail(CASCADE_ERR_NULL, "tree is NULL");
+  if (branch < 0 || branch >= t->num_branches) return fail(CASCADE_ERR_SHAPE, "branch out of range");
+  if (!t->cache_seqlens || !t->req_branch_indptr || !t->branch_qo_indptr)
+    return fail(CASCADE_ERR_NULL, "tree arrays are NULL");
+  if (!mask_out) return fail(CASCADE_ERR_NULL, "mask_out is NULL");
+  if (mask_cols < 0) return fail(CASCADE_ERR_SHAPE, "mask_cols must be >= 0");
+  int32_t ends[2];
+  hipError_t e = hipMemcpy(ends, t->branch_qo_indptr + branch, 2 * sizeof(int32_t), hipMemcpyDeviceToHost);
+  if (e != hipSuccess) return hip_fail(e, "reading branch length");
+  casc::DebugArgs a{};
+  a.batch_size = t->batch_size;
+  a.cache_seqlens = t->cache_seqlens;
+  a.req_branch_indptr = t->req_branch_indptr;
+  a.branch_qo_indptr = t->branch_qo_indptr;
+  a.index = branch;
+  a.count = ends[1] - ends[0];
+  a.cols = mask_cols;
+  a.mask_out = mask_out;
+  e = casc::launch_debug_mask(a, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "debug mask launch");
+  return CASCADE_OK;
+}
+
+cascade_status cascade_device_error(int32_t* flag_out, int32_t clear) {
+  if (!flag_out) return fail(CASCADE_ERR_NULL, "flag_out is NULL");
+  hipError_t e = hipDeviceSynchronize();
+  if (e != hipSuccess) return hip_fail(e, "synchronise");
+  int v64 = 0, v128 = 0, vs = 0;
+  if ((e = casc::read_error_d64(&v64, clear)) != hipSuccess) return hip_fail(e, "read error word");
+  if ((e = casc::read_error_d128(&v128, clear)) != hipSuccess) return hip_fail(e, "read error word");
+  if ((e = casc::read_error_small(&vs, clear)) != hipSuccess) return hip_fail(e, "read error word");
+  *flag_out = v64 | v128 | vs;
+  return CASCADE_OK;
+}
+
+}  // extern "C"

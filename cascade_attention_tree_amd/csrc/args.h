@@ -1,0 +1,96 @@
+// Argument blocks passed by value from the host launchers to the kernels.
+// Plain data only: included by both the HIP kernel sources and the host API.
+#pragma once
+
+#include <stdint.h>
+
+namespace casc {
+
+// One layer's paged K and V.  Element offsets: page*page_stride +
+// slot*token_stride + kv_head*head_stride + channel.
+struct KvView {
+  const uint16_t* k;
+  const uint16_t* v;
+  int64_t page_stride;
+  int64_t token_stride;
+  int64_t head_stride;
+  int32_t num_pages;
+  int32_t log2_page;
+};
+
+enum AttnMode : int {
+  kModePrefix = 0,        // pass A: unsplit -> (o_A, LSE_A); split -> partial states
+  kModeDraft = 1,         // pass B -> (o_B, LSE_B)
+  kModeVerify = 2,        // pass A; unsplit: + pass B + merge -> (o, LSE); split -> partials
+  kModeNaive = 3,         // naive expansion, one softmax per branch -> (o, LSE)
+  kModePrefixFinish = 4,  // merge split partials -> (o_A, LSE_A)
+  kModeVerifyFinish = 5,  // merge split partials, pass B, merge -> (o, LSE)
+};
+
+struct AttnArgs {
+  const uint16_t* q;
+  int64_t q_row_stride;
+  int64_t q_head_stride;
+  int32_t num_qo_heads;
+  int32_t group;
+  int32_t total_rows;
+  float scale_log2;  // sm_scale * log2(e): scores are kept in base 2
+  KvView kv;
+  int32_t num_kv_heads;
+  int32_t batch_size;
+  const int32_t* page_table;
+  int32_t page_table_stride;
+  const int32_t* cache_seqlens;
+  const int32_t* req_branch_indptr;
+  const int32_t* branch_qo_indptr;
+  const int32_t* draft_page_table;
+  int32_t draft_page_table_stride;
+  const int32_t* draft_start;
+  int32_t n_chunks;     // row chunks per segment and kv head
+  int32_t grid_splits;  // key splits in this launch's grid
+  int32_t n_splits;     // key splits of the prefix (partials in the workspace)
+  int32_t split_len;    // keys per split (multiple of 32)
+  void* o;
+  int32_t o_bf16;
+  float* lse;
+  float* ws_o;    // [n_splits, total_rows, Hq, D] normalised partial outputs
+  float* ws_lse;  // [n_splits, total_rows, Hq] partial LSE, base 2
+};
+
+// Elementwise merge of two attention states (the standalone merge_state).
+struct MergeArgs {
+  const float* o_a;
+  const float* lse_a;
+  const float* o_b;
+  const float* lse_b;
+  int64_t rows;  // num_rows * num_heads
+  int32_t head_dim;
+  void* o;
+  int32_t o_bf16;
+  float* lse;
+};
+
+// Debug hooks: gather one sequence's K/V, or one branch's visibility mask.
+struct DebugArgs {
+  KvView kv;
+  int32_t head_dim;
+  int32_t batch_size;
+  const int32_t* page_table;
+  int32_t page_table_stride;
+  const int32_t* cache_seqlens;
+  const int32_t* req_branch_indptr;
+  const int32_t* branch_qo_indptr;
+  const int32_t* draft_page_table;
+  int32_t draft_page_table_stride;
+  const int32_t* draft_start;
+  int32_t which;
+  int32_t index;
+  int32_t kv_head;
+  int32_t count;  // rows to produce (tokens for gather, query rows for the mask)
+  int32_t cols;   // mask columns
+  uint16_t* k_out;
+  uint16_t* v_out;
+  uint8_t* mask_out;
+};
+
+}  // namespace casc

@@ -1,0 +1,102 @@
+// Device-side helpers shared by every kernel of the library: vector types,
+// the paged-KV address computation, the draft-key visibility rule, and the
+// sticky bounds flag.  Built for gfx950 (CDNA4, wave64) only.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "args.h"
+
+namespace casc {
+
+typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8;
+typedef __attribute__((ext_vector_type(4))) float f32x4;
+typedef __attribute__((ext_vector_type(4))) unsigned int u32x4;
+typedef __attribute__((ext_vector_type(2))) unsigned int u32x2;
+
+// Sticky error word of this translation unit (bit flags below); read and
+// cleared by the host through hipMemcpyFromSymbol / hipMemcpyToSymbol.
+static __device__ int g_device_error;
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+constexpr float kNegInf = -__builtin_inff();
+
+// Bit flags of the sticky device error word.
+constexpr int kErrPage = 1;   // a block-table entry outside [0, num_pages)
+constexpr int kErrRow = 2;    // a query row outside [0, total_rows)
+constexpr int kErrLen = 4;    // a sequence longer than its block-table row can hold
+
+
+// Logical slot `slot` of block-table row `table_row` for kv head `g`: the page
+// is table_row[slot / P] and the token sits at slot % P inside it (paged KV,
+// block table mapping logical to physical pages).  Returns -1 when the page id
+// lies outside the pool.
+__device__ __forceinline__ int64_t paged_offset(const KvView& kv, const int32_t* table_row,
+                                                int32_t slot, int32_t g) {
+  const int32_t page = table_row[slot >> kv.log2_page];
+  if ((uint32_t)page >= (uint32_t)kv.num_pages) return -1;
+  const int32_t in_page = slot & ((1 << kv.log2_page) - 1);
+  return (int64_t)page * kv.page_stride + (int64_t)in_page * kv.token_stride +
+         (int64_t)g * kv.head_stride;
+}
+
+// Branch j in [jb, je) whose query rows contain global row `row`
+// (branch_qo_indptr is non-decreasing).
+__device__ __forceinline__ int branch_of_row(const int32_t* qo, int jb, int je, int row) {
+  int lo = jb, hi = je - 1;
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if (qo[mid] <= row) lo = mid; else hi = mid - 1;
+  }
+  return lo;
+}
+
+// Request i with req_branch_indptr[i] <= j < req_branch_indptr[i+1].
+__device__ __forceinline__ int request_of_branch(const int32_t* rb, int batch, int j) {
+  int lo = 0, hi = batch - 1;
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if (rb[mid] <= j) lo = mid; else hi = mid - 1;
+  }
+  return lo;
+}
+
+// Draft-key visibility (tree attention restricted to chains: a node sees its
+// ancestors and itself).  Tokens are numbered within one row segment; a query
+// at token t whose branch starts at token bs sees draft key token kt iff kt
+// lies in its own branch at or before it.
+__device__ __forceinline__ bool draft_visible(int t, int bs, int kt) {
+  return kt >= bs && kt <= t;
+}
+
+// Physical offset of draft token `kt` (numbered from the first row of branch
+// jb) of kv head g.  Branch j's token u is at logical slot draft_start[j] + u
+// of draft block-table row j (dstride entries).  -1 when the slot lies past
+// the row or the page id is outside the pool.
+__device__ __forceinline__ int64_t draft_offset(const KvView& kv, const int32_t* qo,
+                                                const int32_t* dpt, int32_t dstride,
+                                                const int32_t* dstart, int jb, int je,
+                                                int kt, int g) {
+  const int row = qo[jb] + kt;
+  const int j = branch_of_row(qo, jb, je, row);
+  const int u = row - qo[j];
+  const int slot = (dstart ? dstart[j] : 0) + u;
+  if (slot < 0 || (slot >> kv.log2_page) >= dstride) return -1;
+  return paged_offset(kv, dpt + (int64_t)j * dstride, slot, g);
+}
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+__device__ __forceinline__ float fast_log2(float x) { return __builtin_amdgcn_logf(x); }
+
+// Round-to-nearest-even float -> bf16 bits.
+__device__ __forceinline__ uint16_t f32_to_bf16_bits(float f) {
+  return __builtin_bit_cast(uint16_t, (__bf16)f);
+}
+
+__device__ __forceinline__ unsigned int pack_bf16x2(float lo, float hi) {
+  return (unsigned int)f32_to_bf16_bits(lo) | ((unsigned int)f32_to_bf16_bits(hi) << 16);
+}
+
+}  // namespace casc

@@ -1,0 +1,23 @@
+// Host-side launch interface between the C API and the kernel translation units.
+#pragma once
+
+#include <hip/hip_runtime_api.h>
+
+#include "args.h"
+
+namespace casc {
+
+// Attention kernels: head_dim 64 or 128, rb = 16-row blocks per chunk (1..5).
+hipError_t launch_attn_d64(int mode, int rb, const AttnArgs& a, int grid, hipStream_t s);
+hipError_t launch_attn_d128(int mode, int rb, const AttnArgs& a, int grid, hipStream_t s);
+
+hipError_t launch_merge(const MergeArgs& a, hipStream_t s);
+hipError_t launch_debug_gather(const DebugArgs& a, hipStream_t s);
+hipError_t launch_debug_mask(const DebugArgs& a, hipStream_t s);
+
+// Sticky device error words of each translation unit (read, optionally clear).
+hipError_t read_error_d64(int* v, int clear);
+hipError_t read_error_d128(int* v, int clear);
+hipError_t read_error_small(int* v, int clear);
+
+}  // namespace casc

@@ -1,0 +1,128 @@
+// The standalone merge of two attention states, and the debug hooks that
+// expose the paged gather and the draft mask exactly as the attention kernels
+// compute them (same helpers from device_common.h).
+#include "device_common.h"
+#include "launch.h"
+
+namespace casc {
+
+// merge_state: for each (row, head), with natural-log LSEs,
+//   LSE = ln(e^LSE_A + e^LSE_B), o = e^(LSE_A - LSE) o_A + e^(LSE_B - LSE) o_B.
+// Evaluated in base 2 after scaling the LSEs by log2(e), the larger one
+// factored out.  One thread per 4 channels of one (row, head).
+__global__ void __launch_bounds__(256) merge_state_kernel(const MergeArgs a) {
+  const int d4 = a.head_dim >> 2;
+  const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (idx >= a.rows * d4) return;
+  const int64_t r = idx / d4;
+  const int c = (int)(idx - r * d4) * 4;
+  const float la = a.lse_a[r] * kLog2e;
+  const float lb = a.lse_b[r] * kLog2e;
+  const float mx = fmaxf(la, lb);
+  f32x4 out = {0.f, 0.f, 0.f, 0.f};
+  float lse = kNegInf;
+  if (mx != kNegInf) {
+    const float l2 = mx + fast_log2(fast_exp2(la - mx) + fast_exp2(lb - mx));
+    const float wa = fast_exp2(la - l2);
+    const float wb = fast_exp2(lb - l2);
+    const f32x4 oa = *reinterpret_cast<const f32x4*>(a.o_a + r * a.head_dim + c);
+    const f32x4 ob = *reinterpret_cast<const f32x4*>(a.o_b + r * a.head_dim + c);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) out[i] = (wa == 0.f ? 0.f : wa * oa[i]) + (wb == 0.f ? 0.f : wb * ob[i]);
+    lse = l2 * kLn2;
+  }
+  if (a.o_bf16) {
+    *reinterpret_cast<u32x2*>(reinterpret_cast<uint16_t*>(a.o) + r * a.head_dim + c) =
+        u32x2{pack_bf16x2(out[0], out[1]), pack_bf16x2(out[2], out[3])};
+  } else {
+    *reinterpret_cast<f32x4*>(reinterpret_cast<float*>(a.o) + r * a.head_dim + c) = out;
+  }
+  if (c == 0 && a.lse) a.lse[r] = lse;
+}
+
+// Copies `count` tokens of one kv head through the same address helpers the
+// attention kernels use: which == 0, the prefix of request `index`
+// (paged_offset on its block-table row); which == 1, the drafts of branch
+// `index` (draft_offset).  One thread per 8 channels of one token.
+__global__ void __launch_bounds__(256) debug_gather_kernel(const DebugArgs a) {
+  const int c8 = a.head_dim >> 3;
+  const int idx = blockIdx.x * blockDim.x + threadIdx.x;
+  if (idx >= a.count * c8) return;
+  const int t = idx / c8;
+  const int c = (idx - t * c8) * 8;
+  int64_t off;
+  if (a.which == 0) {
+    off = (t >> a.kv.log2_page) < a.page_table_stride
+              ? paged_offset(a.kv, a.page_table + (int64_t)a.index * a.page_table_stride, t, a.kv_head)
+              : -1;
+  } else {
+    off = draft_offset(a.kv, a.branch_qo_indptr, a.draft_page_table, a.draft_page_table_stride,
+                       a.draft_start, a.index, a.index + 1, t, a.kv_head);
+  }
+  u32x4 k = {0u, 0u, 0u, 0u}, v = {0u, 0u, 0u, 0u};
+  if (off >= 0) {
+    k = *reinterpret_cast<const u32x4*>(a.kv.k + off + c);
+    v = *reinterpret_cast<const u32x4*>(a.kv.v + off + c);
+  } else {
+    atomicOr(&g_device_error, kErrPage);
+  }
+  *reinterpret_cast<u32x4*>(a.k_out + (int64_t)t * a.head_dim + c) = k;
+  *reinterpret_cast<u32x4*>(a.v_out + (int64_t)t * a.head_dim + c) = v;
+}
+
+// Branch `index`'s visibility over [its request's prefix ; its drafts]:
+// mask[s][t] = 1 for prefix keys t < L_i, and for draft key u = t - L_i by the
+// attention kernels' in-branch rule, with tokens numbered within the request
+// (as in the fused verify kernel).
+__global__ void __launch_bounds__(256) debug_mask_kernel(const DebugArgs a) {
+  const int idx = blockIdx.x * blockDim.x + threadIdx.x;
+  if (idx >= a.count * a.cols) return;
+  const int s = idx / a.cols;
+  const int t = idx - s * a.cols;
+  const int j = a.index;
+  const int i = request_of_branch(a.req_branch_indptr, a.batch_size, j);
+  const int L = a.cache_seqlens[i];
+  const int S = a.branch_qo_indptr[j + 1] - a.branch_qo_indptr[j];
+  const int req_tok0 = a.branch_qo_indptr[a.req_branch_indptr[i]];
+  const int bs = a.branch_qo_indptr[j] - req_tok0;  // branch start, request-relative
+  uint8_t vis = 0;
+  if (t < L) {
+    vis = 1;
+  } else if (t < L + S) {
+    vis = draft_visible(bs + s, bs, bs + (t - L)) ? 1 : 0;
+  }
+  a.mask_out[idx] = vis;
+}
+
+hipError_t launch_merge(const MergeArgs& a, hipStream_t s) {
+  const int64_t n = a.rows * (a.head_dim / 4);
+  if (n == 0) return hipSuccess;
+  const int64_t blocks = (n + 255) / 256;
+  hipLaunchKernelGGL(merge_state_kernel, dim3((unsigned)blocks), dim3(256), 0, s, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_debug_gather(const DebugArgs& a, hipStream_t s) {
+  const int n = a.count * (a.head_dim / 8);
+  if (n == 0) return hipSuccess;
+  hipLaunchKernelGGL(debug_gather_kernel, dim3((n + 255) / 256), dim3(256), 0, s, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_debug_mask(const DebugArgs& a, hipStream_t s) {
+  const int n = a.count * a.cols;
+  if (n == 0) return hipSuccess;
+  hipLaunchKernelGGL(debug_mask_kernel, dim3((n + 255) / 256), dim3(256), 0, s, a);
+  return hipGetLastError();
+}
+
+hipError_t read_error_small(int* v, int clear) {
+  hipError_t e = hipMemcpyFromSymbol(v, HIP_SYMBOL(g_device_error), sizeof(int));
+  if (e == hipSuccess && clear) {
+    const int zero = 0;
+    e = hipMemcpyToSymbol(HIP_SYMBOL(g_device_error), &zero, sizeof(int));
+  }
+  return e;
+}
+
+}  // namespace casc

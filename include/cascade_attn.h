@@ -1,0 +1,205 @@
+/*
+ * cascade_attn.h -- C ABI of libcascade_attn.so: cascade attention for the
+ * target-verify step of top-k tree speculative decoding, on AMD MI355X (gfx950).
+ *
+ * The operation (cascade attention page, zdszero.github.io):
+ *   request i has a prefix of L_i cached tokens and topk_i branches; branch j
+ *   holds S_j draft tokens.  Draft token s of branch j attends the request's
+ *   prefix plus draft tokens 0..s of its own branch (section "topk > 1").
+ *   The cascade computes this as
+ *     pass A  one attention over the request's prefix, read once, for every
+ *             query row of all its branches  -> (o_A, LSE_A)
+ *     pass B  one attention per branch over its own draft tokens under the
+ *             causal in-branch ancestor mask  -> (o_B, LSE_B)
+ *     merge   LSE = ln(e^LSE_A + e^LSE_B),
+ *             o = e^(LSE_A-LSE) o_A + e^(LSE_B-LSE) o_B
+ *   (sections "splittability of standard attention" and "mathematical
+ *   structure of the cascade scheme").  Scores are sm_scale * q.k; LSE values
+ *   are natural logarithms.  An empty key set has o = 0, LSE = -inf.
+ *
+ * Paged KV (KV-cache tutorial page, sections 5.2-5.3 and 6.2): one layer's K
+ * and V each live in a pool of fixed-size pages; a block-table row lists the
+ * physical page of each logical page of a sequence.  Token at logical slot t
+ * of row r is at page table[r][t / page_size], offset t % page_size.  Pages
+ * may be shared between rows (prefix sharing); the library only reads them.
+ * Query head h uses kv head h / (Hq / Hkv) (tutorial section 6.3, GQA).
+ *
+ * Conventions for every entry point:
+ *  - All array pointers are device pointers owned by the caller.  The library
+ *    never allocates, frees or synchronises; work is enqueued on `stream`
+ *    (a hipStream_t passed as void*, NULL = the default stream).
+ *  - Every argument check runs on the host before any HIP call; a failed check
+ *    returns a status and launches nothing.  cascade_last_error() then holds
+ *    a message (thread-local).
+ *  - Array *contents* (page ids, lengths, indptr monotonicity, the host-side
+ *    maxima in cascade_tree) are the caller's contract.  Kernels never read
+ *    outside the pool for a page id outside [0, num_pages) or a row outside
+ *    [0, total_rows): such keys/rows are skipped and a sticky device flag is
+ *    raised, readable with cascade_device_error().
+ *  - Outputs must not alias inputs.
+ */
+#ifndef CASCADE_ATTN_H
+#define CASCADE_ATTN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#if defined(__GNUC__)
+#define CASCADE_API __attribute__((visibility("default")))
+#else
+#define CASCADE_API
+#endif
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  CASCADE_OK = 0,
+  CASCADE_ERR_NULL = 1,        /* a required pointer is NULL                          */
+  CASCADE_ERR_SHAPE = 2,       /* inconsistent sizes (e.g. Hq % Hkv != 0, negative)  */
+  CASCADE_ERR_UNSUPPORTED = 3, /* head_dim, page size, stride or alignment not handled */
+  CASCADE_ERR_WORKSPACE = 4,   /* workspace missing or smaller than required         */
+  CASCADE_ERR_HIP = 5          /* a HIP runtime call failed (message in last_error)  */
+} cascade_status;
+
+typedef enum { CASCADE_F32 = 0, CASCADE_BF16 = 1 } cascade_dtype;
+
+/* One layer's paged K and V (bf16).  Element (page, slot, kv_head, c) of K is at
+ * k + page*page_stride + slot*token_stride + kv_head*head_stride + c.
+ * Requirements: head_dim in {64, 128}; page_size a power of two in [16, 4096];
+ * the three strides are multiples of 8 elements; k and v 16-byte aligned.
+ * The default layout [num_pages, page_size, Hkv, head_dim] has
+ * page_stride = page_size*Hkv*head_dim, token_stride = Hkv*head_dim,
+ * head_stride = head_dim. */
+typedef struct {
+  const void *k;
+  const void *v;
+  int32_t num_pages;
+  int32_t page_size;
+  int32_t num_kv_heads;
+  int32_t head_dim;
+  int64_t page_stride;
+  int64_t token_stride;
+  int64_t head_stride;
+} cascade_paged_kv;
+
+/* Queries, bf16 [total_rows, Hq, head_dim]; element (row, h, c) at
+ * q + row*row_stride + h*head_stride + c.  Strides are multiples of 8
+ * elements, q is 16-byte aligned.  Rows are ordered request-major, then
+ * branch, then draft position.  sm_scale is usually 1/sqrt(head_dim). */
+typedef struct {
+  const void *q;
+  int64_t row_stride;
+  int64_t head_stride;
+  int32_t num_qo_heads;
+  int32_t total_rows;
+  float sm_scale;
+} cascade_query;
+
+/* The verify tree (all arrays int32, device):
+ *  page_table        [batch_size, page_table_stride]  prefix block table per request
+ *                    (the per-request page table of pass A)
+ *  cache_seqlens     [batch_size]    L_i >= 0
+ *  req_branch_indptr [batch_size+1]  branches of request i are [indptr[i], indptr[i+1])
+ *  branch_qo_indptr  [num_branches+1] query rows of branch j; its S_j = diff rows are
+ *                    also its draft keys.  The rows of request i are contiguous:
+ *                    [branch_qo_indptr[req_branch_indptr[i]], ...[req_branch_indptr[i+1]]).
+ *  draft_page_table  [num_branches, draft_page_table_stride] per-branch block table
+ *                    (the per-branch page table of pass B)
+ *  draft_start       [num_branches] or NULL: draft token u of branch j sits at logical
+ *                    slot draft_start[j] + u of its row (NULL means 0).
+ * Host-side maxima, used to size launches; the caller promises them:
+ *  max_prefix_len    >= every L_i
+ *  max_request_rows  >= the number of query rows of every request
+ *  max_draft_len     >= every S_j */
+typedef struct {
+  int32_t batch_size;
+  int32_t num_branches;
+  const int32_t *page_table;
+  int32_t page_table_stride;
+  const int32_t *cache_seqlens;
+  const int32_t *req_branch_indptr;
+  const int32_t *branch_qo_indptr;
+  const int32_t *draft_page_table;
+  int32_t draft_page_table_stride;
+  const int32_t *draft_start;
+  int32_t max_prefix_len;
+  int32_t max_request_rows;
+  int32_t max_draft_len;
+} cascade_tree;
+
+/* Bytes of workspace cascade_prefix_attn and cascade_verify_attn need for these
+ * shapes (0 when the prefix pass runs unsplit).  Returns 0 on invalid arguments. */
+CASCADE_API size_t cascade_workspace_size(const cascade_query *q, const cascade_paged_kv *kv,
+                              const cascade_tree *tree);
+
+/* Pass A (cascade page, "mathematical structure", first attention): for every
+ * request, all query rows of all its branches attend the L_i prefix tokens,
+ * each page read once per (request, kv head).  Writes o_a float32
+ * [total_rows, Hq, head_dim] and lse_a float32 [total_rows, Hq] (LSE_A = -inf,
+ * o_A = 0 for L_i = 0).  Long prefixes are split into chunks whose partial
+ * states go to `workspace` and are merged with the same LSE identity. */
+CASCADE_API cascade_status cascade_prefix_attn(const cascade_query *q, const cascade_paged_kv *kv,
+                                   const cascade_tree *tree, float *o_a, float *lse_a,
+                                   void *workspace, size_t workspace_bytes, void *stream);
+
+/* Pass B (same section, second attention): each branch's rows attend its own
+ * S_j draft tokens; row s sees draft positions 0..s (the tree-attention
+ * ancestor mask of the tutorial's section 8.2, itself included).  Writes o_b
+ * float32 [total_rows, Hq, head_dim] and lse_b float32 [total_rows, Hq]. */
+CASCADE_API cascade_status cascade_draft_attn(const cascade_query *q, const cascade_paged_kv *kv,
+                                  const cascade_tree *tree, float *o_b, float *lse_b,
+                                  void *stream);
+
+/* The merge of two attention states over disjoint key sets (cascade page,
+ * "splittability"): elementwise over num_rows*num_heads rows of head_dim.
+ * o_a, o_b float32 [num_rows, num_heads, head_dim]; lse_a, lse_b float32
+ * [num_rows, num_heads]; o in o_dtype with the same shape; lse (nullable)
+ * float32.  A side with LSE = -inf contributes nothing; two such sides give
+ * o = 0, LSE = -inf.  head_dim must be a multiple of 4; pointers 16-byte aligned. */
+CASCADE_API cascade_status merge_state(const float *o_a, const float *lse_a, const float *o_b,
+                           const float *lse_b, int64_t num_rows, int32_t num_heads,
+                           int32_t head_dim, void *o, cascade_dtype o_dtype, float *lse,
+                           void *stream);
+
+/* The whole cascade in as few launches as the shapes allow: pass A, pass B and
+ * the merge fused in one kernel when the prefix runs unsplit; otherwise the
+ * split prefix pass, then one kernel that merges the splits, runs pass B and
+ * merges.  o [total_rows, Hq, head_dim] in o_dtype, lse float32 (nullable). */
+CASCADE_API cascade_status cascade_verify_attn(const cascade_query *q, const cascade_paged_kv *kv,
+                                   const cascade_tree *tree, void *o, cascade_dtype o_dtype,
+                                   float *lse, void *workspace, size_t workspace_bytes,
+                                   void *stream);
+
+/* Baseline (cascade page, naive expansion): the batch expanded into one
+ * virtual request per branch; each reads its request's whole prefix and its
+ * own drafts and runs one softmax.  Same outputs as cascade_verify_attn. */
+CASCADE_API cascade_status naive_expand(const cascade_query *q, const cascade_paged_kv *kv,
+                            const cascade_tree *tree, void *o, cascade_dtype o_dtype,
+                            float *lse, void *stream);
+
+CASCADE_API const char *cascade_status_string(cascade_status s);
+CASCADE_API const char *cascade_last_error(void);
+
+/* Test hooks, built on the same index helpers the attention kernels use.
+ * cascade_debug_gather: which = 0 copies request `index`'s L_i prefix tokens,
+ * which = 1 branch `index`'s S_j draft tokens, of kv head `kv_head`, into k_out
+ * and v_out (bf16 [count, head_dim], device, sized by the caller).
+ * cascade_debug_mask: branch `branch`'s visibility over [its request's prefix ;
+ * its drafts] as uint8 [S_j, L_i + S_j] (1 = visible), device, sized by the caller. */
+CASCADE_API cascade_status cascade_debug_gather(const cascade_paged_kv *kv, const cascade_tree *tree,
+                                    int32_t which, int32_t index, int32_t kv_head,
+                                    void *k_out, void *v_out, void *stream);
+CASCADE_API cascade_status cascade_debug_mask(const cascade_tree *tree, int32_t branch,
+                                  uint8_t *mask_out, int32_t mask_cols, void *stream);
+
+/* Reads (and with clear != 0 resets) the sticky device flag raised when a
+ * kernel met a page id or row outside its bounds.  Synchronises the device. */
+CASCADE_API cascade_status cascade_device_error(int32_t *flag_out, int32_t clear);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* CASCADE_ATTN_H */

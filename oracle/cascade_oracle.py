@@ -249,29 +249,43 @@ def naive_expand(wl, rows=None):
 
 
 def cascade_rows(wl, rows):
-    """Cascade result (pass A, pass B, merge) for selected global rows only."""
+    """Cascade result (pass A, pass B, merge) for selected global rows only.
+
+    Rows are grouped by request and by kv head so that one prefix gather and
+    one pass-A call serve all selected rows of a request; pass B runs per row
+    over that row's visible drafts.  Returns (rows, o [n, Hq, d], lse [n, Hq])."""
     R, Hq, d = wl.q.shape
+    Hkv = wl.num_kv_heads
+    grp = Hq // Hkv
     rows = np.unique(np.asarray(list(rows), np.int64))
     req_of = _request_of_branch(wl.req_branch_indptr)
     br_of = _branch_of_row(wl.branch_qo_indptr)
     qo = wl.branch_qo_indptr
-    o_a = np.zeros((rows.size, Hq, d)); lse_a = np.full((rows.size, Hq), -np.inf)
-    o_b = np.zeros((rows.size, Hq, d)); lse_b = np.full((rows.size, Hq), -np.inf)
-    cache = {}
-    for n, r in enumerate(rows):
-        j = int(br_of[r]); i = int(req_of[j]); s = int(r - qo[j])
-        if ("p", i) not in cache:
-            cache[("p", i)] = _prefix_kv(wl, i)
-        if ("d", j) not in cache:
-            cache[("d", j)] = _draft_kv(wl, j)
-        kp, vp = cache[("p", i)]
-        kd, vd = cache[("d", j)]
-        for h in range(Hq):
-            g = _kv_head(h, Hq, wl.num_kv_heads)
-            a = attention_state(wl.q[r, h][None], kp[:, g], vp[:, g], wl.sm_scale)
-            b = attention_state(wl.q[r, h][None], kd[:s + 1, g], vd[:s + 1, g], wl.sm_scale)
-            o_a[n, h], lse_a[n, h] = a[0][0], a[1][0]
-            o_b[n, h], lse_b[n, h] = b[0][0], b[1][0]
+    n = rows.size
+    o_a = np.zeros((n, Hq, d)); lse_a = np.full((n, Hq), -np.inf)
+    o_b = np.zeros((n, Hq, d)); lse_b = np.full((n, Hq), -np.inf)
+    by_req = {}
+    for x, r in enumerate(rows):
+        by_req.setdefault(int(req_of[br_of[r]]), []).append(x)
+    for i, xs in by_req.items():
+        xs = np.array(xs)
+        kp, vp = _prefix_kv(wl, i)
+        drafts = {}
+        for g in range(Hkv):
+            hs = [h for h in range(Hq) if _kv_head(h, Hq, Hkv) == g]
+            q = wl.q[rows[xs]][:, hs].reshape(-1, d)
+            oo, ll = attention_state(q, kp[:, g], vp[:, g], wl.sm_scale)
+            o_a[np.ix_(xs, hs)] = oo.reshape(xs.size, len(hs), d)
+            lse_a[np.ix_(xs, hs)] = ll.reshape(xs.size, len(hs))
+        for x in xs:
+            r = int(rows[x]); j = int(br_of[r]); s = r - int(qo[j])
+            if j not in drafts:
+                drafts[j] = _draft_kv(wl, j)
+            kd, vd = drafts[j]
+            for g in range(Hkv):
+                hs = [h for h in range(Hq) if _kv_head(h, Hq, Hkv) == g]
+                oo, ll = attention_state(wl.q[r, hs], kd[:s + 1, g], vd[:s + 1, g], wl.sm_scale)
+                o_b[x, hs], lse_b[x, hs] = oo, ll
     o, lse = merge_state(o_a, lse_a, o_b, lse_b)
     return rows, o, lse
 

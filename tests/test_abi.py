@@ -1,0 +1,126 @@
+"""C-ABI checks that need no GPU: the library loads, exports every symbol the
+header declares, and rejects bad arguments on the host before any HIP call."""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+from cascade_attention_tree_amd import binding as B
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "cascade_attn.h")
+
+pytestmark = pytest.mark.skipif(not os.path.exists(B.LIB_PATH), reason="library not built")
+
+FAKE = 0x10000  # a 16-byte aligned non-null address; never dereferenced on the host
+
+
+def header_functions():
+    src = open(HEADER, encoding="utf-8").read()
+    return set(re.findall(r"CASCADE_API\s+[\w\s\*]+?\b(\w+)\s*\(", src))
+
+
+def test_exports_every_declared_symbol():
+    declared = header_functions()
+    assert declared == set(B.EXPORTED)
+    lib = B.lib()
+    for name in declared:
+        assert hasattr(lib, name), name
+
+
+def test_status_strings():
+    lib = B.lib()
+    for s in range(6):
+        assert lib.cascade_status_string(s)
+    assert lib.cascade_status_string(99) == b"unknown status"
+
+
+def make(B_=2, Hq=8, Hkv=4, d=128, P=16, L=100, rows=6, npages=64, branches=4, dmax=3):
+    q = B.Query(FAKE, Hq * d, d, Hq, B_ * rows, d ** -0.5)
+    kv = B.PagedKV(FAKE, FAKE, npages, P, Hkv, d, P * Hkv * d, Hkv * d, d)
+    stride = -(-L // P)
+    t = B.Tree(B_, branches, FAKE, stride, FAKE, FAKE, FAKE, FAKE, 1, None, L, rows, dmax)
+    return q, kv, t
+
+
+def call_verify(q, kv, t, o=FAKE, ws=None, nbytes=0):
+    lib = B.lib()
+    return lib.cascade_verify_attn(ctypes.byref(q), ctypes.byref(kv), ctypes.byref(t), o,
+                                   B.CASCADE_F32, None, ws, nbytes, None)
+
+
+def test_rejects_before_launch():
+    lib = B.lib()
+    q, kv, t = make(Hq=6, Hkv=4)
+    assert call_verify(q, kv, t) == B.CASCADE_ERR_SHAPE
+    assert b"multiple" in lib.cascade_last_error()
+    q, kv, t = make(d=96)
+    assert call_verify(q, kv, t) == B.CASCADE_ERR_UNSUPPORTED
+    q, kv, t = make(P=8)
+    assert call_verify(q, kv, t) == B.CASCADE_ERR_UNSUPPORTED
+    q, kv, t = make(P=24)
+    assert call_verify(q, kv, t) == B.CASCADE_ERR_UNSUPPORTED
+    q, kv, t = make()
+    kv.k = None
+    assert call_verify(q, kv, t) == B.CASCADE_ERR_NULL
+    q, kv, t = make()
+    t.cache_seqlens = None
+    assert call_verify(q, kv, t) == B.CASCADE_ERR_NULL
+    q, kv, t = make()
+    assert call_verify(q, kv, t, o=None) == B.CASCADE_ERR_NULL
+    q, kv, t = make()
+    assert call_verify(q, kv, t, o=FAKE + 4) == B.CASCADE_ERR_UNSUPPORTED
+    q, kv, t = make()
+    kv.token_stride = 1020
+    assert call_verify(q, kv, t) == B.CASCADE_ERR_UNSUPPORTED
+    q, kv, t = make()
+    t.page_table_stride = 3          # 3 pages of 16 cannot hold L = 100
+    assert call_verify(q, kv, t) == B.CASCADE_ERR_SHAPE
+    q, kv, t = make()
+    q.sm_scale = float("nan")
+    assert call_verify(q, kv, t) == B.CASCADE_ERR_SHAPE
+    q, kv, t = make()
+    assert lib.naive_expand(ctypes.byref(q), ctypes.byref(kv), ctypes.byref(t), FAKE, 7, None,
+                            None) == B.CASCADE_ERR_UNSUPPORTED
+
+
+def test_workspace_rules():
+    lib = B.lib()
+    # Headline shape: 32 requests x 8 kv heads fill the GPU, the prefix is not split.
+    q, kv, t = make(B_=32, Hq=32, Hkv=8, L=2000, rows=20, branches=128, dmax=5)
+    assert lib.cascade_workspace_size(ctypes.byref(q), ctypes.byref(kv), ctypes.byref(t)) == 0
+    # Few requests with a long prefix: split, so a workspace is required.
+    q, kv, t = make(B_=2, Hq=8, Hkv=4, L=5000, rows=6)
+    need = lib.cascade_workspace_size(ctypes.byref(q), ctypes.byref(kv), ctypes.byref(t))
+    assert need > 0
+    assert call_verify(q, kv, t) == B.CASCADE_ERR_WORKSPACE
+    assert call_verify(q, kv, t, ws=FAKE, nbytes=need - 1) == B.CASCADE_ERR_WORKSPACE
+    # (o, lse) of every split: splits * rows * Hq * (d + 1) floats, lse block 256-aligned.
+    nsplit = need // (12 * 8 * 129 * 4)
+    assert nsplit >= 2
+    # Invalid arguments give 0.
+    q.num_qo_heads = 7
+    assert lib.cascade_workspace_size(ctypes.byref(q), ctypes.byref(kv), ctypes.byref(t)) == 0
+
+
+def test_merge_state_validation():
+    lib = B.lib()
+    assert lib.merge_state(FAKE, FAKE, FAKE, FAKE, 4, 2, 6, FAKE, 0, None, None) == B.CASCADE_ERR_UNSUPPORTED
+    assert lib.merge_state(None, FAKE, FAKE, FAKE, 4, 2, 8, FAKE, 0, None, None) == B.CASCADE_ERR_NULL
+    assert lib.merge_state(FAKE, FAKE, FAKE, FAKE, -1, 2, 8, FAKE, 0, None, None) == B.CASCADE_ERR_SHAPE
+    # nothing to do: OK without touching the GPU
+    assert lib.merge_state(None, None, None, None, 0, 2, 8, None, 0, None, None) == B.CASCADE_OK
+
+
+def test_debug_hook_validation():
+    lib = B.lib()
+    q, kv, t = make()
+    assert lib.cascade_debug_gather(ctypes.byref(kv), ctypes.byref(t), 2, 0, 0, FAKE, FAKE,
+                                    None) == B.CASCADE_ERR_SHAPE
+    assert lib.cascade_debug_gather(ctypes.byref(kv), ctypes.byref(t), 0, 5, 0, FAKE, FAKE,
+                                    None) == B.CASCADE_ERR_SHAPE
+    assert lib.cascade_debug_gather(ctypes.byref(kv), ctypes.byref(t), 0, 0, 9, FAKE, FAKE,
+                                    None) == B.CASCADE_ERR_SHAPE
+    assert lib.cascade_debug_mask(ctypes.byref(t), -1, FAKE, 4, None) == B.CASCADE_ERR_SHAPE
