@@ -8,10 +8,12 @@ Inputs are synthetic (seeded N(0,1) values rounded to bf16) and resident in
 HBM before timing starts.
 
 Protocol: W warm-up steps, then K timed steps.  Before every timed step a
-1 GiB buffer is overwritten (outside the timed interval) so that neither L2
-nor the 256 MB Infinity Cache still holds the 265 MB of KV; each step is
-timed with HIP events on the stream it is launched on.  The same protocol
-times naive expansion (the baseline) on the same inputs.
+1 GiB buffer is read (outside the timed interval) so that neither L2 nor the
+256 MB Infinity Cache still holds the 265 MB of KV.  The flush reads rather
+than writes: a freshly written 1 GiB leaves dirty lines whose write-back then
+lands inside the next timed kernel.  Each step is timed with HIP events on
+the stream it is launched on.  The same protocol times naive expansion (the
+baseline) on the same inputs.
 
 Prints one JSON line.  value = KV GB/s = cascade KV bytes / step time, where
 cascade KV bytes = sum_i (L_i + sum_j S_j) * Hkv * d * 2 (K and V) * 2 bytes.
@@ -128,6 +130,11 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--only-verify", action="store_true", help="time only the fused verify call")
+    ap.add_argument("--layout", choices=("HND", "NHD"), default="HND",
+                    help="page layout of the KV pool on the device (same logical content)")
+    ap.add_argument("--traffic-probe", action="store_true",
+                    help="for hardware-counter runs: one plain 256 MiB device copy (known bytes), "
+                         "then a few flushed verify steps; prints nothing else")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}); "
@@ -141,14 +148,15 @@ def main():
     print("bench: generating headline workload", file=sys.stderr, flush=True)
     wl = W.headline()
     kv_casc, kv_naive, q_bytes, o_bytes = workload_bytes(wl)
-    x = B.to_device(wl, "cuda")
+    x = B.to_device(wl, "cuda", layout=args.layout)
     o = torch.empty(wl.q.shape, dtype=torch.bfloat16, device="cuda")
     lse = torch.empty(wl.q.shape[:2], dtype=torch.float32, device="cuda")
     ws = B.workspace_for(x)
-    flush_buf = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
+    flush_buf = torch.ones(1 << 28, dtype=torch.float32, device="cuda")
+    flush_out = torch.empty((), dtype=torch.float32, device="cuda")
 
     def flush():
-        flush_buf.zero_()
+        torch.sum(flush_buf, dim=0, out=flush_out)   # reads 1 GiB, writes 4 bytes
 
     def verify():
         B.cascade_verify_attn(x, o=o, lse=lse, workspace=ws)
@@ -164,6 +172,19 @@ def main():
         B.cascade_prefix_attn(x, o_a=oa, lse_a=la, workspace=ws)
         B.cascade_draft_attn(x, o_b=ob, lse_b=lb)
         B.merge_state(oa, la, ob, lb, out_dtype=torch.bfloat16, o=o, lse=lse)
+
+    if args.traffic_probe:
+        src = torch.ones(1 << 26, dtype=torch.float32, device="cuda")   # 256 MiB
+        dst = torch.empty_like(src)
+        flush()
+        dst.copy_(src)
+        for _ in range(3):
+            flush()
+            verify()
+        torch.cuda.synchronize()
+        print(json.dumps({"traffic_probe": True, "copy_bytes": src.numel() * 4,
+                          "kernel_hash": kernel_source_hash()}), flush=True)
+        return
 
     print("bench: timing cascade_verify_attn", file=sys.stderr, flush=True)
     ms, wall = time_steps(verify, args.steps, args.warmup, flush, torch)
@@ -206,8 +227,9 @@ def main():
         "data": "synthetic",
         "config": {"workload": "headline verify: B=32, Hq=32, Hkv=8, d=128, L=2000, topk=4, S=5, "
                                "page 16, random page table, bf16 in, bf16 out",
+                   "page_layout": args.layout,
                    "global_batch": wl.batch_size, "query_tokens": wl.total_rows,
-                   "kv_bytes_cascade": kv_casc, "protocol": "cold (1 GiB overwrite between steps)"},
+                   "kv_bytes_cascade": kv_casc, "protocol": "cold (1 GiB read between steps)"},
         "pct_hbm_peak": 100.0 * kv_gbs / HBM_PEAK_GBS,
         "query_tok_per_s": wl.total_rows / (t_ms * 1e-3),
         "median_ms": float(np.median(ms)), "p10_ms": float(np.percentile(ms, 10)),

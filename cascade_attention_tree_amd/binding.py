@@ -154,12 +154,20 @@ def _bf16_tensor(x: np.ndarray, device) -> torch.Tensor:
 
 def make_structs(q, k_pool, v_pool, page_table, cache_seqlens, req_branch_indptr,
                  branch_qo_indptr, draft_page_table, draft_start, sm_scale,
-                 max_prefix_len, max_request_rows, max_draft_len):
+                 max_prefix_len, max_request_rows, max_draft_len, layout="NHD"):
+    """layout "NHD": pools are [pages, P, Hkv, d]; "HND": [pages, Hkv, P, d]."""
     R, Hq, d = q.shape
-    num_pages, P, Hkv, _ = k_pool.shape
+    assert k_pool.stride() == v_pool.stride()
+    if layout == "NHD":
+        num_pages, P, Hkv, _ = k_pool.shape
+        ps, ts, hs = k_pool.stride(0), k_pool.stride(1), k_pool.stride(2)
+    elif layout == "HND":
+        num_pages, Hkv, P, _ = k_pool.shape
+        ps, ts, hs = k_pool.stride(0), k_pool.stride(2), k_pool.stride(1)
+    else:
+        raise ValueError(layout)
     query = Query(q.data_ptr(), q.stride(0), q.stride(1), Hq, R, float(sm_scale))
-    kv = PagedKV(k_pool.data_ptr(), v_pool.data_ptr(), num_pages, P, Hkv, d,
-                 k_pool.stride(0), k_pool.stride(1), k_pool.stride(2))
+    kv = PagedKV(k_pool.data_ptr(), v_pool.data_ptr(), num_pages, P, Hkv, d, ps, ts, hs)
     tree = Tree(int(cache_seqlens.shape[0]), int(branch_qo_indptr.shape[0] - 1),
                 page_table.data_ptr(), page_table.stride(0), cache_seqlens.data_ptr(),
                 req_branch_indptr.data_ptr(), branch_qo_indptr.data_ptr(),
@@ -168,17 +176,24 @@ def make_structs(q, k_pool, v_pool, page_table, cache_seqlens, req_branch_indptr
     return query, kv, tree
 
 
-def to_device(wl: "_wl.Workload", device="cuda") -> DeviceInputs:
-    """Uploads a workload (bf16 values, int32 tables) and builds its C structs."""
+def to_device(wl: "_wl.Workload", device="cuda", layout="NHD") -> DeviceInputs:
+    """Uploads a workload (bf16 values, int32 tables) and builds its C structs.
+
+    layout "NHD" keeps the generator's token-major pages [pages, P, Hkv, d];
+    "HND" stores each page head-major, [pages, Hkv, P, d], so that one kv head's
+    tokens of a page are one contiguous run (same logical content)."""
     i32 = lambda a: torch.from_numpy(np.ascontiguousarray(a, np.int32)).to(device)
     q = _bf16_tensor(wl.q, device)
     k = _bf16_tensor(wl.k_pool, device)
     v = _bf16_tensor(wl.v_pool, device)
+    if layout == "HND":
+        k = k.permute(0, 2, 1, 3).contiguous()
+        v = v.permute(0, 2, 1, 3).contiguous()
     pt, cs, rb = i32(wl.page_table), i32(wl.cache_seqlens), i32(wl.req_branch_indptr)
     qo, dpt, ds = i32(wl.branch_qo_indptr), i32(wl.draft_page_table), i32(wl.draft_start)
     query, kv, tree = make_structs(q, k, v, pt, cs, rb, qo, dpt, ds, wl.sm_scale,
                                    wl.max_prefix_len(), wl.max_rows_per_request(),
-                                   wl.max_draft_len())
+                                   wl.max_draft_len(), layout)
     return DeviceInputs(q, k, v, pt, cs, rb, qo, dpt, ds, query, kv, tree)
 
 

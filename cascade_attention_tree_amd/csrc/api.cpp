@@ -76,6 +76,12 @@ void plan_splits(Plan& p, int max_len) {
   p.n_splits = (int)cdiv(len, p.split_len);
 }
 
+// Bytes from the start of a page to the end of its last (token, head) row.
+int64_t page_extent_bytes(const cascade_paged_kv* kv) {
+  return ((int64_t)(kv->page_size - 1) * kv->token_stride +
+          (int64_t)(kv->num_kv_heads - 1) * kv->head_stride + kv->head_dim) * 2;
+}
+
 cascade_status check_kv(const cascade_paged_kv* kv) {
   if (!kv) return fail(CASCADE_ERR_NULL, "kv is NULL");
   if (!kv->k || !kv->v) return fail(CASCADE_ERR_NULL, "kv->k or kv->v is NULL");
@@ -92,6 +98,8 @@ cascade_status check_kv(const cascade_paged_kv* kv) {
     return fail(CASCADE_ERR_UNSUPPORTED, "kv strides must be multiples of 8 elements");
   if (!aligned16(kv->k) || !aligned16(kv->v))
     return fail(CASCADE_ERR_UNSUPPORTED, "kv->k and kv->v must be 16-byte aligned");
+  if (page_extent_bytes(kv) >= (1ll << 30))
+    return fail(CASCADE_ERR_UNSUPPORTED, "one page spans more than 1 GiB");
   return CASCADE_OK;
 }
 
@@ -162,6 +170,7 @@ casc::AttnArgs make_args(const cascade_query* q, const cascade_paged_kv* kv, con
   a.kv.head_stride = kv->head_stride;
   a.kv.num_pages = kv->num_pages;
   a.kv.log2_page = ilog2(kv->page_size);
+  a.kv.page_bytes = (int32_t)page_extent_bytes(kv);
   a.num_kv_heads = kv->num_kv_heads;
   a.batch_size = t->batch_size;
   a.page_table = t->page_table;

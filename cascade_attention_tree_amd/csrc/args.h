@@ -16,6 +16,8 @@ struct KvView {
   int64_t head_stride;
   int32_t num_pages;
   int32_t log2_page;
+  int32_t page_bytes;  // bytes spanned by one page of K (or V): the range of
+                       // its buffer descriptor, so reads past it return zero
 };
 
 enum AttnMode : int {

@@ -229,7 +229,7 @@ attn_kernel(const AttnArgs a) {
   };
 
   const KvView kv = a.kv;
-  const int32_t* __restrict__ pt_row = a.page_table + (int64_t)req * a.page_table_stride;
+  cint32* pt_row = as_const(a.page_table + (int64_t)req * a.page_table_stride);
   const float c2 = a.scale_log2;
   const int pmask = (1 << kv.log2_page) - 1;
   const int64_t head_off = (int64_t)g * kv.head_stride + g4 * 8;
@@ -239,66 +239,57 @@ attn_kernel(const AttnArgs a) {
   // Prefix tiles start at a multiple of 32 and pages hold >= 16 tokens, so
   // each 16-key half of a tile lies in one page whose id pg[kb] is
   // wave-uniform (-1: no key in that half, or an id outside the pool).
-  auto load_k_prefix = [&](const int (&pg)[2], int base, int end, bf16x8 (&kr)[2][KS]) {
+  auto load_prefix = [&](const uint16_t* pool, const int (&pg)[2], int base, int end,
+                         bf16x8 (&r)[2][KS]) {
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
       const int key = base + kb * 16 + l16;
-      const bool ok = key < end && pg[kb] >= 0;
-      // Lanes without a key read the pool's first row instead (always
-      // mapped); their scores are masked, so K needs no zeroing.
-      const int64_t off = ok ? (int64_t)pg[kb] * kv.page_stride +
-                                   (int64_t)(key & pmask) * kv.token_stride + head_off
-                             : (int64_t)(g4 * 8);
+      const bool page_ok = pg[kb] >= 0;
+      const __amdgpu_buffer_rsrc_t rs =
+          page_rsrc(pool + (int64_t)(page_ok ? pg[kb] : 0) * kv.page_stride, page_ok ? kv.page_bytes : 0);
+      const int off = key < end ? (int)(((int64_t)(key & pmask) * kv.token_stride + head_off) * 2)
+                                : kOutOfRange;
 #pragma unroll
-      for (int ks = 0; ks < KS; ++ks) kr[kb][ks] = *reinterpret_cast<const bf16x8*>(kv.k + off + ks * 32);
+      for (int ks = 0; ks < KS; ++ks) r[kb][ks] = __builtin_bit_cast(bf16x8, buf_load16(rs, off + ks * 64));
     }
   };
+  auto load_k_prefix = [&](const int (&pg)[2], int base, int end, bf16x8 (&kr)[2][KS]) {
+    load_prefix(kv.k, pg, base, end, kr);
+  };
   auto load_v_prefix = [&](const int (&pg)[2], int base, int end, bf16x8 (&vr)[2][KS]) {
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
-      const int key = base + kb * 16 + l16;
-      const bool ok = key < end && pg[kb] >= 0;
-      const int64_t off = ok ? (int64_t)pg[kb] * kv.page_stride +
-                                   (int64_t)(key & pmask) * kv.token_stride + head_off
-                             : (int64_t)(g4 * 8);
-#pragma unroll
-      for (int ks = 0; ks < KS; ++ks) {
-        // V of lanes without a key must be zero: a weight of 0 times a NaN
-        // left in an unused slot would still poison the sum.
-        const u32x4 x = *reinterpret_cast<const u32x4*>(kv.v + off + ks * 32);
-        vr[kb][ks] = __builtin_bit_cast(bf16x8, ok ? x : u32x4{0u, 0u, 0u, 0u});
-      }
-    }
+    load_prefix(kv.v, pg, base, end, vr);
   };
   auto prefix_pages = [&](int base, int end, int (&pg)[2]) {
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
       const int first = base + kb * 16;
-      int id = -1;
-      if (first < end) {
-        id = pt_row[first >> kv.log2_page];
-        if ((uint32_t)id >= (uint32_t)kv.num_pages) {
-          if (lane == 0) atomicOr(&g_device_error, kErrPage);
-          id = -1;
-        }
+      int id = first < end ? pt_row[first >> kv.log2_page] : -1;
+      if (id >= kv.num_pages) {
+        if (lane == 0) atomicOr(&g_device_error, kErrPage);
       }
-      pg[kb] = id;
+      if ((uint32_t)id >= (uint32_t)kv.num_pages) id = -1;
+      pg[kb] = __builtin_amdgcn_readfirstlane(id);  // uniform by construction
     }
   };
   // Draft tiles: keys are segment tokens [base, base+32); each lane resolves
-  // its own key's branch, slot and page.
-  auto load_draft = [&](int base, int end, bf16x8 (&kr)[2][KS], bf16x8 (&vr)[2][KS]) {
+  // its own key's branch, slot and page (-2: no key, -1: bad page).
+  auto draft_offsets = [&](int base, int end, int64_t (&off)[2]) {
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
       const int key = base + kb * 16 + l16;
-      int64_t off = -2;
+      off[kb] = -2;
       if (key < end) {
-        off = draft_offset(kv, qo, a.draft_page_table, a.draft_page_table_stride, a.draft_start,
-                           jb, je, key, g);
-        if (off == -1) atomicOr(&g_device_error, kErrPage);
+        off[kb] = draft_offset(kv, qo, a.draft_page_table, a.draft_page_table_stride, a.draft_start,
+                               jb, je, key, g);
+        if (off[kb] == -1) atomicOr(&g_device_error, kErrPage);
       }
-      const bool ok = off >= 0;
-      const int64_t o2 = ok ? off + g4 * 8 : (int64_t)(g4 * 8);
+    }
+  };
+  auto load_draft_at = [&](const int64_t (&off)[2], bf16x8 (&kr)[2][KS], bf16x8 (&vr)[2][KS]) {
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+      const bool ok = off[kb] >= 0;
+      const int64_t o2 = ok ? off[kb] + g4 * 8 : (int64_t)(g4 * 8);
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks) {
         kr[kb][ks] = *reinterpret_cast<const bf16x8*>(kv.k + o2 + ks * 32);
@@ -307,6 +298,21 @@ attn_kernel(const AttnArgs a) {
       }
     }
   };
+  auto load_draft = [&](int base, int end, bf16x8 (&kr)[2][KS], bf16x8 (&vr)[2][KS]) {
+    int64_t off[2];
+    draft_offsets(base, end, off);
+    load_draft_at(off, kr, vr);
+  };
+
+  // The fused verify epilogue starts with the first draft tile of the chunk;
+  // its addresses are resolved now so that its loads can be issued as soon as
+  // the prefix loop ends.
+  int64_t doff0[2] = {-2, -2};
+  if constexpr (kEpilogueDraft) {
+    if (dlo < dhi) draft_offsets(dlo, dhi, doff0);
+  }
+  bf16x8 dkr[2][KS], dvr[2][KS];
+  bool draft_loaded = false;
 
   // S^T for one tile: s[rb][kb] holds keys kb*16 + 4*g4 + i of row rb*16 + l16.
   auto scores = [&](const bf16x8 (&kr)[2][KS], f32x4 (&s)[RB][2]) {
@@ -533,6 +539,12 @@ attn_kernel(const AttnArgs a) {
     }
 
     mfma_drain();
+    if constexpr (MODE == kModeVerify) {
+      if (a.n_splits == 1 && dlo < dhi) {
+        load_draft_at(doff0, dkr, dvr);  // lands while the waves merge
+        draft_loaded = true;
+      }
+    }
 
     // ---- merge the four waves' states (LSE identity) ----------------------
 #pragma unroll
@@ -601,6 +613,12 @@ attn_kernel(const AttnArgs a) {
   }
 
   if constexpr (kFinish) {
+    if constexpr (MODE == kModeVerifyFinish) {
+      if (dlo < dhi) {
+        load_draft_at(doff0, dkr, dvr);  // lands while the partials merge
+        draft_loaded = true;
+      }
+    }
     // Merge the prefix split partials of these rows (fixed split order).
     const int nsp = (L + a.split_len - 1) / a.split_len;
     const int64_t plane = (int64_t)a.total_rows * a.num_qo_heads;
@@ -655,7 +673,17 @@ attn_kernel(const AttnArgs a) {
       }
       for (int base = dlo; base < dhi; base += 32) {
         bf16x8 kr[2][KS], vr[2][KS];
-        load_draft(base, dhi, kr, vr);
+        if (base == dlo && draft_loaded) {
+#pragma unroll
+          for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+            for (int ks = 0; ks < KS; ++ks) {
+              kr[kb][ks] = dkr[kb][ks];
+              vr[kb][ks] = dvr[kb][ks];
+            }
+        } else {
+          load_draft(base, dhi, kr, vr);
+        }
         stage_v(vr, vs);
         f32x4 s[RB][2];
         scores(kr, s);

@@ -14,6 +14,11 @@ typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8;
 typedef __attribute__((ext_vector_type(4))) float f32x4;
 typedef __attribute__((ext_vector_type(4))) unsigned int u32x4;
 typedef __attribute__((ext_vector_type(2))) unsigned int u32x2;
+// Read-only tables (block tables, lengths) seen through the constant address
+// space: uniform reads of them compile to scalar loads, which complete on
+// their own counter instead of behind the vector loads of K and V.
+typedef const __attribute__((address_space(4))) int32_t cint32;
+__device__ __forceinline__ cint32* as_const(const int32_t* p) { return (cint32*)(uintptr_t)p; }
 
 // Sticky error word of this translation unit (bit flags below); read and
 // cleared by the host through hipMemcpyFromSymbol / hipMemcpyToSymbol.
@@ -85,6 +90,18 @@ __device__ __forceinline__ int64_t draft_offset(const KvView& kv, const int32_t*
   const int slot = (dstart ? dstart[j] : 0) + u;
   if (slot < 0 || (slot >> kv.log2_page) >= dstride) return -1;
   return paged_offset(kv, dpt + (int64_t)j * dstride, slot, g);
+}
+
+// Buffer descriptor over one page (gfx9-family raw buffer: stride 0, dword 3
+// = 0x00020000).  A lane whose byte offset lies past `bytes` reads zeros, so a
+// partially valid tile needs neither branches nor selects.
+constexpr int kBufFlags = 0x00020000;
+constexpr int kOutOfRange = 0x7ff00000;  // a byte offset beyond any page
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t page_rsrc(const uint16_t* base, int bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc((void*)base, 0, bytes, kBufFlags);
+}
+__device__ __forceinline__ u32x4 buf_load16(__amdgpu_buffer_rsrc_t r, int byte_off) {
+  return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, byte_off, 0, 0));
 }
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }

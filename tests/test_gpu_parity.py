@@ -91,11 +91,12 @@ def test_draft_pass(B, case):
     cmp(o, l, ro, rl)
 
 
+@pytest.mark.parametrize("layout", ["NHD", "HND"])
 @pytest.mark.parametrize("case", CASES)
-def test_verify_and_three_call_path(B, case):
+def test_verify_and_three_call_path(B, case, layout):
     wl = small_cases()[case]()
-    note(f"verify {case}")
-    x = B.to_device(wl)
+    note(f"verify {case} {layout}")
+    x = B.to_device(wl, layout=layout)
     ro, rl = O.cascade(wl)
     o, l = B.cascade_verify_attn(x)
     oa, la = B.cascade_prefix_attn(x)
@@ -106,11 +107,12 @@ def test_verify_and_three_call_path(B, case):
     cmp(o3, l3, ro, rl)
 
 
+@pytest.mark.parametrize("layout", ["NHD", "HND"])
 @pytest.mark.parametrize("case", CASES)
-def test_naive_expand(B, case):
+def test_naive_expand(B, case, layout):
     wl = small_cases()[case]()
-    note(f"naive_expand {case}")
-    x = B.to_device(wl)
+    note(f"naive_expand {case} {layout}")
+    x = B.to_device(wl, layout=layout)
     o, l = B.naive_expand(x)
     torch.cuda.synchronize()
     ro, rl = O.naive_expand(wl)
@@ -141,10 +143,11 @@ def test_merge_state_kernel(B):
     assert np.max(np.abs(ob16.float().cpu().numpy() - ref16)) <= 2 ** -7
 
 
-def test_verify_headline_all_rows(B):
+@pytest.mark.parametrize("layout", ["NHD", "HND"])
+def test_verify_headline_all_rows(B, layout):
     wl = W.headline()
-    note(f"verify headline rows={wl.total_rows}")
-    x = B.to_device(wl)
+    note(f"verify headline rows={wl.total_rows} {layout}")
+    x = B.to_device(wl, layout=layout)
     o, l = B.cascade_verify_attn(x)
     on, ln = B.naive_expand(x)
     torch.cuda.synchronize()
