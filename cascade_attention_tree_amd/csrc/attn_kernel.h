@@ -10,17 +10,21 @@
 //
 // Inside the workgroup every wave keeps all rows of the chunk and takes every
 // 4th 32-key tile.  Per tile a wave
-//   * loads K straight from HBM into MFMA A-fragments (16 keys x 32 channels:
-//     one 16-byte load per lane and k-step), gathered through the block table,
-//   * computes S^T = K Q^T with v_mfma_f32_16x16x32_bf16 (keys on M, rows on N),
-//   * updates a base-2 online softmax per row (in-lane max over 8 keys, then
-//     two cross-lane exchanges),
-//   * stages V through its own LDS region and reads it back transposed as the
-//     A-fragments of O^T += V^T P^T.  P^T is already in B-fragment layout in
-//     the lanes that computed S^T, so P never moves between lanes.
-// Loads of the wave's next tile are issued as soon as the registers they land
-// in are free (V right after staging, K right after its MFMAs), so they run
-// under the current tile's softmax and PV work.
+//   * has the tile's K and V rows in registers (loaded one iteration earlier:
+//     whole 256-byte key rows per group of lanes, through the block table),
+//     writes them to its own LDS stage and issues the loads of its next tile,
+//   * reads K back as MFMA A-fragments and computes S^T = K Q^T with
+//     v_mfma_f32_16x16x32_bf16 (keys on M, rows on N),
+//   * updates a base-2 online softmax per row; the cross-lane row max is only
+//     formed when some lane's own max exceeds the carried max by the slack,
+//   * reads V back transposed (ds_read_b64_tr_b16) as the A-fragments of
+//     O^T += V^T P^T.  P^T is already in B-fragment layout in the lanes that
+//     computed S^T, so P never moves between lanes.
+//
+// Before the key loop the workgroup resolves everything that depends on the
+// tree layout into small LDS tables (branch starts of its tokens, physical
+// offsets of the draft keys it can see), so that no chain of dependent global
+// loads sits on the path of the key loop or of the epilogue.
 //
 // The four waves then merge their states with the LSE identity; each wave
 // ends up owning a quarter of the head dimension.  Depending on the mode the
@@ -72,6 +76,54 @@ __device__ __forceinline__ void mfma_drain() {
   __builtin_amdgcn_sched_barrier(0);
 }
 
+// Max and sum over lanes l, l^16, l^32, l^48 -- the four key groups that hold
+// one row of an S^T block -- with the row swaps of CDNA4 (VALU only).  A swap
+// of a register with a copy of itself leaves rows {0,1} (resp. {2,3}, or the
+// two halves) of the same lanes in the two results; every lane ends with the
+// same value, combined in the same order.  Both results pass through an empty
+// asm: without it the optimizer folds a combine of the two results of the
+// swap into its first result.
+__device__ __forceinline__ void swap_rows16(float x, float& p, float& q) {
+  unsigned u = __builtin_bit_cast(unsigned, x), c = u;
+  asm volatile("" : "+v"(c));
+  const auto r = __builtin_amdgcn_permlane16_swap(u, c, false, false);
+  unsigned r0 = r[0], r1 = r[1];
+  asm volatile("" : "+v"(r0), "+v"(r1));
+  p = __builtin_bit_cast(float, r0);
+  q = __builtin_bit_cast(float, r1);
+}
+__device__ __forceinline__ void swap_rows32(float x, float& p, float& q) {
+  unsigned u = __builtin_bit_cast(unsigned, x), c = u;
+  asm volatile("" : "+v"(c));
+  const auto r = __builtin_amdgcn_permlane32_swap(u, c, false, false);
+  unsigned r0 = r[0], r1 = r[1];
+  asm volatile("" : "+v"(r0), "+v"(r1));
+  p = __builtin_bit_cast(float, r0);
+  q = __builtin_bit_cast(float, r1);
+}
+__device__ __forceinline__ float rowgroup_max(float x) {
+  float p, q;
+  swap_rows16(x, p, q);
+  swap_rows32(fmaxf(p, q), p, q);
+  return fmaxf(p, q);
+}
+__device__ __forceinline__ float rowgroup_sum(float x) {
+  float p, q;
+  swap_rows16(x, p, q);
+  swap_rows32(p + q, p, q);
+  return p + q;
+}
+
+typedef __attribute__((ext_vector_type(4))) short i16x4;
+typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
+
+// Transposing LDS read: within each group of 16 lanes, lane i receives
+// element (i & 3) of the 4-element vectors addressed by lanes i/4, 4 + i/4,
+// 8 + i/4, 12 + i/4 (in that order).
+__device__ __forceinline__ i16x4 lds_read_tr16(const uint16_t* p) {
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(p));
+}
+
 template <int D, int RB, int MODE>
 __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
 attn_kernel(const AttnArgs a) {
@@ -79,26 +131,43 @@ attn_kernel(const AttnArgs a) {
   constexpr int DB = D / 16;        // 16-channel blocks of the head dim
   constexpr int DBW = DB / 4;       // blocks each wave owns after the combine
   constexpr int ROWS = RB * 16;
-  constexpr int VSTR = D + 4;       // LDS row stride of a staged V tile (bf16): the
-                                    // transposed reads of keys 4 apart hit distinct banks
-  constexpr int STAGE = 32 * VSTR;  // bf16 elements per staged tile
+  constexpr int NI = D / 16;        // 16-byte loads per lane for one 32-key tile of K (or V)
+  constexpr int CPR = D / 8;        // 16-byte chunks per key row
+  constexpr int TPI = 64 / CPR;     // key rows covered by one row-shaped load
+  // LDS row stride (bf16) of staged K and V tiles.  D + 16 puts consecutive
+  // rows 8 banks apart: the A-fragment reads (16 B of 8 consecutive keys per
+  // pass) and the transposed V reads (8 B of 4 consecutive keys x 4 column
+  // quads per 16 lanes) touch distinct banks, and rows stay 16-byte aligned.
+  constexpr int RS = D + 16;
+  constexpr int STAGE = 2 * 32 * RS;  // bf16 elements per wave: the K tile, then the V tile
   constexpr int XSLOT = RB * DBW * 64 * 4;  // floats per (owner, source) exchange slot
-  constexpr int STAGE_BYTES = 4 * 2 * STAGE * 2;
+  constexpr int STAGE_BYTES = 4 * STAGE * 2;
   constexpr int XBYTES = 12 * XSLOT * 4;
   constexpr int UNION_BYTES = STAGE_BYTES > XBYTES ? STAGE_BYTES : XBYTES;
   constexpr bool kMainLoop = MODE <= kModeNaive;
   constexpr bool kFinish = MODE == kModePrefixFinish || MODE == kModeVerifyFinish;
   constexpr bool kEpilogueDraft = MODE == kModeVerify || MODE == kModeVerifyFinish;
+  constexpr bool kDraftKeys = MODE == kModeDraft || MODE == kModeNaive || kEpilogueDraft;
   constexpr bool kNeedQ = MODE != kModePrefixFinish;
   // Large row tiles keep Q in LDS (read per tile as B-fragments) so that the
   // architectural VGPRs stay free for K/V in flight and the softmax.
   constexpr bool kQInLds = kNeedQ && RB * KS >= 16;
   constexpr int QSTR = D + 8;  // padded LDS row stride of Q: rows land 4 banks apart
   constexpr int QBYTES = kQInLds ? ROWS * QSTR * 2 : 0;
+  constexpr int MLBYTES = 4 * ROWS * 2 * 4;
+  // Tree tables: branches of one segment, and draft keys of one chunk, whose
+  // lookups are resolved in LDS; larger segments fall back to global lookups.
+  constexpr int NBCAP = 128;
+  constexpr int KEYCAP = 512;
+  constexpr int TBYTES = kDraftKeys ? KEYCAP * 8 + ((2 * NBCAP + 1 + ROWS) * 4 + 15) / 16 * 16 : 0;
 
-  __shared__ __attribute__((aligned(16))) unsigned char smem[UNION_BYTES + QBYTES + 4 * ROWS * 2 * 4];
-  uint16_t* qs = reinterpret_cast<uint16_t*>(smem + UNION_BYTES);               // [ROWS][QSTR]
-  float* ml = reinterpret_cast<float*>(smem + UNION_BYTES + QBYTES);  // [4 waves][ROWS][m, l]
+  __shared__ __attribute__((aligned(16))) unsigned char smem[UNION_BYTES + QBYTES + MLBYTES + TBYTES];
+  uint16_t* qs = reinterpret_cast<uint16_t*>(smem + UNION_BYTES);                // [ROWS][QSTR]
+  float* ml = reinterpret_cast<float*>(smem + UNION_BYTES + QBYTES);             // [4][ROWS][m, l]
+  int64_t* t_doff = reinterpret_cast<int64_t*>(smem + UNION_BYTES + QBYTES + MLBYTES);  // [KEYCAP]
+  int* t_bnd = reinterpret_cast<int*>(t_doff + KEYCAP);  // [NBCAP + 1] branch_qo_indptr window
+  int* t_dst = t_bnd + NBCAP + 1;                        // [NBCAP] draft_start window
+  int* t_rbs = t_dst + NBCAP;                            // [ROWS] branch start per chunk token
 
   const int lane = threadIdx.x & 63;
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -115,18 +184,27 @@ attn_kernel(const AttnArgs a) {
   const int seg = item / a.num_kv_heads;
 
   const int32_t* __restrict__ qo = a.branch_qo_indptr;
+  cint32* cqo = as_const(qo);
   int req, jb, je;
   if constexpr (MODE == kModeNaive) {
     jb = seg;
     je = seg + 1;
-    req = request_of_branch(a.req_branch_indptr, a.batch_size, seg);
+    // The request owning branch `seg`: the requests whose first branch is at
+    // or before it, minus one (req_branch_indptr is non-decreasing).
+    int cnt = 0;
+    for (int i0 = 0; i0 < a.batch_size; i0 += 256) {
+      const int i = i0 + (int)threadIdx.x;
+      cnt += __syncthreads_count(i < a.batch_size && a.req_branch_indptr[i] <= seg);
+    }
+    req = __builtin_amdgcn_readfirstlane(cnt > 0 ? cnt - 1 : 0);
   } else {
+    cint32* crb = as_const(a.req_branch_indptr);
     req = seg;
-    jb = a.req_branch_indptr[seg];
-    je = a.req_branch_indptr[seg + 1];
+    jb = crb[seg];
+    je = crb[seg + 1];
   }
-  const int tok0 = qo[jb];
-  const int tok1 = qo[je];
+  const int tok0 = cqo[jb];
+  const int tok1 = cqo[je];
   if (tok0 < 0 || tok1 < tok0 || tok1 > a.total_rows) {
     if (threadIdx.x == 0) atomicOr(&g_device_error, kErrRow);
     return;
@@ -139,7 +217,7 @@ attn_kernel(const AttnArgs a) {
   if (row0 >= nrows) return;
   const int row_end = min(nrows, row0 + ROWS);
 
-  int L = a.cache_seqlens[req];
+  int L = as_const(a.cache_seqlens)[req];
   {
     const int cap = a.page_table_stride << a.kv.log2_page;
     if (L > cap) {
@@ -157,57 +235,183 @@ attn_kernel(const AttnArgs a) {
     }
   }
 
+  const KvView kv = a.kv;
+  cint32* pt_row = as_const(a.page_table + (int64_t)req * a.page_table_stride);
+  const float c2 = a.scale_log2;
+  const int pmask = (1 << kv.log2_page) - 1;
+  const int64_t head_off = (int64_t)g * kv.head_stride;
+  // Segment tokens of this chunk's rows, and the draft keys [dlo, dhi) they
+  // can see (dlo, the start of the first row's branch, is set below).
+  const int tok_first = row0 / a.group;
+  const int tok_last = (row_end - 1) / a.group;
+  const int dhi = tok_last + 1;
+
   // ---- rows of this lane (column l16 of each 16-row block of S^T / O^T) --
   // Recomputed where needed rather than kept live across the key loop.
   auto row_valid = [&](int rb) { return row0 + rb * 16 + l16 < nrows; };
-  auto row_tok = [&](int rb) {  // segment token of the row (0 for padding rows)
+  auto row_tok = [&](int rb) {  // segment token of the row (tok_first for padding rows)
     const int rho = row0 + rb * 16 + l16;
-    return rho < nrows ? rho / a.group : 0;
+    return rho < nrows ? rho / a.group : tok_first;
   };
   auto row_out = [&](int rb) -> int64_t {  // index of (row, head) in [total_rows, Hq]
     const int rho = row0 + rb * 16 + l16;
     const int t = rho / a.group;
     return (int64_t)(tok0 + t) * a.num_qo_heads + g * a.group + (rho - t * a.group);
   };
-  // Segment token where the row's branch starts (draft masks only).
-  auto row_branch_start = [&](int rb) {
-    if constexpr (MODE == kModeNaive) return 0;
-    return qo[branch_of_row(qo, jb, je, tok0 + row_tok(rb))] - tok0;
-  };
   int rtok[RB] = {}, rbs[RB] = {};
   auto load_row_masks = [&]() {
 #pragma unroll
     for (int rb = 0; rb < RB; ++rb) {
       rtok[rb] = row_tok(rb);
-      rbs[rb] = row_branch_start(rb);
+      rbs[rb] = t_rbs[rtok[rb] - tok_first];
     }
   };
-  // Draft keys this chunk can see: [dlo, dhi) in segment tokens.
-  const int tok_first = row0 / a.group;
-  const int tok_last = (row_end - 1) / a.group;
+
+  // ---- per-tile building blocks ----------------------------------------
+
+  // A tile's K and V arrive in registers, 16 bytes per lane and load, in one
+  // of two shapes, and are written to the wave's LDS stage by (key, chunk):
+  //  * row shape (prefix tiles): load n covers keys n*TPI .. +TPI, lane reads
+  //    chunk lane % CPR of key n*TPI + lane / CPR -- whole key rows, so a load
+  //    reads contiguous runs (one 1 KB run per load for head-major pages);
+  //  * fragment shape (draft tiles, whose keys resolve their pages lane by
+  //    lane): load kb*KS + ks holds key kb*16 + l16, chunk ks*4 + g4.
+  // Prefix tiles start at a multiple of 32 and pages hold >= 16 tokens, so
+  // each 16-key half of a tile lies in one page whose id pg[kb] is
+  // wave-uniform (-1: no key in that half, or an id outside the pool).
+  auto load_rows = [&](const int (&pg)[2], int base, int end, u32x4 (&kr)[NI], u32x4 (&vr)[NI]) {
+    __amdgpu_buffer_rsrc_t rk[2], rv[2];
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+      const bool page_ok = pg[kb] >= 0;
+      const int64_t pbase = (int64_t)(page_ok ? pg[kb] : 0) * kv.page_stride;
+      rk[kb] = page_rsrc(kv.k + pbase, page_ok ? kv.page_bytes : 0);
+      rv[kb] = page_rsrc(kv.v + pbase, page_ok ? kv.page_bytes : 0);
+    }
+    const int chunk = lane % CPR;
+#pragma unroll
+    for (int n = 0; n < NI; ++n) {
+      const int key = base + n * TPI + lane / CPR;
+      const int kb = (n * TPI) / 16;
+      const int off = key < end ? (int)(((int64_t)(key & pmask) * kv.token_stride + head_off + chunk * 8) * 2)
+                                : kOutOfRange;
+      kr[n] = buf_load16(rk[kb], off);
+      vr[n] = buf_load16(rv[kb], off);
+    }
+  };
+  auto prefix_pages = [&](int base, int end, int (&pg)[2]) {
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+      const int first = base + kb * 16;
+      int id = first < end ? pt_row[first >> kv.log2_page] : -1;
+      if (id >= kv.num_pages) {
+        if (lane == 0) atomicOr(&g_device_error, kErrPage);
+      }
+      if ((uint32_t)id >= (uint32_t)kv.num_pages) id = -1;
+      pg[kb] = __builtin_amdgcn_readfirstlane(id);  // uniform by construction
+    }
+  };
+
+  // ---- prefix range of the key loop; its first tile is requested now -----
+  int p0 = 0, p1 = 0;
+  if constexpr (MODE == kModePrefix || MODE == kModeVerify) {
+    p0 = split * a.split_len;
+    p1 = min(L, p0 + a.split_len);
+    if (a.n_splits > 1 && p0 >= L) return;  // no keys in this split: no partial
+    if (p1 < p0) p1 = p0;
+  } else if constexpr (MODE == kModeNaive) {
+    p1 = L;
+  }
+  const int npt = (p1 - p0 + 31) >> 5;
+  u32x4 kr[NI], vr[NI];
+  int pg[2] = {-1, -1};
+  if constexpr (kMainLoop) {
+    if (w < npt) {
+      prefix_pages(p0 + w * 32, p1, pg);
+      load_rows(pg, p0 + w * 32, p1, kr, vr);
+    }
+  }
+
+  // ---- Q rows of the chunk (into registers now, into LDS below) ---------
+  constexpr int kQChunks = D / 8;
+  constexpr int QIT = (ROWS * kQChunks + 255) / 256;
+  u32x4 qtmp[kQInLds ? QIT : 1];
+  if constexpr (kQInLds) {
+#pragma unroll
+    for (int it = 0; it < QIT; ++it) {
+      const int idx = (int)threadIdx.x + it * 256;
+      const int r = idx / kQChunks, c = idx % kQChunks;
+      const int rho = row0 + r;
+      qtmp[it] = u32x4{0u, 0u, 0u, 0u};
+      if (idx < ROWS * kQChunks && rho < nrows) {
+        const int t = rho / a.group;
+        const int h = g * a.group + (rho - t * a.group);
+        qtmp[it] = *reinterpret_cast<const u32x4*>(a.q + (int64_t)(tok0 + t) * a.q_row_stride +
+                                                   (int64_t)h * a.q_head_stride + c * 8);
+      }
+    }
+  }
+
+  // ---- tree tables ---------------------------------------------------------
+  // t_bnd / t_dst: branch_qo_indptr[jb .. je] and draft_start[jb .. je) of the
+  // segment's branches; t_rbs: branch start of each token of the chunk;
+  // t_doff: element offset (head excluded) of draft key dlo + t, -1 when its
+  // slot lies past its draft block-table row or its page outside the pool.
   int dlo = 0;
-  if constexpr (MODE != kModeNaive) dlo = qo[branch_of_row(qo, jb, je, tok0 + tok_first)] - tok0;
-  const int dhi = tok_last + 1;
+  const int nb = je - jb;
+  const bool lds_bnd = nb <= NBCAP;
+  auto branch_at = [&](int x) -> int {  // local branch index of segment token x
+    if (lds_bnd) {
+      int lo = 0, hi = nb - 1;
+      while (lo < hi) {
+        const int mid = (lo + hi + 1) >> 1;
+        if (t_bnd[mid] - tok0 <= x) lo = mid; else hi = mid - 1;
+      }
+      return lo;
+    }
+    return branch_of_row(qo, jb, je, tok0 + x) - jb;
+  };
+  auto branch_start = [&](int jl) { return (lds_bnd ? t_bnd[jl] : qo[jb + jl]) - tok0; };
+  auto branch_dstart = [&](int jl) {
+    return lds_bnd ? t_dst[jl] : (a.draft_start ? a.draft_start[jb + jl] : 0);
+  };
+  if constexpr (kDraftKeys) {
+    if (lds_bnd) {
+      for (int t = threadIdx.x; t <= nb; t += 256) t_bnd[t] = qo[jb + t];
+      for (int t = threadIdx.x; t < nb; t += 256) t_dst[t] = a.draft_start ? a.draft_start[jb + t] : 0;
+    }
+    __syncthreads();
+    dlo = __builtin_amdgcn_readfirstlane(branch_start(branch_at(tok_first)));
+    for (int t = threadIdx.x; t <= tok_last - tok_first; t += 256)
+      t_rbs[t] = branch_start(branch_at(tok_first + t));
+    const int nk = min(dhi - dlo, KEYCAP);
+    const int dstride = a.draft_page_table_stride;
+    for (int t = threadIdx.x; t < nk; t += 256) {
+      const int x = dlo + t;
+      const int jl = branch_at(x);
+      const int slot = branch_dstart(jl) + (x - branch_start(jl));
+      int64_t off = -1;
+      if (slot >= 0 && (slot >> kv.log2_page) < dstride) {
+        const int page = a.draft_page_table[(int64_t)(jb + jl) * dstride + (slot >> kv.log2_page)];
+        if ((uint32_t)page < (uint32_t)kv.num_pages)
+          off = (int64_t)page * kv.page_stride + (int64_t)(slot & pmask) * kv.token_stride;
+      }
+      t_doff[t] = off;
+    }
+  }
+  if constexpr (kQInLds) {
+#pragma unroll
+    for (int it = 0; it < QIT; ++it) {
+      const int idx = (int)threadIdx.x + it * 256;
+      if (idx < ROWS * kQChunks)
+        *reinterpret_cast<u32x4*>(qs + (idx / kQChunks) * QSTR + (idx % kQChunks) * 8) = qtmp[it];
+    }
+  }
+  if constexpr (kQInLds || kDraftKeys) __syncthreads();
 
   // Q B-fragments: lane holds row rb*16 + l16, channels ks*32 + g4*8 .. +8.
   bf16x8 qf[kQInLds ? 1 : RB][KS];
-  if constexpr (kQInLds) {
-    // Cooperative copy of the chunk's rows into LDS; 16 bytes per thread step.
-    constexpr int kChunks = D / 8;
-    for (int idx = threadIdx.x; idx < ROWS * kChunks; idx += 256) {
-      const int r = idx / kChunks, c = idx % kChunks;
-      const int rho = row0 + r;
-      u32x4 x = {0u, 0u, 0u, 0u};
-      if (rho < nrows) {
-        const int t = rho / a.group;
-        const int h = g * a.group + (rho - t * a.group);
-        x = *reinterpret_cast<const u32x4*>(a.q + (int64_t)(tok0 + t) * a.q_row_stride +
-                                            (int64_t)h * a.q_head_stride + c * 8);
-      }
-      *reinterpret_cast<u32x4*>(qs + r * QSTR + c * 8) = x;
-    }
-    __syncthreads();
-  } else if constexpr (kNeedQ) {
+  if constexpr (!kQInLds && kNeedQ) {
 #pragma unroll
     for (int rb = 0; rb < RB; ++rb) {
       const int rho = row0 + rb * 16 + l16;
@@ -228,101 +432,88 @@ attn_kernel(const AttnArgs a) {
     }
   };
 
-  const KvView kv = a.kv;
-  cint32* pt_row = as_const(a.page_table + (int64_t)req * a.page_table_stride);
-  const float c2 = a.scale_log2;
-  const int pmask = (1 << kv.log2_page) - 1;
-  const int64_t head_off = (int64_t)g * kv.head_stride + g4 * 8;
-
-  // ---- per-tile building blocks ----------------------------------------
-
-  // Prefix tiles start at a multiple of 32 and pages hold >= 16 tokens, so
-  // each 16-key half of a tile lies in one page whose id pg[kb] is
-  // wave-uniform (-1: no key in that half, or an id outside the pool).
-  auto load_prefix = [&](const uint16_t* pool, const int (&pg)[2], int base, int end,
-                         bf16x8 (&r)[2][KS]) {
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
-      const int key = base + kb * 16 + l16;
-      const bool page_ok = pg[kb] >= 0;
-      const __amdgpu_buffer_rsrc_t rs =
-          page_rsrc(pool + (int64_t)(page_ok ? pg[kb] : 0) * kv.page_stride, page_ok ? kv.page_bytes : 0);
-      const int off = key < end ? (int)(((int64_t)(key & pmask) * kv.token_stride + head_off) * 2)
-                                : kOutOfRange;
-#pragma unroll
-      for (int ks = 0; ks < KS; ++ks) r[kb][ks] = __builtin_bit_cast(bf16x8, buf_load16(rs, off + ks * 64));
-    }
-  };
-  auto load_k_prefix = [&](const int (&pg)[2], int base, int end, bf16x8 (&kr)[2][KS]) {
-    load_prefix(kv.k, pg, base, end, kr);
-  };
-  auto load_v_prefix = [&](const int (&pg)[2], int base, int end, bf16x8 (&vr)[2][KS]) {
-    load_prefix(kv.v, pg, base, end, vr);
-  };
-  auto prefix_pages = [&](int base, int end, int (&pg)[2]) {
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
-      const int first = base + kb * 16;
-      int id = first < end ? pt_row[first >> kv.log2_page] : -1;
-      if (id >= kv.num_pages) {
-        if (lane == 0) atomicOr(&g_device_error, kErrPage);
-      }
-      if ((uint32_t)id >= (uint32_t)kv.num_pages) id = -1;
-      pg[kb] = __builtin_amdgcn_readfirstlane(id);  // uniform by construction
-    }
-  };
-  // Draft tiles: keys are segment tokens [base, base+32); each lane resolves
-  // its own key's branch, slot and page (-2: no key, -1: bad page).
+  // Draft tiles: keys are segment tokens [base, base+32); off[kb] is the
+  // offset of key base + kb*16 + l16 (-2: no key, -1: bad slot or page).
   auto draft_offsets = [&](int base, int end, int64_t (&off)[2]) {
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
       const int key = base + kb * 16 + l16;
-      off[kb] = -2;
+      int64_t o = -2;
       if (key < end) {
-        off[kb] = draft_offset(kv, qo, a.draft_page_table, a.draft_page_table_stride, a.draft_start,
-                               jb, je, key, g);
-        if (off[kb] == -1) atomicOr(&g_device_error, kErrPage);
+        if (key - dlo < KEYCAP) {
+          o = t_doff[key - dlo];
+          if (o >= 0) o += head_off;
+        } else {
+          o = draft_offset(kv, qo, a.draft_page_table, a.draft_page_table_stride, a.draft_start, jb, je,
+                           key, g);
+        }
+        if (o == -1) atomicOr(&g_device_error, kErrPage);
       }
+      off[kb] = o;
     }
   };
-  auto load_draft_at = [&](const int64_t (&off)[2], bf16x8 (&kr)[2][KS], bf16x8 (&vr)[2][KS]) {
+  // Lanes without a key read the pool's first row (always mapped); their K is
+  // masked later and their V is zeroed when staged (bit kb of `ok`), so the
+  // select does not wait for the load here.
+  auto load_draft_at = [&](const int64_t (&off)[2], u32x4 (&kr)[NI], u32x4 (&vr)[NI], int& ok) {
+    ok = 0;
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
-      const bool ok = off[kb] >= 0;
-      const int64_t o2 = ok ? off[kb] + g4 * 8 : (int64_t)(g4 * 8);
+      const bool valid = off[kb] >= 0;
+      ok |= valid ? (1 << kb) : 0;
+      const int64_t o2 = (valid ? off[kb] : 0) + g4 * 8;
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks) {
-        kr[kb][ks] = *reinterpret_cast<const bf16x8*>(kv.k + o2 + ks * 32);
-        const u32x4 x = *reinterpret_cast<const u32x4*>(kv.v + o2 + ks * 32);
-        vr[kb][ks] = __builtin_bit_cast(bf16x8, ok ? x : u32x4{0u, 0u, 0u, 0u});
+        kr[kb * KS + ks] = *reinterpret_cast<const u32x4*>(kv.k + o2 + ks * 32);
+        vr[kb * KS + ks] = *reinterpret_cast<const u32x4*>(kv.v + o2 + ks * 32);
       }
     }
   };
-  auto load_draft = [&](int base, int end, bf16x8 (&kr)[2][KS], bf16x8 (&vr)[2][KS]) {
+  auto load_draft = [&](int base, int end, u32x4 (&kr)[NI], u32x4 (&vr)[NI], int& ok) {
     int64_t off[2];
     draft_offsets(base, end, off);
-    load_draft_at(off, kr, vr);
+    load_draft_at(off, kr, vr, ok);
+  };
+  // Writes a tile's K and V rows into the wave's stage (row = key, RS stride).
+  auto stage = [&](const u32x4 (&kr)[NI], const u32x4 (&vr)[NI], bool rows, int ok, uint16_t* st) {
+#pragma unroll
+    for (int r = 0; r < NI; ++r) {
+      int key, ch;
+      u32x4 v = vr[r];
+      if (rows) {
+        key = r * TPI + lane / CPR;
+        ch = lane % CPR;
+      } else {
+        key = (r / KS) * 16 + l16;
+        ch = (r % KS) * 4 + g4;
+        if (!((ok >> (r / KS)) & 1)) v = u32x4{0u, 0u, 0u, 0u};
+      }
+      *reinterpret_cast<u32x4*>(st + key * RS + ch * 8) = kr[r];
+      *reinterpret_cast<u32x4*>(st + 32 * RS + key * RS + ch * 8) = v;
+    }
   };
 
-  // The fused verify epilogue starts with the first draft tile of the chunk;
-  // its addresses are resolved now so that its loads can be issued as soon as
-  // the prefix loop ends.
-  int64_t doff0[2] = {-2, -2};
-  if constexpr (kEpilogueDraft) {
-    if (dlo < dhi) draft_offsets(dlo, dhi, doff0);
-  }
-  bf16x8 dkr[2][KS], dvr[2][KS];
+  u32x4 dkr[NI], dvr[NI];
+  int dok = 0;
   bool draft_loaded = false;
 
   // S^T for one tile: s[rb][kb] holds keys kb*16 + 4*g4 + i of row rb*16 + l16.
-  auto scores = [&](const bf16x8 (&kr)[2][KS], f32x4 (&s)[RB][2]) {
+  auto kfrag = [&](const uint16_t* st, int kb, int ks) -> bf16x8 {
+    return *reinterpret_cast<const bf16x8*>(st + (kb * 16 + l16) * RS + (ks * 4 + g4) * 8);
+  };
+  auto scores = [&](const uint16_t* st, f32x4 (&s)[RB][2]) {
+    bf16x8 kf[2][KS];
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) kf[kb][ks] = kfrag(st, kb, ks);
 #pragma unroll
     for (int rb = 0; rb < RB; ++rb) {
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb) {
         f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int ks = 0; ks < KS; ++ks) acc = mfma16(kr[kb][ks], qfrag(rb, ks), acc);
+        for (int ks = 0; ks < KS; ++ks) acc = mfma16(kf[kb][ks], qfrag(rb, ks), acc);
         s[rb][kb] = acc;
       }
     }
@@ -364,22 +555,38 @@ attn_kernel(const AttnArgs a) {
   // Online softmax update in base 2.  m is the carried max (raised only past
   // the slack), alpha the factor the accumulator must be scaled by, pf the
   // weights as P^T B-fragments.  Returns whether this lane needs a rescale.
+  // A row's max only moves when the max over its 32 keys exceeds m + slack;
+  // each lane checks its own 8 keys first, and only when some lane of the
+  // wave finds such a key are the row maxima formed across lanes.
   auto softmax = [&](f32x4 (&s)[RB][2], float (&m)[RB], float (&l)[RB], float (&alpha)[RB],
                      bf16x8 (&pf)[RB]) -> bool {
-    bool rescale = false;
+    float lm[RB];
+    bool raise = false;
 #pragma unroll
     for (int rb = 0; rb < RB; ++rb) {
-      float mx = fmaxf(fmaxf(fmaxf(s[rb][0][0], s[rb][0][1]), fmaxf(s[rb][0][2], s[rb][0][3])),
-                       fmaxf(fmaxf(s[rb][1][0], s[rb][1][1]), fmaxf(s[rb][1][2], s[rb][1][3])));
-      mx = fmaxf(mx, __shfl_xor(mx, 16));
-      mx = fmaxf(mx, __shfl_xor(mx, 32));
-      mx *= c2;
-      const float mold = m[rb];
-      const float mnew = mx > mold + kMaxSlack ? mx : mold;
-      const float ms = mnew == kNegInf ? 0.f : mnew;
-      alpha[rb] = mnew == mold ? 1.f : fast_exp2(mold - ms);
-      rescale |= mnew != mold && mold != kNegInf;
-      m[rb] = mnew;
+      lm[rb] = fmaxf(fmaxf(fmaxf(s[rb][0][0], s[rb][0][1]), fmaxf(s[rb][0][2], s[rb][0][3])),
+                     fmaxf(fmaxf(s[rb][1][0], s[rb][1][1]), fmaxf(s[rb][1][2], s[rb][1][3])));
+      raise |= lm[rb] * c2 > m[rb] + kMaxSlack;
+    }
+    bool rescale = false;
+    if (__any(raise)) {
+#pragma unroll
+      for (int rb = 0; rb < RB; ++rb) {
+        const float mx = rowgroup_max(lm[rb]) * c2;
+        const float mold = m[rb];
+        const float mnew = mx > mold + kMaxSlack ? mx : mold;
+        const float ms = mnew == kNegInf ? 0.f : mnew;
+        alpha[rb] = mnew == mold ? 1.f : fast_exp2(mold - ms);
+        rescale |= mnew != mold && mold != kNegInf;
+        m[rb] = mnew;
+      }
+    } else {
+#pragma unroll
+      for (int rb = 0; rb < RB; ++rb) alpha[rb] = 1.f;
+    }
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb) {
+      const float ms = m[rb] == kNegInf ? 0.f : m[rb];
       float p[8];
       float sum = 0.f;
 #pragma unroll
@@ -398,33 +605,15 @@ attn_kernel(const AttnArgs a) {
     return rescale;
   };
 
-  // Writes a tile's V rows to this wave's LDS stage: row = key, VSTR stride.
-  auto stage_v = [&](const bf16x8 (&vr)[2][KS], uint16_t* vs) {
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
-#pragma unroll
-      for (int ks = 0; ks < KS; ++ks) {
-        const u32x4 x = __builtin_bit_cast(u32x4, vr[kb][ks]);
-        u32x2* dst = reinterpret_cast<u32x2*>(vs + (kb * 16 + l16) * VSTR + ks * 32 + g4 * 8);
-        dst[0] = u32x2{x[0], x[1]};
-        dst[1] = u32x2{x[2], x[3]};
-      }
-    }
-  };
-
   // V^T A-fragment of channel block db: lane holds channel db*16 + l16 of keys
-  // kb*16 + 4*g4 + i, the key order of P^T.
-  auto vt_frag = [&](const uint16_t* vs, int db) -> bf16x8 {
-    const uint16_t* vb = vs + (4 * g4) * VSTR + db * 16 + l16;
-    uint32_t e[8];
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
-#pragma unroll
-      for (int i = 0; i < 4; ++i) e[kb * 4 + i] = vb[(kb * 16 + i) * VSTR];
-    }
-    const u32x4 pk = {e[0] | (e[1] << 16), e[2] | (e[3] << 16), e[4] | (e[5] << 16),
-                      e[6] | (e[7] << 16)};
-    return __builtin_bit_cast(bf16x8, pk);
+  // kb*16 + 4*g4 + j (k slot kb*4 + j), the key order of P^T.  Lane a of each
+  // 16-lane group addresses key row 4*g4 + a/4, channels db*16 + 4*(a%4) ..+4;
+  // the transposing read hands lane l16 element l16%4 of lanes l16/4 + 4j.
+  auto vt_frag = [&](const uint16_t* st, int db) -> bf16x8 {
+    const uint16_t* vb = st + 32 * RS + (4 * g4 + (l16 >> 2)) * RS + db * 16 + 4 * (l16 & 3);
+    const i16x4 lo = lds_read_tr16(vb);
+    const i16x4 hi = lds_read_tr16(vb + 16 * RS);
+    return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
   };
 
   // Merged pass state of this lane's rows for the channel blocks this wave
@@ -433,21 +622,11 @@ attn_kernel(const AttnArgs a) {
   float lse2[RB];
 
   if constexpr (kMainLoop) {
-    int p0 = 0, p1 = 0;
-    if constexpr (MODE == kModePrefix || MODE == kModeVerify) {
-      p0 = split * a.split_len;
-      p1 = min(L, p0 + a.split_len);
-      if (a.n_splits > 1 && p0 >= L) return;  // no keys in this split: no partial
-      if (p1 < p0) p1 = p0;
-    } else if constexpr (MODE == kModeNaive) {
-      p1 = L;
-    }
     int d0 = 0, d1 = 0;
     if constexpr (MODE == kModeDraft || MODE == kModeNaive) {
       d0 = dlo;
       d1 = dhi;
     }
-    const int npt = (p1 - p0 + 31) >> 5;
     const int ndt = (d1 - d0 + 31) >> 5;
     const int nt = npt + ndt;
     if constexpr (MODE == kModeDraft || MODE == kModeNaive) load_row_masks();
@@ -461,10 +640,11 @@ attn_kernel(const AttnArgs a) {
 #pragma unroll
       for (int db = 0; db < DB; ++db) o[rb][db] = f32x4{0.f, 0.f, 0.f, 0.f};
     }
-    uint16_t* stage = reinterpret_cast<uint16_t*>(smem) + w * 2 * STAGE;
+    uint16_t* st = reinterpret_cast<uint16_t*>(smem) + w * STAGE;
 
     // Tile tau covers prefix keys p0 + 32*tau .. for tau < npt, then draft
-    // tokens d0 + 32*(tau - npt) .. .  Draft tiles load K and V together.
+    // tokens d0 + 32*(tau - npt) .. .  pg always holds the pages of the next
+    // prefix tile to be loaded.
     auto pages_of = [&](int tau, int (&pg)[2]) {
       if (tau < npt) {
         prefix_pages(p0 + tau * 32, p1, pg);
@@ -473,50 +653,42 @@ attn_kernel(const AttnArgs a) {
         pg[1] = -1;
       }
     };
-
-    bf16x8 kr[2][KS], vr[2][KS];
-    int pg[2] = {-1, -1};
+    int ok = 3;
+    auto issue = [&](int tau) {
+      if (tau < npt) {
+        load_rows(pg, p0 + tau * 32, p1, kr, vr);
+        ok = 3;
+      } else {
+        load_draft(d0 + (tau - npt) * 32, d1, kr, vr, ok);
+      }
+    };
     // Prefix-only launches (pass A, verify) prefetch without branches: past the
     // wave's last tile the "next" tile is the current one again (L2-resident,
     // never used), so the load sequence and its wait counts are the same every
     // iteration.
     constexpr bool kPrefixOnly = MODE == kModePrefix || MODE == kModeVerify;
     if (w < nt) {
-      pages_of(w, pg);
-      if (w < npt) {
-        load_v_prefix(pg, p0 + w * 32, p1, vr);
-        load_k_prefix(pg, p0 + w * 32, p1, kr);
-      } else {
-        load_draft(d0 + (w - npt) * 32, d1, kr, vr);
-      }
+      if (w >= npt) issue(w);  // a draft tile (prefix tiles were requested above)
       pages_of(w + 4 < nt ? w + 4 : w, pg);
     }
-    int buf = 0;
     for (int tau = w; tau < nt; tau += 4) {
       const int nxt = tau + 4;
       const bool is_prefix = tau < npt;
       const int base = is_prefix ? p0 + tau * 32 : d0 + (tau - npt) * 32;
       const int end = is_prefix ? p1 : d1;
-      uint16_t* vs = stage + buf * STAGE;
-      buf ^= 1;
-      stage_v(vr, vs);
-      f32x4 s[RB][2];
+      // Stage this tile, then reuse its registers for the next tile's loads,
+      // which then have a whole iteration to land.
+      stage(kr, vr, is_prefix, ok, st);
       if constexpr (kPrefixOnly) {
         const int ld = nxt < nt ? nxt : tau;
-        load_v_prefix(pg, p0 + ld * 32, p1, vr);
-        scores(kr, s);
-        load_k_prefix(pg, p0 + ld * 32, p1, kr);
+        load_rows(pg, p0 + ld * 32, p1, kr, vr);
         pages_of(nxt + 4 < nt ? nxt + 4 : ld, pg);
       } else {
-        if (nxt < npt) load_v_prefix(pg, p0 + nxt * 32, p1, vr);
-        scores(kr, s);
-        if (nxt < npt) {
-          load_k_prefix(pg, p0 + nxt * 32, p1, kr);
-        } else if (nxt < nt) {
-          load_draft(d0 + (nxt - npt) * 32, d1, kr, vr);
-        }
+        if (nxt < nt) issue(nxt);
         if (nxt + 4 < nt) pages_of(nxt + 4, pg);
       }
+      f32x4 s[RB][2];
+      scores(st, s);
       if (!is_prefix) {
         mask_draft(base, end, s);
       } else if (base + 32 > end) {
@@ -532,7 +704,7 @@ attn_kernel(const AttnArgs a) {
       }
 #pragma unroll
       for (int db = 0; db < DB; ++db) {
-        const bf16x8 vf = vt_frag(vs, db);
+        const bf16x8 vf = vt_frag(st, db);
 #pragma unroll
         for (int rb = 0; rb < RB; ++rb) o[rb][db] = mfma16(vf, pf[rb], o[rb][db]);
       }
@@ -541,17 +713,16 @@ attn_kernel(const AttnArgs a) {
     mfma_drain();
     if constexpr (MODE == kModeVerify) {
       if (a.n_splits == 1 && dlo < dhi) {
-        load_draft_at(doff0, dkr, dvr);  // lands while the waves merge
+        int64_t off[2];
+        draft_offsets(dlo, dhi, off);
+        load_draft_at(off, dkr, dvr, dok);  // lands while the waves merge
         draft_loaded = true;
       }
     }
 
     // ---- merge the four waves' states (LSE identity) ----------------------
 #pragma unroll
-    for (int rb = 0; rb < RB; ++rb) {
-      l[rb] += __shfl_xor(l[rb], 16);
-      l[rb] += __shfl_xor(l[rb], 32);
-    }
+    for (int rb = 0; rb < RB; ++rb) l[rb] = rowgroup_sum(l[rb]);
     if (g4 == 0) {
 #pragma unroll
       for (int rb = 0; rb < RB; ++rb) {
@@ -615,7 +786,9 @@ attn_kernel(const AttnArgs a) {
   if constexpr (kFinish) {
     if constexpr (MODE == kModeVerifyFinish) {
       if (dlo < dhi) {
-        load_draft_at(doff0, dkr, dvr);  // lands while the partials merge
+        int64_t off[2];
+        draft_offsets(dlo, dhi, off);
+        load_draft_at(off, dkr, dvr, dok);  // lands while the partials merge
         draft_loaded = true;
       }
     }
@@ -661,7 +834,7 @@ attn_kernel(const AttnArgs a) {
       // blocks of o_B, then merges with pass A by the LSE identity.
       __syncthreads();  // the exchange buffer is reused as staging below
       load_row_masks();
-      uint16_t* vs = reinterpret_cast<uint16_t*>(smem) + w * STAGE;
+      uint16_t* st = reinterpret_cast<uint16_t*>(smem) + w * STAGE;
       float mB[RB], lB[RB];
       f32x4 oB[RB][DBW];
 #pragma unroll
@@ -672,21 +845,16 @@ attn_kernel(const AttnArgs a) {
         for (int dbl = 0; dbl < DBW; ++dbl) oB[rb][dbl] = f32x4{0.f, 0.f, 0.f, 0.f};
       }
       for (int base = dlo; base < dhi; base += 32) {
-        bf16x8 kr[2][KS], vr[2][KS];
         if (base == dlo && draft_loaded) {
-#pragma unroll
-          for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-            for (int ks = 0; ks < KS; ++ks) {
-              kr[kb][ks] = dkr[kb][ks];
-              vr[kb][ks] = dvr[kb][ks];
-            }
+          stage(dkr, dvr, false, dok, st);
         } else {
-          load_draft(base, dhi, kr, vr);
+          u32x4 kr2[NI], vr2[NI];
+          int ok2;
+          load_draft(base, dhi, kr2, vr2, ok2);
+          stage(kr2, vr2, false, ok2, st);
         }
-        stage_v(vr, vs);
         f32x4 s[RB][2];
-        scores(kr, s);
+        scores(st, s);
         mask_draft(base, dhi, s);
         float alpha[RB];
         bf16x8 pf[RB];
@@ -697,7 +865,7 @@ attn_kernel(const AttnArgs a) {
           for (int dbl = 0; dbl < DBW; ++dbl) oB[rb][dbl] *= alpha[rb];
 #pragma unroll
         for (int dbl = 0; dbl < DBW; ++dbl) {
-          const bf16x8 vf = vt_frag(vs, w * DBW + dbl);
+          const bf16x8 vf = vt_frag(st, w * DBW + dbl);
 #pragma unroll
           for (int rb = 0; rb < RB; ++rb) oB[rb][dbl] = mfma16(vf, pf[rb], oB[rb][dbl]);
         }
@@ -705,8 +873,7 @@ attn_kernel(const AttnArgs a) {
       mfma_drain();
 #pragma unroll
       for (int rb = 0; rb < RB; ++rb) {
-        lB[rb] += __shfl_xor(lB[rb], 16);
-        lB[rb] += __shfl_xor(lB[rb], 32);
+        lB[rb] = rowgroup_sum(lB[rb]);
         const float lseB = lB[rb] > 0.f ? mB[rb] + fast_log2(lB[rb]) : kNegInf;
         const float invB = lB[rb] > 0.f ? 1.f / lB[rb] : 0.f;
         float wa, wb, lt;
