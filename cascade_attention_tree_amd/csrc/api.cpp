@@ -96,6 +96,8 @@ cascade_status check_kv(const cascade_paged_kv* kv) {
     return fail(CASCADE_ERR_SHAPE, "kv strides must be >= 0");
   if (kv->page_stride % 8 || kv->token_stride % 8 || kv->head_stride % 8)
     return fail(CASCADE_ERR_UNSUPPORTED, "kv strides must be multiples of 8 elements");
+  if (kv->token_stride < kv->head_dim)
+    return fail(CASCADE_ERR_UNSUPPORTED, "token_stride must be >= head_dim (rows of one kv head may not overlap)");
   if (!aligned16(kv->k) || !aligned16(kv->v))
     return fail(CASCADE_ERR_UNSUPPORTED, "kv->k and kv->v must be 16-byte aligned");
   if (page_extent_bytes(kv) >= (1ll << 30))

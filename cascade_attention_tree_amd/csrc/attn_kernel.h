@@ -278,25 +278,34 @@ attn_kernel(const AttnArgs a) {
   //    lane): load kb*KS + ks holds key kb*16 + l16, chunk ks*4 + g4.
   // Prefix tiles start at a multiple of 32 and pages hold >= 16 tokens, so
   // each 16-key half of a tile lies in one page whose id pg[kb] is
-  // wave-uniform (-1: no key in that half, or an id outside the pool).
+  // wave-uniform (-1: no key in that half, or an id outside the pool).  The
+  // half's buffer descriptors start at its first key and end after the row
+  // of its last valid key, so keys past `end` (and bad pages) read zeros and
+  // the loads need no per-lane bounds arithmetic: load n of a lane reads at
+  // the fixed byte offset lane_off[n % NV] (key (n*TPI) % 16 + lane / CPR of
+  // the half, chunk lane % CPR; rows are token_stride >= head_dim apart).
+  constexpr int NV = 16 / TPI;
+  int lane_off[NV];
+#pragma unroll
+  for (int i = 0; i < NV; ++i)
+    lane_off[i] = (int)(((int64_t)(i * TPI + lane / CPR) * kv.token_stride + head_off + (lane % CPR) * 8) * 2);
   auto load_rows = [&](const int (&pg)[2], int base, int end, u32x4 (&kr)[NI], u32x4 (&vr)[NI]) {
     __amdgpu_buffer_rsrc_t rk[2], rv[2];
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
-      const bool page_ok = pg[kb] >= 0;
-      const int64_t pbase = (int64_t)(page_ok ? pg[kb] : 0) * kv.page_stride;
-      rk[kb] = page_rsrc(kv.k + pbase, page_ok ? kv.page_bytes : 0);
-      rv[kb] = page_rsrc(kv.v + pbase, page_ok ? kv.page_bytes : 0);
+      const int first = base + kb * 16;
+      const int nvalid = min(max(end - first, 0), 16);
+      const bool ok = pg[kb] >= 0 && nvalid > 0;
+      const int64_t hbase = (int64_t)(ok ? pg[kb] : 0) * kv.page_stride + (int64_t)(first & pmask) * kv.token_stride;
+      const int bytes = ok ? (int)(((int64_t)(nvalid - 1) * kv.token_stride + head_off + D) * 2) : 0;
+      rk[kb] = page_rsrc(kv.k + hbase, bytes);
+      rv[kb] = page_rsrc(kv.v + hbase, bytes);
     }
-    const int chunk = lane % CPR;
 #pragma unroll
     for (int n = 0; n < NI; ++n) {
-      const int key = base + n * TPI + lane / CPR;
       const int kb = (n * TPI) / 16;
-      const int off = key < end ? (int)(((int64_t)(key & pmask) * kv.token_stride + head_off + chunk * 8) * 2)
-                                : kOutOfRange;
-      kr[n] = buf_load16(rk[kb], off);
-      vr[n] = buf_load16(rv[kb], off);
+      kr[n] = buf_load16(rk[kb], lane_off[n % NV]);
+      vr[n] = buf_load16(rv[kb], lane_off[n % NV]);
     }
   };
   auto prefix_pages = [&](int base, int end, int (&pg)[2]) {
@@ -553,8 +562,9 @@ attn_kernel(const AttnArgs a) {
   };
 
   // Online softmax update in base 2.  m is the carried max (raised only past
-  // the slack), alpha the factor the accumulator must be scaled by, pf the
-  // weights as P^T B-fragments.  Returns whether this lane needs a rescale.
+  // the slack), l the lane's partial row sum (its 8 keys of each tile, fp32),
+  // alpha the factor the accumulator must be scaled by, pf the weights as P^T
+  // B-fragments.  Returns whether this lane needs a rescale.
   // A row's max only moves when the max over its 32 keys exceeds m + slack;
   // each lane checks its own 8 keys first, and only when some lane of the
   // wave finds such a key are the row maxima formed across lanes.

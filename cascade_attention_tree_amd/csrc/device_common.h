@@ -92,11 +92,11 @@ __device__ __forceinline__ int64_t draft_offset(const KvView& kv, const int32_t*
   return paged_offset(kv, dpt + (int64_t)j * dstride, slot, g);
 }
 
-// Buffer descriptor over one page (gfx9-family raw buffer: stride 0, dword 3
-// = 0x00020000).  A lane whose byte offset lies past `bytes` reads zeros, so a
-// partially valid tile needs neither branches nor selects.
+// Buffer descriptor over a byte range (gfx9-family raw buffer: stride 0,
+// dword 3 = 0x00020000).  A lane whose 16-byte read does not lie inside
+// `bytes` reads zeros, so a partially valid tile needs neither branches nor
+// selects.
 constexpr int kBufFlags = 0x00020000;
-constexpr int kOutOfRange = 0x7ff00000;  // a byte offset beyond any page
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t page_rsrc(const uint16_t* base, int bytes) {
   return __builtin_amdgcn_make_buffer_rsrc((void*)base, 0, bytes, kBufFlags);
 }

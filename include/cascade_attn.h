@@ -68,7 +68,8 @@ typedef enum { CASCADE_F32 = 0, CASCADE_BF16 = 1 } cascade_dtype;
 /* One layer's paged K and V (bf16).  Element (page, slot, kv_head, c) of K is at
  * k + page*page_stride + slot*token_stride + kv_head*head_stride + c.
  * Requirements: head_dim in {64, 128}; page_size a power of two in [16, 4096];
- * the three strides are multiples of 8 elements; k and v 16-byte aligned.
+ * the three strides are multiples of 8 elements, token_stride >= head_dim;
+ * k and v 16-byte aligned.
  * The default layout [num_pages, page_size, Hkv, head_dim] has
  * page_stride = page_size*Hkv*head_dim, token_stride = Hkv*head_dim,
  * head_stride = head_dim. */

@@ -76,6 +76,10 @@ def test_rejects_before_launch():
     kv.token_stride = 1020
     assert call_verify(q, kv, t) == B.CASCADE_ERR_UNSUPPORTED
     q, kv, t = make()
+    kv.token_stride = kv.head_dim - 8   # rows of one kv head would overlap
+    assert call_verify(q, kv, t) == B.CASCADE_ERR_UNSUPPORTED
+    assert b"token_stride" in lib.cascade_last_error()
+    q, kv, t = make()
     t.page_table_stride = 3          # 3 pages of 16 cannot hold L = 100
     assert call_verify(q, kv, t) == B.CASCADE_ERR_SHAPE
     q, kv, t = make()
