@@ -461,20 +461,28 @@ attn_kernel(const AttnArgs a) {
       off[kb] = o;
     }
   };
-  // Lanes without a key read the pool's first row (always mapped); their K is
-  // masked later and their V is zeroed when staged (bit kb of `ok`), so the
-  // select does not wait for the load here.
+  // Lanes without a key load nothing (all such lanes of all workgroups would
+  // otherwise hit one row) and hold zeros; their K is masked later and their
+  // V is zero (bit kb of `ok` also zeroes it when staged).
   auto load_draft_at = [&](const int64_t (&off)[2], u32x4 (&kr)[NI], u32x4 (&vr)[NI], int& ok) {
     ok = 0;
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
       const bool valid = off[kb] >= 0;
       ok |= valid ? (1 << kb) : 0;
-      const int64_t o2 = (valid ? off[kb] : 0) + g4 * 8;
+      if (valid) {
+        const int64_t o2 = off[kb] + g4 * 8;
 #pragma unroll
-      for (int ks = 0; ks < KS; ++ks) {
-        kr[kb * KS + ks] = *reinterpret_cast<const u32x4*>(kv.k + o2 + ks * 32);
-        vr[kb * KS + ks] = *reinterpret_cast<const u32x4*>(kv.v + o2 + ks * 32);
+        for (int ks = 0; ks < KS; ++ks) {
+          kr[kb * KS + ks] = *reinterpret_cast<const u32x4*>(kv.k + o2 + ks * 32);
+          vr[kb * KS + ks] = *reinterpret_cast<const u32x4*>(kv.v + o2 + ks * 32);
+        }
+      } else {
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+          kr[kb * KS + ks] = u32x4{0u, 0u, 0u, 0u};
+          vr[kb * KS + ks] = u32x4{0u, 0u, 0u, 0u};
+        }
       }
     }
   };
@@ -543,7 +551,7 @@ attn_kernel(const AttnArgs a) {
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
         for (int i = 0; i < 4; ++i)
-          if (base + kb * 16 + g4 * 4 + i >= end) s[rb][kb][i] = kNegInf;
+          s[rb][kb][i] = base + kb * 16 + g4 * 4 + i < end ? s[rb][kb][i] : kNegInf;
   };
   // Draft keys: the bound `end` and the in-branch ancestor rule (rtok / rbs
   // must have been loaded by load_row_masks).
@@ -555,7 +563,8 @@ attn_kernel(const AttnArgs a) {
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           const int key = base + kb * 16 + g4 * 4 + i;
-          if (!(key < end && draft_visible(rtok[rb], rbs[rb], key))) s[rb][kb][i] = kNegInf;
+          const bool vis = (key < end) & draft_visible(rtok[rb], rbs[rb], key);
+          s[rb][kb][i] = vis ? s[rb][kb][i] : kNegInf;
         }
       }
     }

@@ -73,7 +73,7 @@ __device__ __forceinline__ int request_of_branch(const int32_t* rb, int batch, i
 // at token t whose branch starts at token bs sees draft key token kt iff kt
 // lies in its own branch at or before it.
 __device__ __forceinline__ bool draft_visible(int t, int bs, int kt) {
-  return kt >= bs && kt <= t;
+  return (kt >= bs) & (kt <= t);  // bitwise: a select, not a branch, per key
 }
 
 // Physical offset of draft token `kt` (numbered from the first row of branch
