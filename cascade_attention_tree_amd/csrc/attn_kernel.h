@@ -146,9 +146,14 @@ attn_kernel(const AttnArgs a) {
   constexpr int UNION_BYTES = STAGE_BYTES > XBYTES ? STAGE_BYTES : XBYTES;
   constexpr bool kMainLoop = MODE <= kModeNaive;
   constexpr bool kFinish = MODE == kModePrefixFinish || MODE == kModeVerifyFinish;
-  constexpr bool kEpilogueDraft = MODE == kModeVerify || MODE == kModeVerifyFinish;
-  constexpr bool kDraftKeys = MODE == kModeDraft || MODE == kModeNaive || kEpilogueDraft;
-  constexpr bool kNeedQ = MODE != kModePrefixFinish;
+  constexpr bool kDraftKeys = MODE == kModeDraft || MODE == kModeNaive || MODE == kModeVerify;
+  // In the fused verify launch the request's draft tiles are taken by one
+  // wave, after its share of the prefix tiles, into its own online softmax
+  // state; the wave merge below then combines pass A and pass B with the same
+  // LSE identity as the prefix partial states.  Wave 3 has the fewest prefix
+  // tiles (tiles go round-robin from wave 0).
+  constexpr int kDraftWave = 3;
+  constexpr bool kNeedQ = !kFinish;
   // Large row tiles keep Q in LDS (read per tile as B-fragments) so that the
   // architectural VGPRs stay free for K/V in flight and the softmax.
   constexpr bool kQInLds = kNeedQ && RB * KS >= 16;
@@ -326,7 +331,9 @@ attn_kernel(const AttnArgs a) {
   if constexpr (MODE == kModePrefix || MODE == kModeVerify) {
     p0 = split * a.split_len;
     p1 = min(L, p0 + a.split_len);
-    if (a.n_splits > 1 && p0 >= L) return;  // no keys in this split: no partial
+    // No keys in this split: no partial (split 0 of a verify launch also
+    // holds the draft tiles, so it always writes one).
+    if (a.n_splits > 1 && p0 >= L && (MODE == kModePrefix || split != 0)) return;
     if (p1 < p0) p1 = p0;
   } else if constexpr (MODE == kModeNaive) {
     p1 = L;
@@ -510,9 +517,6 @@ attn_kernel(const AttnArgs a) {
     }
   };
 
-  u32x4 dkr[NI], dvr[NI];
-  int dok = 0;
-  bool draft_loaded = false;
 
   // S^T for one tile: s[rb][kb] holds keys kb*16 + 4*g4 + i of row rb*16 + l16.
   auto kfrag = [&](const uint16_t* st, int kb, int ks) -> bf16x8 {
@@ -690,6 +694,10 @@ attn_kernel(const AttnArgs a) {
       if (w >= npt) issue(w);  // a draft tile (prefix tiles were requested above)
       pages_of(w + 4 < nt ? w + 4 : w, pg);
     }
+    // The draft wave of a verify launch: its first draft tile is requested in
+    // place of the prefetch past its last prefix tile.
+    const bool verify_drafts = MODE == kModeVerify && split == 0 && dlo < dhi && w == kDraftWave;
+    if (verify_drafts && w >= nt) load_draft(dlo, dhi, kr, vr, ok);
     for (int tau = w; tau < nt; tau += 4) {
       const int nxt = tau + 4;
       const bool is_prefix = tau < npt;
@@ -699,9 +707,13 @@ attn_kernel(const AttnArgs a) {
       // which then have a whole iteration to land.
       stage(kr, vr, is_prefix, ok, st);
       if constexpr (kPrefixOnly) {
-        const int ld = nxt < nt ? nxt : tau;
-        load_rows(pg, p0 + ld * 32, p1, kr, vr);
-        pages_of(nxt + 4 < nt ? nxt + 4 : ld, pg);
+        if (verify_drafts && nxt >= nt) {
+          load_draft(dlo, dhi, kr, vr, ok);
+        } else {
+          const int ld = nxt < nt ? nxt : tau;
+          load_rows(pg, p0 + ld * 32, p1, kr, vr);
+          pages_of(nxt + 4 < nt ? nxt + 4 : ld, pg);
+        }
       } else {
         if (nxt < nt) issue(nxt);
         if (nxt + 4 < nt) pages_of(nxt + 4, pg);
@@ -729,15 +741,34 @@ attn_kernel(const AttnArgs a) {
       }
     }
 
-    mfma_drain();
-    if constexpr (MODE == kModeVerify) {
-      if (a.n_splits == 1 && dlo < dhi) {
-        int64_t off[2];
-        draft_offsets(dlo, dhi, off);
-        load_draft_at(off, dkr, dvr, dok);  // lands while the waves merge
-        draft_loaded = true;
+    if (verify_drafts) {
+      // Pass B of the chunk's rows into this wave's state: its visible draft
+      // tiles (usually one), under the in-branch ancestor mask.
+      load_row_masks();
+      for (int base = dlo; base < dhi; base += 32) {
+        if (base != dlo) load_draft(base, dhi, kr, vr, ok);
+        stage(kr, vr, false, ok, st);
+        f32x4 s[RB][2];
+        scores(st, s);
+        mask_draft(base, dhi, s);
+        float alpha[RB];
+        bf16x8 pf[RB];
+        if (__any(softmax(s, m, l, alpha, pf))) {
+#pragma unroll
+          for (int rb = 0; rb < RB; ++rb)
+#pragma unroll
+            for (int db = 0; db < DB; ++db) o[rb][db] *= alpha[rb];
+        }
+#pragma unroll
+        for (int db = 0; db < DB; ++db) {
+          const bf16x8 vf = vt_frag(st, db);
+#pragma unroll
+          for (int rb = 0; rb < RB; ++rb) o[rb][db] = mfma16(vf, pf[rb], o[rb][db]);
+        }
       }
     }
+
+    mfma_drain();
 
     // ---- merge the four waves' states (LSE identity) ----------------------
 #pragma unroll
@@ -803,16 +834,9 @@ attn_kernel(const AttnArgs a) {
   }
 
   if constexpr (kFinish) {
-    if constexpr (MODE == kModeVerifyFinish) {
-      if (dlo < dhi) {
-        int64_t off[2];
-        draft_offsets(dlo, dhi, off);
-        load_draft_at(off, dkr, dvr, dok);  // lands while the partials merge
-        draft_loaded = true;
-      }
-    }
     // Merge the prefix split partials of these rows (fixed split order).
-    const int nsp = (L + a.split_len - 1) / a.split_len;
+    int nsp = (L + a.split_len - 1) / a.split_len;
+    if constexpr (MODE == kModeVerifyFinish) nsp = nsp > 0 ? nsp : 1;  // split 0 holds the drafts
     const int64_t plane = (int64_t)a.total_rows * a.num_qo_heads;
 #pragma unroll
     for (int rb = 0; rb < RB; ++rb) {
@@ -845,65 +869,6 @@ attn_kernel(const AttnArgs a) {
   // Split prefix passes stop at a partial state; everything else is final.
   bool partial = false;
   if constexpr (MODE == kModePrefix || MODE == kModeVerify) partial = a.n_splits > 1;
-
-  if constexpr (kEpilogueDraft) {
-    if (!partial) {
-      // Pass B for the rows of this chunk: every wave walks the request's
-      // visible draft tiles (a handful of keys), keeping only its own channel
-      // blocks of o_B, then merges with pass A by the LSE identity.
-      __syncthreads();  // the exchange buffer is reused as staging below
-      load_row_masks();
-      uint16_t* st = reinterpret_cast<uint16_t*>(smem) + w * STAGE;
-      float mB[RB], lB[RB];
-      f32x4 oB[RB][DBW];
-#pragma unroll
-      for (int rb = 0; rb < RB; ++rb) {
-        mB[rb] = kNegInf;
-        lB[rb] = 0.f;
-#pragma unroll
-        for (int dbl = 0; dbl < DBW; ++dbl) oB[rb][dbl] = f32x4{0.f, 0.f, 0.f, 0.f};
-      }
-      for (int base = dlo; base < dhi; base += 32) {
-        if (base == dlo && draft_loaded) {
-          stage(dkr, dvr, false, dok, st);
-        } else {
-          u32x4 kr2[NI], vr2[NI];
-          int ok2;
-          load_draft(base, dhi, kr2, vr2, ok2);
-          stage(kr2, vr2, false, ok2, st);
-        }
-        f32x4 s[RB][2];
-        scores(st, s);
-        mask_draft(base, dhi, s);
-        float alpha[RB];
-        bf16x8 pf[RB];
-        softmax(s, mB, lB, alpha, pf);
-#pragma unroll
-        for (int rb = 0; rb < RB; ++rb)
-#pragma unroll
-          for (int dbl = 0; dbl < DBW; ++dbl) oB[rb][dbl] *= alpha[rb];
-#pragma unroll
-        for (int dbl = 0; dbl < DBW; ++dbl) {
-          const bf16x8 vf = vt_frag(st, w * DBW + dbl);
-#pragma unroll
-          for (int rb = 0; rb < RB; ++rb) oB[rb][dbl] = mfma16(vf, pf[rb], oB[rb][dbl]);
-        }
-      }
-      mfma_drain();
-#pragma unroll
-      for (int rb = 0; rb < RB; ++rb) {
-        lB[rb] = rowgroup_sum(lB[rb]);
-        const float lseB = lB[rb] > 0.f ? mB[rb] + fast_log2(lB[rb]) : kNegInf;
-        const float invB = lB[rb] > 0.f ? 1.f / lB[rb] : 0.f;
-        float wa, wb, lt;
-        merge_weights(lse2[rb], lseB, wa, wb, lt);
-#pragma unroll
-        for (int dbl = 0; dbl < DBW; ++dbl)
-          acc[rb][dbl] = wsum(wa, acc[rb][dbl], wb, oB[rb][dbl] * invB);
-        lse2[rb] = lt;
-      }
-    }
-  }
 
   // ---- output ----------------------------------------------------------------
   const int64_t plane = (int64_t)a.total_rows * a.num_qo_heads;
