@@ -208,8 +208,25 @@ attn_kernel(const AttnArgs a) {
     jb = crb[seg];
     je = crb[seg + 1];
   }
+  // The request's length and the block-table entries of this wave's first
+  // prefix tile are requested together with the branch range, so that the
+  // first K/V loads wait for one round trip of small loads, not a chain.
+  const int L_in = as_const(a.cache_seqlens)[req];
+  cint32* pt_row = as_const(a.page_table + (int64_t)req * a.page_table_stride);
+  int pt_first[2] = {-1, -1};
+  if constexpr (MODE == kModePrefix || MODE == kModeVerify) {
+    const int stride = a.page_table_stride;
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+      const int idx = (split * a.split_len + w * 32 + kb * 16) >> a.kv.log2_page;
+      if (stride > 0) pt_first[kb] = pt_row[idx < stride ? idx : stride - 1];  // clamped: used only if in range
+    }
+  }
   const int tok0 = cqo[jb];
   const int tok1 = cqo[je];
+  // Keeps the length load in the same round trip as the branch-range loads
+  // (otherwise it is sunk past the checks below).
+  asm volatile("" ::"s"(L_in));
   if (tok0 < 0 || tok1 < tok0 || tok1 > a.total_rows) {
     if (threadIdx.x == 0) atomicOr(&g_device_error, kErrRow);
     return;
@@ -222,7 +239,7 @@ attn_kernel(const AttnArgs a) {
   if (row0 >= nrows) return;
   const int row_end = min(nrows, row0 + ROWS);
 
-  int L = as_const(a.cache_seqlens)[req];
+  int L = L_in;
   {
     const int cap = a.page_table_stride << a.kv.log2_page;
     if (L > cap) {
@@ -241,7 +258,6 @@ attn_kernel(const AttnArgs a) {
   }
 
   const KvView kv = a.kv;
-  cint32* pt_row = as_const(a.page_table + (int64_t)req * a.page_table_stride);
   const float c2 = a.scale_log2;
   const int pmask = (1 << kv.log2_page) - 1;
   const int64_t head_off = (int64_t)g * kv.head_stride;
@@ -313,16 +329,18 @@ attn_kernel(const AttnArgs a) {
       vr[n] = buf_load16(rv[kb], lane_off[n % NV]);
     }
   };
+  auto page_id = [&](int id) {  // -1 (and the error flag) for ids outside the pool
+    if (id >= kv.num_pages) {
+      if (lane == 0) atomicOr(&g_device_error, kErrPage);
+    }
+    if ((uint32_t)id >= (uint32_t)kv.num_pages) id = -1;
+    return __builtin_amdgcn_readfirstlane(id);  // uniform by construction
+  };
   auto prefix_pages = [&](int base, int end, int (&pg)[2]) {
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
       const int first = base + kb * 16;
-      int id = first < end ? pt_row[first >> kv.log2_page] : -1;
-      if (id >= kv.num_pages) {
-        if (lane == 0) atomicOr(&g_device_error, kErrPage);
-      }
-      if ((uint32_t)id >= (uint32_t)kv.num_pages) id = -1;
-      pg[kb] = __builtin_amdgcn_readfirstlane(id);  // uniform by construction
+      pg[kb] = page_id(first < end ? pt_row[first >> kv.log2_page] : -1);
     }
   };
 
@@ -339,14 +357,6 @@ attn_kernel(const AttnArgs a) {
     p1 = L;
   }
   const int npt = (p1 - p0 + 31) >> 5;
-  u32x4 kr[NI], vr[NI];
-  int pg[2] = {-1, -1};
-  if constexpr (kMainLoop) {
-    if (w < npt) {
-      prefix_pages(p0 + w * 32, p1, pg);
-      load_rows(pg, p0 + w * 32, p1, kr, vr);
-    }
-  }
 
   // ---- Q rows of the chunk (into registers now, into LDS below) ---------
   constexpr int kQChunks = D / 8;
@@ -368,14 +378,51 @@ attn_kernel(const AttnArgs a) {
     }
   }
 
+  // ---- tree tables: their loads go out ahead of the first tile ------------
+  // In the fused verify launch only the draft wave (of split 0) reads the
+  // tables, so it alone builds them, ordered at wave level; the draft and
+  // naive launches build them with the whole workgroup.
+  constexpr bool kWaveTables = MODE == kModeVerify;
+  constexpr int TNT = kWaveTables ? 64 : 256;       // threads building the tables
+  constexpr int TLD = (NBCAP + 1 + TNT - 1) / TNT;  // window entries per thread
+  const int nb = je - jb;
+  const bool lds_bnd = nb <= NBCAP;
+  const int tid = kWaveTables ? lane : (int)threadIdx.x;
+  bool builder = kDraftKeys;
+  if constexpr (kWaveTables) builder = w == kDraftWave && split == 0;
+  int tb_reg[TLD], td_reg[TLD];
+  if constexpr (kDraftKeys) {
+    if (builder && lds_bnd) {
+#pragma unroll
+      for (int i = 0; i < TLD; ++i) {
+        const int t = tid + i * TNT;
+        tb_reg[i] = t <= nb ? qo[jb + t] : 0;
+        td_reg[i] = t < nb && a.draft_start ? a.draft_start[jb + t] : 0;
+      }
+    }
+  }
+
+  // The first prefix tile goes out after Q, which the first scores need.
+  u32x4 kr[NI], vr[NI];
+  int pg[2] = {-1, -1};
+  if constexpr (kMainLoop) {
+    if (w < npt) {
+      if constexpr (MODE == kModePrefix || MODE == kModeVerify) {
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb) pg[kb] = page_id(p0 + w * 32 + kb * 16 < p1 ? pt_first[kb] : -1);
+      } else {
+        prefix_pages(p0 + w * 32, p1, pg);
+      }
+      load_rows(pg, p0 + w * 32, p1, kr, vr);
+    }
+  }
+
   // ---- tree tables ---------------------------------------------------------
   // t_bnd / t_dst: branch_qo_indptr[jb .. je] and draft_start[jb .. je) of the
   // segment's branches; t_rbs: branch start of each token of the chunk;
   // t_doff: element offset (head excluded) of draft key dlo + t, -1 when its
   // slot lies past its draft block-table row or its page outside the pool.
   int dlo = 0;
-  const int nb = je - jb;
-  const bool lds_bnd = nb <= NBCAP;
   auto branch_at = [&](int x) -> int {  // local branch index of segment token x
     if (lds_bnd) {
       int lo = 0, hi = nb - 1;
@@ -392,28 +439,38 @@ attn_kernel(const AttnArgs a) {
     return lds_bnd ? t_dst[jl] : (a.draft_start ? a.draft_start[jb + jl] : 0);
   };
   if constexpr (kDraftKeys) {
-    if (lds_bnd) {
-      for (int t = threadIdx.x; t <= nb; t += 256) t_bnd[t] = qo[jb + t];
-      for (int t = threadIdx.x; t < nb; t += 256) t_dst[t] = a.draft_start ? a.draft_start[jb + t] : 0;
-    }
-    __syncthreads();
-    dlo = __builtin_amdgcn_readfirstlane(branch_start(branch_at(tok_first)));
-    for (int t = threadIdx.x; t <= tok_last - tok_first; t += 256)
-      t_rbs[t] = branch_start(branch_at(tok_first + t));
-    const int nk = min(dhi - dlo, KEYCAP);
-    const int dstride = a.draft_page_table_stride;
-    for (int t = threadIdx.x; t < nk; t += 256) {
-      const int x = dlo + t;
-      const int jl = branch_at(x);
-      const int slot = branch_dstart(jl) + (x - branch_start(jl));
-      int64_t off = -1;
-      if (slot >= 0 && (slot >> kv.log2_page) < dstride) {
-        const int page = a.draft_page_table[(int64_t)(jb + jl) * dstride + (slot >> kv.log2_page)];
-        if ((uint32_t)page < (uint32_t)kv.num_pages)
-          off = (int64_t)page * kv.page_stride + (int64_t)(slot & pmask) * kv.token_stride;
+    if (builder && lds_bnd) {
+#pragma unroll
+      for (int i = 0; i < TLD; ++i) {
+        const int t = tid + i * TNT;
+        if (t <= nb) t_bnd[t] = tb_reg[i];
+        if (t < nb) t_dst[t] = td_reg[i];
       }
-      t_doff[t] = off;
     }
+    if constexpr (kWaveTables) {
+      wave_lds_sync();
+    } else {
+      __syncthreads();
+    }
+    if (builder) {
+      dlo = __builtin_amdgcn_readfirstlane(branch_start(branch_at(tok_first)));
+      for (int t = tid; t <= tok_last - tok_first; t += TNT) t_rbs[t] = branch_start(branch_at(tok_first + t));
+      const int nk = min(dhi - dlo, KEYCAP);
+      const int dstride = a.draft_page_table_stride;
+      for (int t = tid; t < nk; t += TNT) {
+        const int x = dlo + t;
+        const int jl = branch_at(x);
+        const int slot = branch_dstart(jl) + (x - branch_start(jl));
+        int64_t off = -1;
+        if (slot >= 0 && (slot >> kv.log2_page) < dstride) {
+          const int page = a.draft_page_table[(int64_t)(jb + jl) * dstride + (slot >> kv.log2_page)];
+          if ((uint32_t)page < (uint32_t)kv.num_pages)
+            off = (int64_t)page * kv.page_stride + (int64_t)(slot & pmask) * kv.token_stride;
+        }
+        t_doff[t] = off;
+      }
+    }
+    if constexpr (kWaveTables) wave_lds_sync();  // t_rbs and t_doff before the draft wave reads them
   }
   if constexpr (kQInLds) {
 #pragma unroll
@@ -423,7 +480,7 @@ attn_kernel(const AttnArgs a) {
         *reinterpret_cast<u32x4*>(qs + (idx / kQChunks) * QSTR + (idx % kQChunks) * 8) = qtmp[it];
     }
   }
-  if constexpr (kQInLds || kDraftKeys) __syncthreads();
+  if constexpr (kQInLds || (kDraftKeys && !kWaveTables)) __syncthreads();
 
   // Q B-fragments: lane holds row rb*16 + l16, channels ks*32 + g4*8 .. +8.
   bf16x8 qf[kQInLds ? 1 : RB][KS];

@@ -24,6 +24,15 @@ __device__ __forceinline__ cint32* as_const(const int32_t* p) { return (cint32*)
 // cleared by the host through hipMemcpyFromSymbol / hipMemcpyToSymbol.
 static __device__ int g_device_error;
 
+// Orders one wave's LDS writes before its later LDS reads from other lanes.
+// A wave's LDS instructions execute in order, so this only keeps the compiler
+// from moving them across the point.
+__device__ __forceinline__ void wave_lds_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 constexpr float kNegInf = -__builtin_inff();

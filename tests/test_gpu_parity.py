@@ -63,6 +63,10 @@ def small_cases():
         "long_split": lambda: W.build_workload("long_split", [5000, 2500], [[4, 4], [2]], 8, 8, 128, 32,
                                                seed=24),
         "topk1": lambda: W.build_workload("topk1", [90, 17], [[6], [9]], 4, 2, 128, 16, seed=25),
+        # More branches per request than one wave has lanes (70), and more than
+        # the per-workgroup branch window holds (130): the tree tables' slow paths.
+        "wide_tree": lambda: W.build_workload("wide_tree", [300, 50], [[1] * 70, [2] * 130], 4, 2, 64, 16,
+                                              seed=26),
     }
 
 
