@@ -33,6 +33,7 @@ EXPORTED = (
     "cascade_workspace_size", "cascade_prefix_attn", "cascade_draft_attn", "merge_state",
     "cascade_verify_attn", "naive_expand", "cascade_status_string", "cascade_last_error",
     "cascade_debug_gather", "cascade_debug_mask", "cascade_device_error",
+    "cascade_kernel_timing", "cascade_last_verify_ms",
 )
 
 
@@ -103,6 +104,10 @@ def lib() -> ctypes.CDLL:
         L.cascade_debug_mask.restype = st
         L.cascade_device_error.argtypes = [P(ctypes.c_int32), ctypes.c_int32]
         L.cascade_device_error.restype = st
+        L.cascade_kernel_timing.argtypes = [ctypes.c_int32]
+        L.cascade_kernel_timing.restype = st
+        L.cascade_last_verify_ms.argtypes = [P(ctypes.c_float)]
+        L.cascade_last_verify_ms.restype = st
         _LIB = L
     return _LIB
 
@@ -306,3 +311,13 @@ def cascade_device_error(clear: bool = True) -> int:
     v = ctypes.c_int32(0)
     _check(lib().cascade_device_error(ctypes.byref(v), 1 if clear else 0))
     return int(v.value)
+
+
+def cascade_kernel_timing(enable: bool) -> None:
+    _check(lib().cascade_kernel_timing(1 if enable else 0))
+
+
+def cascade_last_verify_ms() -> float:
+    v = ctypes.c_float(0.0)
+    _check(lib().cascade_last_verify_ms(ctypes.byref(v)))
+    return float(v.value)

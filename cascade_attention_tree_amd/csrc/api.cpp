@@ -215,11 +215,21 @@ WsLayout ws_layout(const cascade_query* q, const cascade_paged_kv* kv, const Pla
   return w;
 }
 
-hipError_t launch(int mode, int head_dim, int rb, const casc::AttnArgs& a, int64_t grid, hipStream_t s) {
+hipError_t launch(int mode, int head_dim, int rb, const casc::AttnArgs& a, int64_t grid, hipStream_t s,
+                  hipEvent_t e0 = nullptr, hipEvent_t e1 = nullptr) {
   if (grid <= 0) return hipSuccess;
-  if (head_dim == 64) return casc::launch_attn_d64(mode, rb, a, (int)grid, s);
-  return casc::launch_attn_d128(mode, rb, a, (int)grid, s);
+  if (head_dim == 64) return casc::launch_attn_d64(mode, rb, a, (int)grid, s, e0, e1);
+  return casc::launch_attn_d128(mode, rb, a, (int)grid, s, e0, e1);
 }
+
+// Kernel timing of cascade_verify_attn (per thread; see the header).
+struct KernelTiming {
+  bool enabled = false;
+  bool recorded = false;
+  hipEvent_t start = nullptr;
+  hipEvent_t stop = nullptr;
+};
+thread_local KernelTiming g_timing;
 
 cascade_status check_grid(int64_t grid) {
   if (grid > INT32_MAX) return fail(CASCADE_ERR_SHAPE, "launch too large (%lld work items)", (long long)grid);
@@ -350,19 +360,22 @@ cascade_status cascade_verify_attn(const cascade_query* q, const cascade_paged_k
   a.o_bf16 = o_dtype == CASCADE_BF16;
   a.lse = lse;
   hipError_t e;
+  hipEvent_t e0 = g_timing.enabled ? g_timing.start : nullptr;
+  hipEvent_t e1 = g_timing.enabled ? g_timing.stop : nullptr;
   if (p.n_splits > 1) {
     a.ws_o = static_cast<float*>(ws);
     a.ws_lse = reinterpret_cast<float*>(static_cast<char*>(ws) + wl.lse_off);
     a.grid_splits = p.n_splits;
-    e = launch(casc::kModeVerify, kv->head_dim, p.rb, a, p.items * p.n_splits, s);
+    e = launch(casc::kModeVerify, kv->head_dim, p.rb, a, p.items * p.n_splits, s, e0, nullptr);
     if (e != hipSuccess) return hip_fail(e, "verify prefix launch");
     a.grid_splits = 1;
-    e = launch(casc::kModeVerifyFinish, kv->head_dim, p.rb, a, p.items, s);
+    e = launch(casc::kModeVerifyFinish, kv->head_dim, p.rb, a, p.items, s, nullptr, e1);
     if (e != hipSuccess) return hip_fail(e, "verify merge launch");
   } else {
-    e = launch(casc::kModeVerify, kv->head_dim, p.rb, a, p.items, s);
+    e = launch(casc::kModeVerify, kv->head_dim, p.rb, a, p.items, s, e0, e1);
     if (e != hipSuccess) return hip_fail(e, "verify launch");
   }
+  if (g_timing.enabled) g_timing.recorded = true;
   return CASCADE_OK;
 }
 
@@ -478,6 +491,26 @@ cascade_status cascade_device_error(int32_t* flag_out, int32_t clear) {
   if ((e = casc::read_error_d128(&v128, clear)) != hipSuccess) return hip_fail(e, "read error word");
   if ((e = casc::read_error_small(&vs, clear)) != hipSuccess) return hip_fail(e, "read error word");
   *flag_out = v64 | v128 | vs;
+  return CASCADE_OK;
+}
+
+cascade_status cascade_kernel_timing(int32_t enable) {
+  if (enable && !g_timing.start) {
+    hipError_t e = hipEventCreate(&g_timing.start);
+    if (e == hipSuccess) e = hipEventCreate(&g_timing.stop);
+    if (e != hipSuccess) return hip_fail(e, "timing event creation");
+  }
+  g_timing.enabled = enable != 0;
+  g_timing.recorded = false;
+  return CASCADE_OK;
+}
+
+cascade_status cascade_last_verify_ms(float* ms_out) {
+  if (!ms_out) return fail(CASCADE_ERR_NULL, "ms_out is NULL");
+  if (!g_timing.recorded) return fail(CASCADE_ERR_SHAPE, "no timed cascade_verify_attn call");
+  hipError_t e = hipEventSynchronize(g_timing.stop);
+  if (e == hipSuccess) e = hipEventElapsedTime(ms_out, g_timing.start, g_timing.stop);
+  if (e != hipSuccess) return hip_fail(e, "timing event query");
   return CASCADE_OK;
 }
 

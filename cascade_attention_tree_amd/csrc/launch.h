@@ -8,8 +8,12 @@
 namespace casc {
 
 // Attention kernels: head_dim 64 or 128, rb = 16-row blocks per chunk (1..5).
-hipError_t launch_attn_d64(int mode, int rb, const AttnArgs& a, int grid, hipStream_t s);
-hipError_t launch_attn_d128(int mode, int rb, const AttnArgs& a, int grid, hipStream_t s);
+// ev_start / ev_stop (may be null): HIP events the command processor records
+// immediately before the kernel starts / after it ends.
+hipError_t launch_attn_d64(int mode, int rb, const AttnArgs& a, int grid, hipStream_t s,
+                           hipEvent_t ev_start, hipEvent_t ev_stop);
+hipError_t launch_attn_d128(int mode, int rb, const AttnArgs& a, int grid, hipStream_t s,
+                            hipEvent_t ev_start, hipEvent_t ev_stop);
 
 hipError_t launch_merge(const MergeArgs& a, hipStream_t s);
 hipError_t launch_debug_gather(const DebugArgs& a, hipStream_t s);

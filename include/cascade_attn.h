@@ -199,6 +199,17 @@ CASCADE_API cascade_status cascade_debug_mask(const cascade_tree *tree, int32_t 
  * kernel met a page id or row outside its bounds.  Synchronises the device. */
 CASCADE_API cascade_status cascade_device_error(int32_t *flag_out, int32_t clear);
 
+/* Kernel timing, for measurement tools.  With enable != 0, every later
+ * cascade_verify_attn call on this thread launches its kernels with HIP events
+ * recorded by the command processor immediately around them (the first
+ * kernel's start, the last kernel's end); enable = 0 turns it off.  The events
+ * are created on the current device by the first enabling call.
+ * cascade_last_verify_ms: the elapsed time between those two events of the
+ * latest timed call, in ms; synchronises on the stop event.  Returns
+ * CASCADE_ERR_SHAPE when no call has been timed since timing was enabled. */
+CASCADE_API cascade_status cascade_kernel_timing(int32_t enable);
+CASCADE_API cascade_status cascade_last_verify_ms(float *ms_out);
+
 #ifdef __cplusplus
 }
 #endif

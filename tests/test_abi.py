@@ -128,3 +128,12 @@ def test_debug_hook_validation():
     assert lib.cascade_debug_gather(ctypes.byref(kv), ctypes.byref(t), 0, 0, 9, FAKE, FAKE,
                                     None) == B.CASCADE_ERR_SHAPE
     assert lib.cascade_debug_mask(ctypes.byref(t), -1, FAKE, 4, None) == B.CASCADE_ERR_SHAPE
+
+
+def test_kernel_timing_without_a_timed_call():
+    lib = B.lib()
+    assert lib.cascade_last_verify_ms(None) == B.CASCADE_ERR_NULL
+    assert lib.cascade_kernel_timing(0) == 0
+    v = ctypes.c_float(0.0)
+    assert lib.cascade_last_verify_ms(ctypes.byref(v)) == B.CASCADE_ERR_SHAPE
+    assert b"timed" in lib.cascade_last_error()

@@ -311,6 +311,26 @@ def test_bf16_output(B):
     cmp(n16, l16, ro, rl)
 
 
+@pytest.mark.parametrize("case", ["tiny", "long_split"])
+def test_kernel_timing_events(B, case):
+    """Timed launches (events around the kernels, split and unsplit plans)
+    give the same bits as plain launches and a positive kernel time."""
+    wl = small_cases()[case]()
+    x = B.to_device(wl, layout="HND")
+    ws = B.workspace_for(x)
+    note(f"kernel timing {case}")
+    o0, l0 = B.cascade_verify_attn(x, workspace=ws)
+    B.cascade_kernel_timing(True)
+    try:
+        o1, l1 = B.cascade_verify_attn(x, workspace=ws)
+        ms = B.cascade_last_verify_ms()
+    finally:
+        B.cascade_kernel_timing(False)
+    torch.cuda.synchronize()
+    assert 0.0 < ms < 1000.0
+    assert torch.equal(o0, o1) and torch.equal(l0, l1)
+
+
 def test_no_device_error_raised(B):
     note("device error word")
     assert B.cascade_device_error(clear=True) == 0
