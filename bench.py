@@ -22,6 +22,10 @@ entry uses the kernel's own duration, from a second pass of K cold steps in
 which the library records HIP events on the same stream immediately around
 its kernel (cascade_kernel_timing), i.e. without the dispatch latency that an
 event pair around the call also measures.
+
+The line also carries the prefix-hit suffix prefill (B=4, N=8192, hit ratio
+h = 0, 0.5, 0.9; three calls, cold protocol) beside the closed-form work
+ratio 1 - H(H+1)/(N(N+1)), unless --no-prefix-hit.
 """
 
 from __future__ import annotations
@@ -142,6 +146,43 @@ def cpu_baseline(wl, kv_bytes, budget_s):
             "query_tok_per_s": wl.total_rows / dt}
 
 
+def prefix_hit_timings(B, W, torch, flush, steps=5, warmup=2):
+    """Prefix-hit suffix prefill (B=4 requests of N=8192 tokens, a hit of
+    H = floor(h N)): pass A over the hit, pass B causal over the suffix, merge
+    (three calls), cold protocol.  Reported beside the closed-form work ratio
+    1 - H(H+1)/(N(N+1)) and against the dense bf16 MFMA peak (2.5 PFLOP/s)."""
+    out = {}
+    base = None
+    for h in (0.0, 0.5, 0.9):
+        wl = W.prefix_hit(h)
+        N, H, M = wl.meta["N"], wl.meta["H"], wl.meta["M"]
+        x = B.to_device(wl, "cuda", layout="HND")
+        ws = B.workspace_for(x)
+        oa = torch.empty(wl.q.shape, dtype=torch.float32, device="cuda")
+        la = torch.empty(wl.q.shape[:2], dtype=torch.float32, device="cuda")
+        ob, lb = torch.empty_like(oa), torch.empty_like(la)
+        o = torch.empty(wl.q.shape, dtype=torch.bfloat16, device="cuda")
+        lse = torch.empty_like(la)
+
+        def step():
+            B.cascade_prefix_attn(x, o_a=oa, lse_a=la, workspace=ws)
+            B.cascade_draft_attn(x, o_b=ob, lse_b=lb)
+            B.merge_state(oa, la, ob, lb, out_dtype=torch.bfloat16, o=o, lse=lse)
+
+        ms, _ = time_steps(step, steps, warmup, flush, torch)
+        t = float(np.median(ms))
+        base = t if base is None else base
+        pairs = wl.batch_size * (M * H + M * (M + 1) // 2)           # visible (query, key) pairs per head
+        flops = 4.0 * wl.head_dim * wl.num_qo_heads * pairs
+        out[f"h{h}"] = {"H": H, "M": M, "median_ms": t, "tflops": flops / (t * 1e-3) / 1e12,
+                        "mfma_frac": flops / (t * 1e-3) / 2.5e15,
+                        "time_ratio_vs_h0": t / base,
+                        "work_ratio_closed_form": 1.0 - H * (H + 1) / (N * (N + 1))}
+        del x, ws, oa, la, ob, lb, o, lse
+        torch.cuda.empty_cache()
+    return out
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -152,6 +193,8 @@ def main():
     ap.add_argument("--only-verify", action="store_true", help="time only the fused verify call")
     ap.add_argument("--layout", choices=("HND", "NHD"), default="HND",
                     help="page layout of the KV pool on the device (same logical content)")
+    ap.add_argument("--no-prefix-hit", action="store_true",
+                    help="skip the prefix-hit (suffix prefill) timings")
     ap.add_argument("--traffic-probe", action="store_true",
                     help="for hardware-counter runs: one plain 256 MiB device copy (known bytes), "
                          "then a few flushed verify steps; prints nothing else")
@@ -270,6 +313,9 @@ def main():
                                       "(hipExtLaunchKernel), mean of K cold steps"},
     }
     line.update(extra)
+    if not args.no_prefix_hit and not args.only_verify:
+        print("bench: timing prefix-hit suffix prefill (h = 0, 0.5, 0.9)", file=sys.stderr, flush=True)
+        line["prefix_hit"] = prefix_hit_timings(B, W, torch, flush)
     if not args.no_cpu_baseline:
         print("bench: timing the CPU oracle", file=sys.stderr, flush=True)
         line["cpu_baseline"] = cpu_baseline(wl, kv_casc, args.cpu_seconds)
