@@ -75,6 +75,13 @@ class Workload:
     branch_qo_indptr: np.ndarray
     draft_page_table: np.ndarray
     draft_start: np.ndarray
+    # General draft trees (None: every branch is a chain).  Per query row, the
+    # parent of its node within its branch (-1: the node hangs off the prefix)
+    # and the node's ancestor set as a bit mask over the branch's nodes (bit u:
+    # node u is the row's node or one of its ancestors).  Nodes are numbered in
+    # breadth-first order, so a parent always precedes its children.
+    draft_parent: Optional[np.ndarray] = None
+    draft_mask: Optional[np.ndarray] = None
     # Logical (unpaged) copies, kept only when asked for: per request the prefix
     # tokens [L_i, Hkv, d], per branch its draft tokens [S_j, Hkv, d].
     prefix_k: Optional[List[np.ndarray]] = None
@@ -244,6 +251,51 @@ def build_workload(name: str,
     return wl
 
 
+def attach_random_trees(wl: Workload, seed: int, max_children: int = 4) -> Workload:
+    """Turn every branch of ``wl`` into a random draft tree over its S_j nodes
+    (S_j <= 64): nodes are created level by level, each node of a level picking
+    its parent uniformly among the previous level's nodes that still have fewer
+    than ``max_children`` children (level 0 hangs off the prefix).  Sets
+    ``draft_parent`` and ``draft_mask`` (uint64 per row)."""
+    rng = np.random.default_rng(seed)
+    R = wl.total_rows
+    parent = np.full(R, -1, np.int32)
+    mask = np.zeros(R, np.uint64)
+    qo = wl.branch_qo_indptr
+    for j in range(wl.num_branches):
+        r0, S = int(qo[j]), int(qo[j + 1] - qo[j])
+        if S > 64:
+            raise ValueError("draft trees are limited to 64 nodes per branch")
+        par = np.full(S, -1, np.int64)
+        prev = [-1]                      # level 0: children of the prefix
+        nxt: List[int] = []
+        kids = {-1: 0}
+        u = 0
+        while u < S:
+            open_ = [p for p in prev if kids.get(p, 0) < (max_children if p >= 0 else max_children)]
+            if not open_:
+                prev, nxt = nxt, []
+                continue
+            p = int(open_[rng.integers(len(open_))])
+            par[u] = p
+            kids[p] = kids.get(p, 0) + 1
+            nxt.append(u)
+            u += 1
+            if rng.random() < 0.35 and nxt:
+                prev, nxt = prev + nxt, []
+        m = np.zeros(S, np.uint64)
+        for u in range(S):
+            m[u] = np.uint64(1) << np.uint64(u)
+            if par[u] >= 0:
+                m[u] |= m[par[u]]
+        parent[r0:r0 + S] = par
+        mask[r0:r0 + S] = m
+    wl.draft_parent = parent
+    wl.draft_mask = mask
+    wl.meta["trees"] = {"seed": seed, "max_children": max_children}
+    return wl
+
+
 # ----------------------------------------------------------------------------
 # The five workloads the path is measured and checked on.
 # ----------------------------------------------------------------------------
@@ -293,6 +345,14 @@ def prefix_hit(h: float, values: str = "bf16", keep_logical: bool = False, seed:
                         keep_logical=keep_logical)
     wl.meta.update({"N": n_tokens, "H": H, "M": M, "h": h})
     return wl
+
+
+def tree_headline(values: str = "bf16", keep_logical: bool = False, seed: int = 6) -> Workload:
+    """The headline shapes with one 20-node random draft tree per request instead of
+    4 chains of 5: B=32, Hq=32, Hkv=8, d=128, L=2000, pages of 16."""
+    wl = build_workload("tree_headline", [2000] * 32, [[20]] * 32, 32, 8, 128, 16, seed,
+                        values, keep_logical=keep_logical)
+    return attach_random_trees(wl, seed + 100)
 
 
 CONFIGS = {

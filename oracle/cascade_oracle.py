@@ -37,7 +37,10 @@ Readings taken where the pages leave a step open:
 * An empty key set has o = 0 and LSE = -inf; a merge with one empty side
   returns the other side; a merge of two empty sides is (0, -inf).
 * A draft token sees itself (ancestor set includes the node).
-* Branches share nothing but the prefix (chains, no node de-duplication).
+* Branches share nothing but the prefix.  A branch is a chain unless the
+  workload carries a draft tree; then each row's visible drafts are the nodes
+  whose bits are set in its ancestor mask (tree attention mask, tutorial page
+  section 8.2), and a request's tree is one branch holding all of its nodes.
 * Draft token u of branch j lives at logical slot draft_start[j] + u of the
   block-table row draft_page_table[j].
 
@@ -159,6 +162,19 @@ def _draft_kv(wl, j):
 # The two passes and their merge (cascade page, "mathematical structure")
 # ---------------------------------------------------------------------------
 
+def draft_visible(wl, j, s):
+    """Draft positions of branch j that its position s attends: its ancestors
+    and itself (tutorial page, section 8.2).  A chain is the tree in which node
+    u's parent is u - 1, so it sees positions 0..s; a general tree gives each
+    row its ancestor set as a bit mask over the branch's nodes."""
+    if getattr(wl, "draft_mask", None) is None:
+        return np.arange(s + 1)
+    r0 = int(wl.branch_qo_indptr[j])
+    S = int(wl.branch_qo_indptr[j + 1]) - r0
+    m = int(wl.draft_mask[r0 + s])
+    return np.array([u for u in range(S) if (m >> u) & 1], np.int64)
+
+
 def prefix_pass(wl, requests=None):
     """Pass A.  Request i's prefix (L_i tokens via its page-table row) is read
     once and attended by every query row of all of its branches.
@@ -183,7 +199,7 @@ def prefix_pass(wl, requests=None):
 def draft_pass(wl, branches=None):
     """Pass B.  Branch j (one of the B*topk virtual requests) reads only its own
     S_j draft tokens via its draft page-table row; its token at position s
-    attends draft positions u <= s (its ancestors and itself).
+    attends its ancestors and itself (draft_visible: u <= s for a chain).
 
     Returns (o_B [rows, Hq, d], lse_B [rows, Hq])."""
     R, Hq, d = wl.q.shape
@@ -195,10 +211,11 @@ def draft_pass(wl, branches=None):
         r0, r1 = int(qo[j]), int(qo[j + 1])
         k, v = _draft_kv(wl, j)
         for s in range(r1 - r0):
+            vis = draft_visible(wl, j, s)
             for h in range(Hq):
                 g = _kv_head(h, Hq, wl.num_kv_heads)
-                oo, ll = attention_state(wl.q[r0 + s, h][None], k[:s + 1, g],
-                                         v[:s + 1, g], wl.sm_scale)
+                oo, ll = attention_state(wl.q[r0 + s, h][None], k[vis, g],
+                                         v[vis, g], wl.sm_scale)
                 o[r0 + s, h], lse[r0 + s, h] = oo[0], ll[0]
     return o, lse
 
@@ -218,8 +235,9 @@ def naive_expand(wl, rows=None):
     """One softmax per (row, head) over everything the row may see.
 
     Row r is position s of branch j of request i.  Its visible keys are the
-    L_i prefix tokens of request i and draft tokens 0..s of branch j, read
-    through the two page tables (each virtual request re-reads the prefix).
+    L_i prefix tokens of request i and the draft tokens of branch j that s
+    attends (0..s for a chain), read through the two page tables (each virtual
+    request re-reads the prefix).
 
     rows: optional iterable of global row ids; others stay (0, -inf).
     Returns (o [rows, Hq, d], lse [rows, Hq])."""
@@ -239,8 +257,9 @@ def naive_expand(wl, rows=None):
         kd, vd = _draft_kv(wl, j)
         for r in rs:
             s = r - int(qo[j])
-            k = np.concatenate([kp, kd[:s + 1]], axis=0)
-            v = np.concatenate([vp, vd[:s + 1]], axis=0)
+            vis = draft_visible(wl, j, s)
+            k = np.concatenate([kp, kd[vis]], axis=0)
+            v = np.concatenate([vp, vd[vis]], axis=0)
             for h in range(Hq):
                 g = _kv_head(h, Hq, wl.num_kv_heads)
                 oo, ll = attention_state(wl.q[r, h][None], k[:, g], v[:, g], wl.sm_scale)
@@ -282,9 +301,10 @@ def cascade_rows(wl, rows):
             if j not in drafts:
                 drafts[j] = _draft_kv(wl, j)
             kd, vd = drafts[j]
+            vis = draft_visible(wl, j, s)
             for g in range(Hkv):
                 hs = [h for h in range(Hq) if _kv_head(h, Hq, Hkv) == g]
-                oo, ll = attention_state(wl.q[r, hs], kd[:s + 1, g], vd[:s + 1, g], wl.sm_scale)
+                oo, ll = attention_state(wl.q[r, hs], kd[vis, g], vd[vis, g], wl.sm_scale)
                 o_b[x, hs], lse_b[x, hs] = oo, ll
     o, lse = merge_state(o_a, lse_a, o_b, lse_b)
     return rows, o, lse
@@ -303,7 +323,7 @@ def visibility_mask(wl, j):
     m = np.zeros((S, L + S), bool)
     for s in range(S):
         m[s, :L] = True
-        m[s, L:L + s + 1] = True
+        m[s, L + draft_visible(wl, j, s)] = True
     return m
 
 

@@ -61,6 +61,35 @@ def wl_topk1(seed=12):
                             seed=seed, values="fp32", keep_logical=True)
 
 
+def wl_trees(seed=13):
+    # One random draft tree per request (ragged prefixes incl. an empty one, a
+    # 40-node tree), GQA group 3.
+    wl = W.build_workload("pin_trees", [13, 0, 30], [[9], [5], [40]], 6, 2, 16, page_size=8,
+                          seed=seed, values="fp32", keep_logical=True)
+    return W.attach_random_trees(wl, seed + 1)
+
+
+def wl_chain_masks(seed=14):
+    # Chains written out as trees: node u's parent is u - 1.
+    wl = W.build_workload("pin_chain_masks", [11, 3], [[4, 2], [6]], 4, 2, 16, page_size=8,
+                          seed=seed, values="fp32", keep_logical=True)
+    par = np.concatenate([np.arange(-1, s - 1) for s in np.diff(wl.branch_qo_indptr)]).astype(np.int32)
+    wl.draft_parent = par
+    wl.draft_mask = np.concatenate([(np.uint64(2) << np.arange(s, dtype=np.uint64)) - np.uint64(1)
+                                    for s in np.diff(wl.branch_qo_indptr)]).astype(np.uint64)
+    return wl
+
+
+def ancestors(wl, j, s):
+    """Draft node s of branch j and its ancestors, by walking the parent array
+    (chains: parent u - 1)."""
+    out, u = [], s
+    while u >= 0:
+        out.append(u)
+        u = int(wl.draft_parent[int(wl.branch_qo_indptr[j]) + u]) if wl.draft_parent is not None else u - 1
+    return sorted(out)
+
+
 # ---------------------------------------------------------------------------
 # Independent formulations
 # ---------------------------------------------------------------------------
@@ -69,9 +98,10 @@ def brute_force_tree(wl):
     """Dense attention per request over its BFS-flattened token tree.
 
     Nodes: the prefix chain, then the draft nodes level by level across the
-    branches.  Each node's parent is the previous prefix token or the previous
-    draft token of its branch (the first draft token hangs off the last prefix
-    token).  Mask[x, y] = y is an ancestor of x or x itself.  Attention is
+    branches.  Each node's parent is the previous prefix token or its parent
+    draft node (for a chain the previous draft token of its branch; roots hang
+    off the last prefix token).  Mask[x, y] = y is an ancestor of x or x
+    itself, found by walking parents.  Attention is
     torch's scaled_dot_product_attention (GQA by the library), the LSE is
     torch.logsumexp over the masked scores.  Uses the logical (unpaged) tensors
     only, never a page table."""
@@ -95,8 +125,11 @@ def brute_force_tree(wl):
             if n[0] == "p":
                 return ("p", n[1] - 1) if n[1] > 0 else None
             _, j, u = n
-            if u > 0:
-                return ("d", j, u - 1)
+            pu = u - 1
+            if wl.draft_parent is not None:
+                pu = int(wl.draft_parent[int(qo[j]) + u])
+            if pu >= 0:
+                return ("d", j, pu)
             return ("p", L - 1) if L > 0 else None
 
         n_all = len(nodes)
@@ -225,7 +258,7 @@ def pin_brute_force(O):
     """Oracle naive expansion and cascade == dense tree-mask brute force, also on
     a prefix-hit shape (one branch continuing the prefix inside its pages)."""
     hit = W.prefix_hit(0.5, values="fp32", keep_logical=True, batch=2, n_tokens=45)
-    for wl in (wl_tiny(), wl_gqa_tree(), wl_topk1(), hit):
+    for wl in (wl_tiny(), wl_gqa_tree(), wl_topk1(), hit, wl_trees()):
         ref_o, ref_l = brute_force_tree(wl)
         for o, l in (O.naive_expand(wl), O.cascade(wl)):
             assert np.max(np.abs(o - ref_o)) < 1e-12
@@ -262,9 +295,10 @@ def pin_topk1_is_causal(O):
 
 
 def pin_zero_query(O):
-    """q = 0 makes every visible key weigh the same: LSE = ln(L_i + s + 1) and o is
-    the plain mean of the visible values."""
-    for wl in (wl_tiny(), wl_gqa_tree()):
+    """q = 0 makes every visible key weigh the same: LSE = ln(L_i + n) with n the
+    row's node and its ancestors (s + 1 on a chain), and o is the plain mean of
+    the visible values."""
+    for wl in (wl_tiny(), wl_gqa_tree(), wl_trees()):
         wl.q[:] = 0.0
         qo, rb = wl.branch_qo_indptr, wl.req_branch_indptr
         g_of = np.arange(wl.num_qo_heads) // (wl.num_qo_heads // wl.num_kv_heads)
@@ -275,9 +309,32 @@ def pin_zero_query(O):
                 for j in range(int(rb[i]), int(rb[i + 1])):
                     for s in range(int(qo[j + 1] - qo[j])):
                         r = int(qo[j]) + s
-                        assert np.allclose(l[r], math.log(L + s + 1), rtol=0, atol=1e-13)
-                        vis = np.concatenate([wl.prefix_v[i], wl.draft_v[j][:s + 1]]).astype(np.float64)
+                        anc = ancestors(wl, j, s)
+                        assert np.allclose(l[r], math.log(L + len(anc)), rtol=0, atol=1e-13)
+                        vis = np.concatenate([wl.prefix_v[i], wl.draft_v[j][anc]]).astype(np.float64)
                         assert np.allclose(o[r], vis.mean(axis=0)[g_of], rtol=0, atol=1e-13)
+
+
+def pin_chain_as_tree(O):
+    """Chains given as trees (parent u - 1, mask of bits 0..u) give the same bits
+    as the same workload without a tree; the generator's tree masks are exactly
+    the ancestor sets of its parent arrays."""
+    wl = wl_chain_masks()
+    o1, l1 = O.cascade(wl)
+    n1, m1 = O.naive_expand(wl)
+    wl.draft_parent, wl.draft_mask = None, None
+    o0, l0 = O.cascade(wl)
+    n0, m0 = O.naive_expand(wl)
+    assert np.array_equal(o1, o0) and np.array_equal(l1, l0)
+    assert np.array_equal(n1, n0) and np.array_equal(m1, m0)
+    wl = wl_trees()
+    for j in range(wl.num_branches):
+        S = int(wl.branch_qo_indptr[j + 1] - wl.branch_qo_indptr[j])
+        for s in range(S):
+            assert list(O.draft_visible(wl, j, s)) == ancestors(wl, j, s)
+            vm = O.visibility_mask(wl, j)
+            L = vm.shape[1] - S
+            assert vm[s, L:].nonzero()[0].tolist() == ancestors(wl, j, s)
 
 
 def pin_read_counts(O):
@@ -359,7 +416,7 @@ def pin_block_table_sharing(O):
 
 ALL_PINS = [pin_gather, pin_single_key, pin_attention_vs_library, pin_merge_identity,
             pin_merge_closed_forms, pin_brute_force, pin_topk1_is_causal, pin_zero_query,
-            pin_read_counts, pin_prefix_hit_pairs, pin_block_table_sharing]
+            pin_chain_as_tree, pin_read_counts, pin_prefix_hit_pairs, pin_block_table_sharing]
 
 
 @pytest.mark.parametrize("pin", ALL_PINS, ids=lambda f: f.__name__)
@@ -374,8 +431,10 @@ MUTATIONS = {
     "no max shift sign": ("w = np.exp(z - zmax)", "w = np.exp(z + zmax - 2 * zmax.max())"),
     "gqa modulo": ("return h // (num_qo_heads // num_kv_heads)", "return h % num_kv_heads"),
     "slot/page swapped": ("return np.asarray(pool[pages, t % page_size]", "return np.asarray(pool[pages, t // page_size % page_size]"),
-    "draft excludes self (pass B)": ("k[:s + 1, g],\n                                         v[:s + 1, g]", "k[:s, g],\n                                         v[:s, g]"),
-    "naive excludes self": ("kd[:s + 1]], axis=0)\n            v = np.concatenate([vp, vd[:s + 1]]", "kd[:s]], axis=0)\n            v = np.concatenate([vp, vd[:s]]"),
+    "draft excludes self (chains)": ("return np.arange(s + 1)", "return np.arange(s)"),
+    "tree mask shifted": ("if (m >> u) & 1]", "if (m >> (u + 1)) & 1]"),
+    "tree mask ignored": ("m = int(wl.draft_mask[r0 + s])", "m = (2 << s) - 1"),
+    "naive drops the drafts": ("k = np.concatenate([kp, kd[vis]], axis=0)", "k = np.concatenate([kp, kd[vis[:1]]], axis=0)"),
     "merge weights swapped": ("o = wa[..., None] * o_a + wb[..., None] * o_b", "o = wb[..., None] * o_a + wa[..., None] * o_b"),
     "merge without log": ("lse = np.where(empty, -np.inf, m_safe + np.log(np.where(empty, 1.0, tot)))", "lse = np.where(empty, -np.inf, m_safe + np.where(empty, 1.0, tot) - 1)"),
     "prefix off by one": ("t = int(first_slot) + np.arange(int(count))", "t = int(first_slot) + 1 + np.arange(int(count))"),
