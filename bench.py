@@ -23,7 +23,8 @@ which the library records HIP events on the same stream immediately around
 its kernel (cascade_kernel_timing), i.e. without the dispatch latency that an
 event pair around the call also measures.
 
-The line also carries the prefix-hit suffix prefill (B=4, N=8192, hit ratio
+The line also carries the same shapes with one 20-node random draft tree per
+request (tree attention mask), and the prefix-hit suffix prefill (B=4, N=8192, hit ratio
 h = 0, 0.5, 0.9; three calls, cold protocol) beside the closed-form work
 ratio 1 - H(H+1)/(N(N+1)), unless --no-prefix-hit.
 """
@@ -146,6 +147,29 @@ def cpu_baseline(wl, kv_bytes, budget_s):
             "query_tok_per_s": wl.total_rows / dt}
 
 
+def draft_tree_timing(B, W, torch, flush, steps, warmup):
+    """The headline shapes with one 20-node random draft tree per request (tree
+    attention mask) instead of 4 chains of 5: fused verify, cold protocol."""
+    wl = W.tree_headline()
+    kv_bytes, _, q_bytes, o_bytes = workload_bytes(wl)
+    x = B.to_device(wl, "cuda", layout="HND")
+    ws = B.workspace_for(x)
+    o = torch.empty(wl.q.shape, dtype=torch.bfloat16, device="cuda")
+    lse = torch.empty(wl.q.shape[:2], dtype=torch.float32, device="cuda")
+
+    def verify():
+        B.cascade_verify_attn(x, o=o, lse=lse, workspace=ws)
+
+    ms, _ = time_steps(verify, steps, warmup, flush, torch)
+    k_ms = time_kernel(verify, steps, flush, B)
+    t, kt = float(np.mean(ms)), float(np.mean(k_ms))
+    return {"workload": "B=32, Hq=32, Hkv=8, d=128, L=2000, one 20-node draft tree per request, "
+                        "page 16, HND",
+            "ms_per_step": t, "kv_GBps": kv_bytes / (t * 1e-3) / 1e9,
+            "query_tok_per_s": wl.total_rows / (t * 1e-3), "kernel_ms": kt,
+            "roofline_frac": (kv_bytes + q_bytes + o_bytes) / (kt * 1e-3) / 1e9 / HBM_PEAK_GBS}
+
+
 def prefix_hit_timings(B, W, torch, flush, steps=5, warmup=2):
     """Prefix-hit suffix prefill (B=4 requests of N=8192 tokens, a hit of
     H = floor(h N)): pass A over the hit, pass B causal over the suffix, merge
@@ -193,6 +217,8 @@ def main():
     ap.add_argument("--only-verify", action="store_true", help="time only the fused verify call")
     ap.add_argument("--layout", choices=("HND", "NHD"), default="HND",
                     help="page layout of the KV pool on the device (same logical content)")
+    ap.add_argument("--no-draft-tree", action="store_true",
+                    help="skip the draft-tree variant of the headline shapes")
     ap.add_argument("--no-prefix-hit", action="store_true",
                     help="skip the prefix-hit (suffix prefill) timings")
     ap.add_argument("--traffic-probe", action="store_true",
@@ -313,6 +339,9 @@ def main():
                                       "(hipExtLaunchKernel), mean of K cold steps"},
     }
     line.update(extra)
+    if not args.no_draft_tree and not args.only_verify:
+        print("bench: timing the draft-tree variant", file=sys.stderr, flush=True)
+        line["draft_tree"] = draft_tree_timing(B, W, torch, flush, args.steps, args.warmup)
     if not args.no_prefix_hit and not args.only_verify:
         print("bench: timing prefix-hit suffix prefill (h = 0, 0.5, 0.9)", file=sys.stderr, flush=True)
         line["prefix_hit"] = prefix_hit_timings(B, W, torch, flush)

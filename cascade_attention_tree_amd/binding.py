@@ -58,7 +58,7 @@ class Tree(ctypes.Structure):
                 ("branch_qo_indptr", ctypes.c_void_p), ("draft_page_table", ctypes.c_void_p),
                 ("draft_page_table_stride", ctypes.c_int32), ("draft_start", ctypes.c_void_p),
                 ("max_prefix_len", ctypes.c_int32), ("max_request_rows", ctypes.c_int32),
-                ("max_draft_len", ctypes.c_int32)]
+                ("max_draft_len", ctypes.c_int32), ("draft_mask", ctypes.c_void_p)]
 
 
 class CascadeError(RuntimeError):
@@ -146,6 +146,7 @@ class DeviceInputs:
     query: Query
     kv: PagedKV
     tree: Tree
+    draft_mask: Optional[torch.Tensor] = None   # int64 view of the uint64 ancestor masks
 
     @property
     def total_rows(self) -> int:
@@ -159,8 +160,10 @@ def _bf16_tensor(x: np.ndarray, device) -> torch.Tensor:
 
 def make_structs(q, k_pool, v_pool, page_table, cache_seqlens, req_branch_indptr,
                  branch_qo_indptr, draft_page_table, draft_start, sm_scale,
-                 max_prefix_len, max_request_rows, max_draft_len, layout="NHD"):
-    """layout "NHD": pools are [pages, P, Hkv, d]; "HND": [pages, Hkv, P, d]."""
+                 max_prefix_len, max_request_rows, max_draft_len, layout="NHD",
+                 draft_mask=None):
+    """layout "NHD": pools are [pages, P, Hkv, d]; "HND": [pages, Hkv, P, d].
+    draft_mask: optional 64-bit ancestor masks per row (draft trees)."""
     R, Hq, d = q.shape
     assert k_pool.stride() == v_pool.stride()
     if layout == "NHD":
@@ -177,7 +180,8 @@ def make_structs(q, k_pool, v_pool, page_table, cache_seqlens, req_branch_indptr
                 page_table.data_ptr(), page_table.stride(0), cache_seqlens.data_ptr(),
                 req_branch_indptr.data_ptr(), branch_qo_indptr.data_ptr(),
                 draft_page_table.data_ptr(), draft_page_table.stride(0),
-                _ptr(draft_start), int(max_prefix_len), int(max_request_rows), int(max_draft_len))
+                _ptr(draft_start), int(max_prefix_len), int(max_request_rows), int(max_draft_len),
+                _ptr(draft_mask))
     return query, kv, tree
 
 
@@ -196,10 +200,13 @@ def to_device(wl: "_wl.Workload", device="cuda", layout="NHD") -> DeviceInputs:
         v = v.permute(0, 2, 1, 3).contiguous()
     pt, cs, rb = i32(wl.page_table), i32(wl.cache_seqlens), i32(wl.req_branch_indptr)
     qo, dpt, ds = i32(wl.branch_qo_indptr), i32(wl.draft_page_table), i32(wl.draft_start)
+    dm = None
+    if getattr(wl, "draft_mask", None) is not None:
+        dm = torch.from_numpy(np.ascontiguousarray(wl.draft_mask, np.uint64).view(np.int64)).to(device)
     query, kv, tree = make_structs(q, k, v, pt, cs, rb, qo, dpt, ds, wl.sm_scale,
                                    wl.max_prefix_len(), wl.max_rows_per_request(),
-                                   wl.max_draft_len(), layout)
-    return DeviceInputs(q, k, v, pt, cs, rb, qo, dpt, ds, query, kv, tree)
+                                   wl.max_draft_len(), layout, draft_mask=dm)
+    return DeviceInputs(q, k, v, pt, cs, rb, qo, dpt, ds, query, kv, tree, dm)
 
 
 # ---------------------------------------------------------------------------

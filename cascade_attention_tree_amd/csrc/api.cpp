@@ -144,6 +144,12 @@ cascade_status check_tree(const cascade_tree* t, const cascade_paged_kv* kv) {
   if (t->num_branches > 0 && t->draft_start == nullptr &&
       (int64_t)t->draft_page_table_stride * kv->page_size < t->max_draft_len)
     return fail(CASCADE_ERR_SHAPE, "draft_page_table_stride * page_size < max_draft_len");
+  if (t->draft_mask) {
+    if (t->max_draft_len > 64)
+      return fail(CASCADE_ERR_UNSUPPORTED, "draft trees (draft_mask) are limited to 64 nodes per branch");
+    if (reinterpret_cast<uintptr_t>(t->draft_mask) & 7u)
+      return fail(CASCADE_ERR_UNSUPPORTED, "draft_mask must be 8-byte aligned");
+  }
   return CASCADE_OK;
 }
 
@@ -183,6 +189,7 @@ casc::AttnArgs make_args(const cascade_query* q, const cascade_paged_kv* kv, con
   a.draft_page_table = t->draft_page_table;
   a.draft_page_table_stride = t->draft_page_table_stride;
   a.draft_start = t->draft_start;
+  a.draft_mask = t->draft_mask;
   a.n_chunks = p.n_chunks;
   a.grid_splits = 1;
   a.n_splits = p.n_splits;
@@ -446,6 +453,7 @@ cascade_status cascade_debug_gather(const cascade_paged_kv* kv, const cascade_tr
   a.draft_page_table = t->draft_page_table;
   a.draft_page_table_stride = t->draft_page_table_stride;
   a.draft_start = t->draft_start;
+  a.draft_mask = t->draft_mask;
   a.which = which;
   a.index = index;
   a.kv_head = kv_head;
@@ -465,6 +473,8 @@ cascade_status cascade_debug_mask(const cascade_tree* t, int32_t branch, uint8_t
     return fail(CASCADE_ERR_NULL, "tree arrays are NULL");
   if (!mask_out) return fail(CASCADE_ERR_NULL, "mask_out is NULL");
   if (mask_cols < 0) return fail(CASCADE_ERR_SHAPE, "mask_cols must be >= 0");
+  if (t->draft_mask && (reinterpret_cast<uintptr_t>(t->draft_mask) & 7u))
+    return fail(CASCADE_ERR_UNSUPPORTED, "draft_mask must be 8-byte aligned");
   int32_t ends[2];
   hipError_t e = hipMemcpy(ends, t->branch_qo_indptr + branch, 2 * sizeof(int32_t), hipMemcpyDeviceToHost);
   if (e != hipSuccess) return hip_fail(e, "reading branch length");
@@ -473,6 +483,7 @@ cascade_status cascade_debug_mask(const cascade_tree* t, int32_t branch, uint8_t
   a.cache_seqlens = t->cache_seqlens;
   a.req_branch_indptr = t->req_branch_indptr;
   a.branch_qo_indptr = t->branch_qo_indptr;
+  a.draft_mask = t->draft_mask;
   a.index = branch;
   a.count = ends[1] - ends[0];
   a.cols = mask_cols;

@@ -48,6 +48,7 @@ struct AttnArgs {
   const int32_t* draft_page_table;
   int32_t draft_page_table_stride;
   const int32_t* draft_start;
+  const uint64_t* draft_mask;  // per row: ancestor set over its branch's nodes (NULL: chains)
   int32_t n_chunks;     // row chunks per segment and kv head
   int32_t grid_splits;  // key splits in this launch's grid
   int32_t n_splits;     // key splits of the prefix (partials in the workspace)
@@ -85,6 +86,7 @@ struct DebugArgs {
   const int32_t* draft_page_table;
   int32_t draft_page_table_stride;
   const int32_t* draft_start;
+  const uint64_t* draft_mask;
   int32_t which;
   int32_t index;
   int32_t kv_head;

@@ -279,12 +279,17 @@ attn_kernel(const AttnArgs a) {
     const int t = rho / a.group;
     return (int64_t)(tok0 + t) * a.num_qo_heads + g * a.group + (rho - t * a.group);
   };
+  // Per row: its segment token, its branch's first token, and with a draft
+  // tree its ancestor mask.
   int rtok[RB] = {}, rbs[RB] = {};
+  uint64_t ranc[RB] = {};
+  const bool tree = a.draft_mask != nullptr;
   auto load_row_masks = [&]() {
 #pragma unroll
     for (int rb = 0; rb < RB; ++rb) {
       rtok[rb] = row_tok(rb);
       rbs[rb] = t_rbs[rtok[rb] - tok_first];
+      if (tree) ranc[rb] = a.draft_mask[tok0 + rtok[rb]];
     }
   };
 
@@ -624,7 +629,8 @@ attn_kernel(const AttnArgs a) {
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           const int key = base + kb * 16 + g4 * 4 + i;
-          const bool vis = (key < end) & draft_visible(rtok[rb], rbs[rb], key);
+          const bool vis = (key < end) & (tree ? draft_visible_tree(ranc[rb], rbs[rb], key)
+                                                : draft_visible(rtok[rb], rbs[rb], key));
           s[rb][kb][i] = vis ? s[rb][kb][i] : kNegInf;
         }
       }

@@ -84,6 +84,12 @@ __device__ __forceinline__ int request_of_branch(const int32_t* rb, int batch, i
 __device__ __forceinline__ bool draft_visible(int t, int bs, int kt) {
   return (kt >= bs) & (kt <= t);  // bitwise: a select, not a branch, per key
 }
+// The same for a general draft tree (tree attention mask): the row's ancestor
+// set `anc` over its branch's nodes (bit u: node u, i.e. token bs + u).
+__device__ __forceinline__ bool draft_visible_tree(uint64_t anc, int bs, int kt) {
+  const int u = kt - bs;
+  return (u >= 0) & (u < 64) & (((anc >> (u & 63)) & 1ull) != 0ull);
+}
 
 // Physical offset of draft token `kt` (numbered from the first row of branch
 // jb) of kv head g.  Branch j's token u is at logical slot draft_start[j] + u

@@ -89,7 +89,11 @@ __global__ void __launch_bounds__(256) debug_mask_kernel(const DebugArgs a) {
   if (t < L) {
     vis = 1;
   } else if (t < L + S) {
-    vis = draft_visible(bs + s, bs, bs + (t - L)) ? 1 : 0;
+    const int kt = bs + (t - L);
+    vis = (a.draft_mask ? draft_visible_tree(a.draft_mask[a.branch_qo_indptr[j] + s], bs, kt)
+                        : draft_visible(bs + s, bs, kt))
+              ? 1
+              : 0;
   }
   a.mask_out[idx] = vis;
 }

@@ -137,3 +137,17 @@ def test_kernel_timing_without_a_timed_call():
     v = ctypes.c_float(0.0)
     assert lib.cascade_last_verify_ms(ctypes.byref(v)) == B.CASCADE_ERR_SHAPE
     assert b"timed" in lib.cascade_last_error()
+
+
+def test_draft_tree_limits():
+    q, kv, t = make(dmax=65)
+    t.draft_page_table_stride = 8
+    mask = (ctypes.c_uint64 * 64)()
+    t.draft_mask = ctypes.addressof(mask)
+    assert call_verify(q, kv, t) == B.CASCADE_ERR_UNSUPPORTED
+    assert b"64 nodes" in B.lib().cascade_last_error()
+    q, kv, t = make(dmax=64)
+    t.draft_page_table_stride = 8
+    t.draft_mask = ctypes.addressof(mask) + 4
+    assert call_verify(q, kv, t) == B.CASCADE_ERR_UNSUPPORTED
+    assert b"8-byte aligned" in B.lib().cascade_last_error()

@@ -67,6 +67,12 @@ def small_cases():
         # the per-workgroup branch window holds (130): the tree tables' slow paths.
         "wide_tree": lambda: W.build_workload("wide_tree", [300, 50], [[1] * 70, [2] * 130], 4, 2, 64, 16,
                                               seed=26),
+        # General draft trees (ancestor masks): one tree per request, incl. an
+        # empty prefix; 64- and 33-node trees over several row chunks at d = 64.
+        "draft_tree": lambda: W.attach_random_trees(
+            W.build_workload("draft_tree", [75, 0, 300], [[12], [7], [20]], 8, 2, 128, 16, seed=27), 28),
+        "draft_tree_big": lambda: W.attach_random_trees(
+            W.build_workload("draft_tree_big", [200, 40], [[64], [33]], 16, 2, 64, 16, seed=29), 30),
     }
 
 
@@ -230,8 +236,12 @@ def test_prefix_hit_full_sampled(B, h):
     cmp(o, l, ro, rl, rows=r)
 
 
-def test_gather_and_mask_bit_exact(B):
+@pytest.mark.parametrize("tree", [False, True])
+def test_gather_and_mask_bit_exact(B, tree):
     wl = W.build_workload("gm", [75, 0, 300], [[2, 4, 1], [3], [1, 5]], 8, 2, 128, 16, seed=51)
+    if tree:
+        wl = W.build_workload("gm_tree", [75, 0, 300], [[13], [3], [40]], 8, 2, 128, 16, seed=52)
+        W.attach_random_trees(wl, 53)
     x = B.to_device(wl)
     kbits = W.bf16_bits(wl.k_pool)
     vbits = W.bf16_bits(wl.v_pool)
