@@ -622,16 +622,31 @@ attn_kernel(const AttnArgs a) {
   // Draft keys: the bound `end` and the in-branch ancestor rule (rtok / rbs
   // must have been loaded by load_row_masks).
   auto mask_draft = [&](int base, int end, f32x4 (&s)[RB][2]) {
+    // One uniform branch per tile picks the rule (tree masks or chains).
+    if (tree) {
 #pragma unroll
-    for (int rb = 0; rb < RB; ++rb) {
+      for (int rb = 0; rb < RB; ++rb) {
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
+        for (int kb = 0; kb < 2; ++kb) {
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int key = base + kb * 16 + g4 * 4 + i;
-          const bool vis = (key < end) & (tree ? draft_visible_tree(ranc[rb], rbs[rb], key)
-                                                : draft_visible(rtok[rb], rbs[rb], key));
-          s[rb][kb][i] = vis ? s[rb][kb][i] : kNegInf;
+          for (int i = 0; i < 4; ++i) {
+            const int key = base + kb * 16 + g4 * 4 + i;
+            const bool vis = (key < end) & draft_visible_tree(ranc[rb], rbs[rb], key);
+            s[rb][kb][i] = vis ? s[rb][kb][i] : kNegInf;
+          }
+        }
+      }
+    } else {
+#pragma unroll
+      for (int rb = 0; rb < RB; ++rb) {
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb) {
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const int key = base + kb * 16 + g4 * 4 + i;
+            const bool vis = (key < end) & draft_visible(rtok[rb], rbs[rb], key);
+            s[rb][kb][i] = vis ? s[rb][kb][i] : kNegInf;
+          }
         }
       }
     }
