@@ -68,6 +68,64 @@ def gather_slots(pool, table_row, first_slot, count, page_size):
     return np.asarray(pool[pages, t % page_size], dtype=np.float64)
 
 
+def scatter_slots(pool, table_row, first_slot, values, page_size):
+    """The inverse of gather_slots: a copy of ``pool`` with ``values`` [count,
+    Hkv, d] written at logical slots [first_slot, first_slot + count) of one
+    block-table row."""
+    out = np.array(pool, copy=True)
+    t = int(first_slot) + np.arange(values.shape[0])
+    pages = np.asarray(table_row)[t // page_size]
+    out[pages, t % page_size] = values
+    return out
+
+
+# ---------------------------------------------------------------------------
+# The serving step around verification (tutorial page, sections 5.2 and 8):
+# the drafts' K/V are written into their pages before the verify pass, and
+# after it the accepted path's K/V join the request's prefix.
+# ---------------------------------------------------------------------------
+
+def append_draft_kv(wl, k_new, v_new):
+    """K and V of every query row's draft token, [total_rows, Hkv, d], written
+    to its slot: row r = position u of branch j goes to logical slot
+    draft_start[j] + u of draft block-table row j.  Returns (k_pool, v_pool)."""
+    k_pool, v_pool = wl.k_pool, wl.v_pool
+    qo = wl.branch_qo_indptr
+    for j in range(wl.num_branches):
+        r0, r1 = int(qo[j]), int(qo[j + 1])
+        k_pool = scatter_slots(k_pool, wl.draft_page_table[j], int(wl.draft_start[j]),
+                               np.asarray(k_new[r0:r1]), wl.page_size)
+        v_pool = scatter_slots(v_pool, wl.draft_page_table[j], int(wl.draft_start[j]),
+                               np.asarray(v_new[r0:r1]), wl.page_size)
+    return k_pool, v_pool
+
+
+def commit_accepted(wl, accepted_indptr, accepted_rows):
+    """For request i, the accepted rows accepted_rows[accepted_indptr[i] ..
+    accepted_indptr[i+1]) (global query rows, in path order) have their draft
+    tokens' K and V appended to the prefix: slots L_i, L_i + 1, ... of block-table
+    row i.  Returns (k_pool, v_pool, new cache_seqlens).  Nothing else changes,
+    so rejected drafts cost nothing (their slots are rewritten next step)."""
+    k_pool, v_pool = wl.k_pool, wl.v_pool
+    br_of = _branch_of_row(wl.branch_qo_indptr)
+    lens = np.array(wl.cache_seqlens, np.int64, copy=True)
+    for i in range(wl.batch_size):
+        rows = [int(r) for r in accepted_rows[int(accepted_indptr[i]):int(accepted_indptr[i + 1])]]
+        if not rows:
+            continue
+        ks, vs = [], []
+        for r in rows:
+            j = int(br_of[r])
+            slot = int(wl.draft_start[j]) + r - int(wl.branch_qo_indptr[j])
+            ks.append(gather_slots(wl.k_pool, wl.draft_page_table[j], slot, 1, wl.page_size)[0])
+            vs.append(gather_slots(wl.v_pool, wl.draft_page_table[j], slot, 1, wl.page_size)[0])
+        L = int(wl.cache_seqlens[i])
+        k_pool = scatter_slots(k_pool, wl.page_table[i], L, np.array(ks), wl.page_size)
+        v_pool = scatter_slots(v_pool, wl.page_table[i], L, np.array(vs), wl.page_size)
+        lens[i] = L + len(rows)
+    return k_pool, v_pool, lens.astype(np.int32)
+
+
 # ---------------------------------------------------------------------------
 # One attention state (cascade page, "splittability of standard attention")
 # ---------------------------------------------------------------------------

@@ -337,6 +337,53 @@ def pin_chain_as_tree(O):
             assert vm[s, L:].nonzero()[0].tolist() == ancestors(wl, j, s)
 
 
+def pin_append_commit(O):
+    """Appended drafts read back through the draft block tables as written, every
+    other slot untouched; committed rows extend the prefix in path order and
+    lengths grow by their count; committing nothing changes nothing."""
+    import copy
+    for wl in (wl_tiny(), wl_gqa_tree()):
+        wl.k_pool = np.nan_to_num(wl.k_pool, nan=7.0)
+        wl.v_pool = np.nan_to_num(wl.v_pool, nan=7.0)
+        rng = np.random.default_rng(21)
+        R = wl.total_rows
+        k_new = rng.standard_normal((R, wl.num_kv_heads, wl.head_dim)).astype(np.float32)
+        v_new = rng.standard_normal((R, wl.num_kv_heads, wl.head_dim)).astype(np.float32)
+        k2, v2 = O.append_draft_kv(wl, k_new, v_new)
+        qo, P = wl.branch_qo_indptr, wl.page_size
+        written = np.zeros(wl.k_pool.shape[:2], bool)
+        for j in range(wl.num_branches):
+            r0, r1 = int(qo[j]), int(qo[j + 1])
+            u = int(wl.draft_start[j]) + np.arange(r1 - r0)
+            pages = wl.draft_page_table[j][u // P]
+            assert np.array_equal(k2[pages, u % P], k_new[r0:r1])
+            assert np.array_equal(v2[pages, u % P], v_new[r0:r1])
+            written[pages, u % P] = True
+        assert np.array_equal(k2[~written], wl.k_pool[~written])
+        assert np.array_equal(v2[~written], wl.v_pool[~written])
+        w2 = copy.copy(wl)
+        w2.k_pool, w2.v_pool = k2, v2
+        # accept a path per request: the first rows of its first branch
+        rb = wl.req_branch_indptr
+        acc, ind = [], [0]
+        for i in range(wl.batch_size):
+            j = int(rb[i])
+            n = min(2, int(qo[j + 1] - qo[j]))
+            acc += list(range(int(qo[j]), int(qo[j]) + n))
+            ind.append(len(acc))
+        k3, v3, lens = O.commit_accepted(w2, np.array(ind), np.array(acc))
+        for i in range(wl.batch_size):
+            L, n = int(wl.cache_seqlens[i]), ind[i + 1] - ind[i]
+            assert lens[i] == L + n
+            t = L + np.arange(n)
+            pages = wl.page_table[i][t // P]
+            assert np.array_equal(k3[pages, t % P], k_new[acc[ind[i]:ind[i + 1]]])
+            assert np.array_equal(v3[pages, t % P], v_new[acc[ind[i]:ind[i + 1]]])
+        k4, v4, lens4 = O.commit_accepted(w2, np.zeros(wl.batch_size + 1, int), np.zeros(0, int))
+        assert np.array_equal(k4, k2) and np.array_equal(v4, v2)
+        assert np.array_equal(lens4, wl.cache_seqlens)
+
+
 def pin_read_counts(O):
     """The pages' worked example and formulas for KV tokens read."""
     g = golden("cascade_worked_example.json")
@@ -416,7 +463,8 @@ def pin_block_table_sharing(O):
 
 ALL_PINS = [pin_gather, pin_single_key, pin_attention_vs_library, pin_merge_identity,
             pin_merge_closed_forms, pin_brute_force, pin_topk1_is_causal, pin_zero_query,
-            pin_chain_as_tree, pin_read_counts, pin_prefix_hit_pairs, pin_block_table_sharing]
+            pin_chain_as_tree, pin_append_commit, pin_read_counts, pin_prefix_hit_pairs,
+            pin_block_table_sharing]
 
 
 @pytest.mark.parametrize("pin", ALL_PINS, ids=lambda f: f.__name__)
@@ -441,6 +489,10 @@ MUTATIONS = {
     "naive reads prefix once": ("naive = int(sum(L[req_of[j]] + S[j] for j in range(S.shape[0])))", "naive = int(L.sum() + S.sum())"),
     "draft start ignored": ("s0 = int(wl.draft_start[j])", "s0 = 0"),
     "causal pairs strict": ("if t <= p:", "if t < p:"),
+    "commit at the wrong slot": ("k_pool = scatter_slots(k_pool, wl.page_table[i], L, np.array(ks), wl.page_size)",
+                                 "k_pool = scatter_slots(k_pool, wl.page_table[i], L + 1, np.array(ks), wl.page_size)"),
+    "append ignores draft_start": ("k_pool = scatter_slots(k_pool, wl.draft_page_table[j], int(wl.draft_start[j]),",
+                                   "k_pool = scatter_slots(k_pool, wl.draft_page_table[j], 0,"),
 }
 
 
