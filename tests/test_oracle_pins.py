@@ -342,7 +342,8 @@ def pin_append_commit(O):
     other slot untouched; committed rows extend the prefix in path order and
     lengths grow by their count; committing nothing changes nothing."""
     import copy
-    for wl in (wl_tiny(), wl_gqa_tree()):
+    hit = W.prefix_hit(0.5, values="fp32", keep_logical=True, batch=2, n_tokens=45)
+    for wl in (wl_tiny(), wl_gqa_tree(), hit):
         wl.k_pool = np.nan_to_num(wl.k_pool, nan=7.0)
         wl.v_pool = np.nan_to_num(wl.v_pool, nan=7.0)
         rng = np.random.default_rng(21)
@@ -361,8 +362,19 @@ def pin_append_commit(O):
             written[pages, u % P] = True
         assert np.array_equal(k2[~written], wl.k_pool[~written])
         assert np.array_equal(v2[~written], wl.v_pool[~written])
+        # room for the committed tokens: one fresh page per request, appended to
+        # the pool and to the end of each block-table row
+        B_, npg = wl.batch_size, wl.k_pool.shape[0]
+        fresh = np.zeros((B_,) + wl.k_pool.shape[1:], np.float32)
         w2 = copy.copy(wl)
-        w2.k_pool, w2.v_pool = k2, v2
+        w2.k_pool = np.concatenate([k2, fresh]); w2.v_pool = np.concatenate([v2, fresh])
+        cols = -(-(wl.cache_seqlens.max() + 2) // P)
+        pt = np.full((B_, max(cols, wl.page_table.shape[1])), -1, np.int32)
+        pt[:, :wl.page_table.shape[1]] = wl.page_table
+        for i in range(B_):
+            pt[i, wl.page_table.shape[1]:] = npg + i
+        w2.page_table = pt
+        k2, v2 = w2.k_pool, w2.v_pool
         # accept a path per request: the first rows of its first branch
         rb = wl.req_branch_indptr
         acc, ind = [], [0]
@@ -376,7 +388,7 @@ def pin_append_commit(O):
             L, n = int(wl.cache_seqlens[i]), ind[i + 1] - ind[i]
             assert lens[i] == L + n
             t = L + np.arange(n)
-            pages = wl.page_table[i][t // P]
+            pages = w2.page_table[i][t // P]
             assert np.array_equal(k3[pages, t % P], k_new[acc[ind[i]:ind[i + 1]]])
             assert np.array_equal(v3[pages, t % P], v_new[acc[ind[i]:ind[i + 1]]])
         k4, v4, lens4 = O.commit_accepted(w2, np.zeros(wl.batch_size + 1, int), np.zeros(0, int))
