@@ -24,7 +24,8 @@ its kernel (cascade_kernel_timing), i.e. without the dispatch latency that an
 event pair around the call also measures.
 
 The line also carries the same shapes with one 20-node random draft tree per
-request (tree attention mask), and the prefix-hit suffix prefill (B=4, N=8192, hit ratio
+request (tree attention mask), an 8-layer step (draft-KV append + verify per
+layer) eager and graph-captured, and the prefix-hit suffix prefill (B=4, N=8192, hit ratio
 h = 0, 0.5, 0.9; three calls, cold protocol) beside the closed-form work
 ratio 1 - H(H+1)/(N(N+1)), unless --no-prefix-hit.
 """
@@ -147,6 +148,47 @@ def cpu_baseline(wl, kv_bytes, budget_s):
             "query_tok_per_s": wl.total_rows / dt}
 
 
+def graph_step_timing(B, torch, flush, wl, x0, n_layers=8, steps=10, warmup=3):
+    """A multi-layer verify step at the headline shapes: for each of n_layers
+    layers (own K/V pools, same tables) the drafts' K/V are appended into their
+    pages, then the fused verify runs.  Timed eagerly and as one captured HIP
+    graph (torch.cuda.CUDAGraph), cold protocol per step."""
+    import copy
+    layers = [x0]
+    for _ in range(n_layers - 1):
+        x = copy.copy(x0)
+        x.k_pool, x.v_pool = x0.k_pool.clone(), x0.v_pool.clone()
+        kv = x0.kv
+        x.kv = B.PagedKV(x.k_pool.data_ptr(), x.v_pool.data_ptr(), kv.num_pages, kv.page_size,
+                         kv.num_kv_heads, kv.head_dim, kv.page_stride, kv.token_stride, kv.head_stride)
+        layers.append(x)
+    wss = [B.workspace_for(x) for x in layers]
+    gen = torch.Generator(device="cuda").manual_seed(5)
+    shape = (wl.total_rows, wl.num_kv_heads, wl.head_dim)
+    drafts = [(torch.randn(shape, generator=gen, device="cuda").to(torch.bfloat16),
+               torch.randn(shape, generator=gen, device="cuda").to(torch.bfloat16)) for _ in layers]
+    outs = [torch.empty(wl.q.shape, dtype=torch.bfloat16, device="cuda") for _ in layers]
+    lses = [torch.empty(wl.q.shape[:2], dtype=torch.float32, device="cuda") for _ in layers]
+
+    def step():
+        for x, (k, v), o, l, ws in zip(layers, drafts, outs, lses, wss):
+            B.cascade_append_draft_kv(x, k, v)
+            B.cascade_verify_attn(x, o=o, lse=l, workspace=ws)
+
+    ms_e, _ = time_steps(step, steps, warmup, flush, torch)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        step()
+    torch.cuda.synchronize()
+    ms_g, _ = time_steps(g.replay, steps, warmup, flush, torch)
+    te, tg = float(np.median(ms_e)), float(np.median(ms_g))
+    return {"layers": n_layers, "eager_ms_per_step": te, "graph_ms_per_step": tg,
+            "graph_ms_per_layer": tg / n_layers,
+            "workload": "headline shapes per layer; per layer: append the 640 drafts' K/V into their "
+                        "pages, then the fused verify"}
+
+
 def draft_tree_timing(B, W, torch, flush, steps, warmup):
     """The headline shapes with one 20-node random draft tree per request (tree
     attention mask) instead of 4 chains of 5: fused verify, cold protocol."""
@@ -217,6 +259,8 @@ def main():
     ap.add_argument("--only-verify", action="store_true", help="time only the fused verify call")
     ap.add_argument("--layout", choices=("HND", "NHD"), default="HND",
                     help="page layout of the KV pool on the device (same logical content)")
+    ap.add_argument("--no-graph-step", action="store_true",
+                    help="skip the multi-layer graph-captured step")
     ap.add_argument("--no-draft-tree", action="store_true",
                     help="skip the draft-tree variant of the headline shapes")
     ap.add_argument("--no-prefix-hit", action="store_true",
@@ -339,6 +383,10 @@ def main():
                                       "(hipExtLaunchKernel), mean of K cold steps"},
     }
     line.update(extra)
+    if not args.no_graph_step and not args.only_verify:
+        print("bench: timing an 8-layer step (append + verify per layer), eager and graph",
+              file=sys.stderr, flush=True)
+        line["graph_step"] = graph_step_timing(B, torch, flush, wl, x)
     if not args.no_draft_tree and not args.only_verify:
         print("bench: timing the draft-tree variant", file=sys.stderr, flush=True)
         line["draft_tree"] = draft_tree_timing(B, W, torch, flush, args.steps, args.warmup)

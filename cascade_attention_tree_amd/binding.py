@@ -33,7 +33,8 @@ EXPORTED = (
     "cascade_workspace_size", "cascade_prefix_attn", "cascade_draft_attn", "merge_state",
     "cascade_verify_attn", "naive_expand", "cascade_status_string", "cascade_last_error",
     "cascade_debug_gather", "cascade_debug_mask", "cascade_device_error",
-    "cascade_kernel_timing", "cascade_last_verify_ms",
+    "cascade_kernel_timing", "cascade_last_verify_ms", "cascade_append_draft_kv",
+    "cascade_commit_accepted",
 )
 
 
@@ -104,6 +105,12 @@ def lib() -> ctypes.CDLL:
         L.cascade_debug_mask.restype = st
         L.cascade_device_error.argtypes = [P(ctypes.c_int32), ctypes.c_int32]
         L.cascade_device_error.restype = st
+        L.cascade_append_draft_kv.argtypes = [P(PagedKV), P(Tree), ctypes.c_int32, vp, vp,
+                                              ctypes.c_int64, ctypes.c_int64, vp]
+        L.cascade_append_draft_kv.restype = st
+        L.cascade_commit_accepted.argtypes = [P(PagedKV), P(Tree), ctypes.c_int32, vp, vp,
+                                              ctypes.c_int32, vp, vp]
+        L.cascade_commit_accepted.restype = st
         L.cascade_kernel_timing.argtypes = [ctypes.c_int32]
         L.cascade_kernel_timing.restype = st
         L.cascade_last_verify_ms.argtypes = [P(ctypes.c_float)]
@@ -328,3 +335,25 @@ def cascade_last_verify_ms() -> float:
     v = ctypes.c_float(0.0)
     _check(lib().cascade_last_verify_ms(ctypes.byref(v)))
     return float(v.value)
+
+
+def cascade_append_draft_kv(x: DeviceInputs, k_new: torch.Tensor, v_new: torch.Tensor, stream=None) -> None:
+    """Writes every query row's draft K/V (bf16 [total_rows, Hkv, d]) into its
+    slot of the paged pool of ``x`` (in place)."""
+    assert k_new.dtype == torch.bfloat16 and v_new.dtype == torch.bfloat16
+    assert k_new.stride() == v_new.stride() and k_new.shape == v_new.shape
+    _check(lib().cascade_append_draft_kv(ctypes.byref(x.kv), ctypes.byref(x.tree), x.total_rows,
+                                         k_new.data_ptr(), v_new.data_ptr(), k_new.stride(0),
+                                         k_new.stride(1), _stream(stream)))
+
+
+def cascade_commit_accepted(x: DeviceInputs, accepted_indptr: torch.Tensor, accepted_rows: torch.Tensor,
+                            max_accepted: int, cache_seqlens_out: Optional[torch.Tensor] = None,
+                            stream=None) -> None:
+    """Appends each request's accepted draft rows (int32 device tensors) to its
+    prefix in the pool of ``x``; lengths go to ``cache_seqlens_out`` (default:
+    ``x.cache_seqlens`` in place)."""
+    out = x.cache_seqlens if cache_seqlens_out is None else cache_seqlens_out
+    _check(lib().cascade_commit_accepted(ctypes.byref(x.kv), ctypes.byref(x.tree), x.total_rows,
+                                         accepted_indptr.data_ptr(), _ptr(accepted_rows),
+                                         int(max_accepted), out.data_ptr(), _stream(stream)))

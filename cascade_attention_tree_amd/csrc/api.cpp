@@ -505,6 +505,89 @@ cascade_status cascade_device_error(int32_t* flag_out, int32_t clear) {
   return CASCADE_OK;
 }
 
+namespace {
+casc::KvView kv_view(const cascade_paged_kv* kv) {
+  casc::KvView v{};
+  v.k = static_cast<const uint16_t*>(kv->k);
+  v.v = static_cast<const uint16_t*>(kv->v);
+  v.page_stride = kv->page_stride;
+  v.token_stride = kv->token_stride;
+  v.head_stride = kv->head_stride;
+  v.num_pages = kv->num_pages;
+  v.log2_page = ilog2(kv->page_size);
+  v.page_bytes = (int32_t)page_extent_bytes(kv);
+  return v;
+}
+}  // namespace
+
+cascade_status cascade_append_draft_kv(const cascade_paged_kv* kv, const cascade_tree* t, int32_t total_rows,
+                                       const void* k_new, const void* v_new, int64_t new_row_stride,
+                                       int64_t new_head_stride, void* stream) {
+  cascade_status st = check_kv(kv);
+  if (st != CASCADE_OK) return st;
+  if ((st = check_tree(t, kv)) != CASCADE_OK) return st;
+  if (total_rows < 0) return fail(CASCADE_ERR_SHAPE, "total_rows must be >= 0");
+  if (total_rows == 0) return CASCADE_OK;
+  if (t->num_branches <= 0) return fail(CASCADE_ERR_SHAPE, "rows without branches");
+  if (!k_new || !v_new) return fail(CASCADE_ERR_NULL, "k_new / v_new is NULL");
+  if (!aligned16(k_new) || !aligned16(v_new)) return fail(CASCADE_ERR_UNSUPPORTED, "k_new / v_new must be 16-byte aligned");
+  if (new_row_stride % 8 || new_head_stride % 8 || new_row_stride < 0 || new_head_stride < 0)
+    return fail(CASCADE_ERR_UNSUPPORTED, "k_new / v_new strides must be non-negative multiples of 8 elements");
+  casc::AppendArgs a{};
+  a.kv = kv_view(kv);
+  a.head_dim = kv->head_dim;
+  a.num_kv_heads = kv->num_kv_heads;
+  a.total_rows = total_rows;
+  a.num_branches = t->num_branches;
+  a.branch_qo_indptr = t->branch_qo_indptr;
+  a.draft_page_table = t->draft_page_table;
+  a.draft_page_table_stride = t->draft_page_table_stride;
+  a.draft_start = t->draft_start;
+  a.k_new = static_cast<const uint16_t*>(k_new);
+  a.v_new = static_cast<const uint16_t*>(v_new);
+  a.new_row_stride = new_row_stride;
+  a.new_head_stride = new_head_stride;
+  const hipError_t e = casc::launch_append_kv(a, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "append launch");
+  return CASCADE_OK;
+}
+
+cascade_status cascade_commit_accepted(const cascade_paged_kv* kv, const cascade_tree* t, int32_t total_rows,
+                                       const int32_t* accepted_indptr, const int32_t* accepted_rows,
+                                       int32_t max_accepted, int32_t* cache_seqlens_out, void* stream) {
+  cascade_status st = check_kv(kv);
+  if (st != CASCADE_OK) return st;
+  if ((st = check_tree(t, kv)) != CASCADE_OK) return st;
+  if (total_rows < 0 || max_accepted < 0) return fail(CASCADE_ERR_SHAPE, "total_rows / max_accepted must be >= 0");
+  if (t->batch_size == 0) return CASCADE_OK;
+  if (!accepted_indptr || !cache_seqlens_out) return fail(CASCADE_ERR_NULL, "accepted_indptr / cache_seqlens_out is NULL");
+  if (max_accepted > 0 && !accepted_rows) return fail(CASCADE_ERR_NULL, "accepted_rows is NULL");
+  if (max_accepted > 0 && !t->page_table) return fail(CASCADE_ERR_NULL, "page_table is NULL");
+  if ((int64_t)t->batch_size * max_accepted * kv->num_kv_heads * 16 > (int64_t)INT32_MAX * 256)
+    return fail(CASCADE_ERR_SHAPE, "commit too large");
+  casc::CommitArgs a{};
+  a.kv = kv_view(kv);
+  a.head_dim = kv->head_dim;
+  a.num_kv_heads = kv->num_kv_heads;
+  a.batch_size = t->batch_size;
+  a.num_branches = t->num_branches;
+  a.total_rows = total_rows;
+  a.max_accepted = max_accepted;
+  a.page_table = t->page_table;
+  a.page_table_stride = t->page_table_stride;
+  a.cache_seqlens = t->cache_seqlens;
+  a.cache_seqlens_out = cache_seqlens_out;
+  a.branch_qo_indptr = t->branch_qo_indptr;
+  a.draft_page_table = t->draft_page_table;
+  a.draft_page_table_stride = t->draft_page_table_stride;
+  a.draft_start = t->draft_start;
+  a.accepted_indptr = accepted_indptr;
+  a.accepted_rows = accepted_rows;
+  const hipError_t e = casc::launch_commit(a, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "commit launch");
+  return CASCADE_OK;
+}
+
 cascade_status cascade_kernel_timing(int32_t enable) {
   if (enable && !g_timing.start) {
     hipError_t e = hipEventCreate(&g_timing.start);

@@ -74,6 +74,43 @@ struct MergeArgs {
 };
 
 // Debug hooks: gather one sequence's K/V, or one branch's visibility mask.
+// Draft-KV append and commit of accepted drafts (the serving step's writes).
+struct AppendArgs {
+  KvView kv;
+  int32_t head_dim;
+  int32_t num_kv_heads;
+  int32_t total_rows;
+  int32_t num_branches;
+  const int32_t* branch_qo_indptr;
+  const int32_t* draft_page_table;
+  int32_t draft_page_table_stride;
+  const int32_t* draft_start;
+  const uint16_t* k_new;  // bf16 [total_rows, Hkv, d] (strided)
+  const uint16_t* v_new;
+  int64_t new_row_stride;
+  int64_t new_head_stride;
+};
+
+struct CommitArgs {
+  KvView kv;
+  int32_t head_dim;
+  int32_t num_kv_heads;
+  int32_t batch_size;
+  int32_t num_branches;
+  int32_t total_rows;
+  int32_t max_accepted;
+  const int32_t* page_table;
+  int32_t page_table_stride;
+  const int32_t* cache_seqlens;  // lengths before the commit
+  int32_t* cache_seqlens_out;    // lengths after it (may alias cache_seqlens)
+  const int32_t* branch_qo_indptr;
+  const int32_t* draft_page_table;
+  int32_t draft_page_table_stride;
+  const int32_t* draft_start;
+  const int32_t* accepted_indptr;  // [batch_size + 1]
+  const int32_t* accepted_rows;    // global query rows, path order
+};
+
 struct DebugArgs {
   KvView kv;
   int32_t head_dim;

@@ -16,6 +16,8 @@ hipError_t launch_attn_d128(int mode, int rb, const AttnArgs& a, int grid, hipSt
                             hipEvent_t ev_start, hipEvent_t ev_stop);
 
 hipError_t launch_merge(const MergeArgs& a, hipStream_t s);
+hipError_t launch_append_kv(const AppendArgs& a, hipStream_t s);
+hipError_t launch_commit(const CommitArgs& a, hipStream_t s);
 hipError_t launch_debug_gather(const DebugArgs& a, hipStream_t s);
 hipError_t launch_debug_mask(const DebugArgs& a, hipStream_t s);
 

@@ -98,6 +98,96 @@ __global__ void __launch_bounds__(256) debug_mask_kernel(const DebugArgs a) {
   a.mask_out[idx] = vis;
 }
 
+// Draft-KV append: query row r, position u of branch j, has its K and V
+// written at logical slot draft_start[j] + u of draft block-table row j.  One
+// group of 16 lanes per (row, kv head), 16 bytes per lane and step.
+__global__ void __launch_bounds__(256) append_kv_kernel(const AppendArgs a) {
+  const int64_t item = ((int64_t)blockIdx.x * blockDim.x + threadIdx.x) >> 4;
+  const int lane = threadIdx.x & 15;
+  if (item >= (int64_t)a.total_rows * a.num_kv_heads) return;
+  const int r = (int)(item / a.num_kv_heads);
+  const int g = (int)(item - (int64_t)r * a.num_kv_heads);
+  if (r >= a.branch_qo_indptr[a.num_branches]) {  // total_rows past the branches' rows
+    if (lane == 0) atomicOr(&g_device_error, kErrRow);
+    return;
+  }
+  const int64_t off = draft_offset(a.kv, a.branch_qo_indptr, a.draft_page_table, a.draft_page_table_stride,
+                                   a.draft_start, 0, a.num_branches, r, g);
+  if (off < 0) {
+    if (lane == 0) atomicOr(&g_device_error, kErrPage);
+    return;
+  }
+  uint16_t* dk = const_cast<uint16_t*>(a.kv.k) + off;
+  uint16_t* dv = const_cast<uint16_t*>(a.kv.v) + off;
+  const int64_t src = (int64_t)r * a.new_row_stride + (int64_t)g * a.new_head_stride;
+  for (int c = lane * 8; c < a.head_dim; c += 128) {
+    *reinterpret_cast<u32x4*>(dk + c) = *reinterpret_cast<const u32x4*>(a.k_new + src + c);
+    *reinterpret_cast<u32x4*>(dv + c) = *reinterpret_cast<const u32x4*>(a.v_new + src + c);
+  }
+}
+
+// Commit: the k-th accepted row of request i has its draft K/V copied to
+// logical slot L_i + k of block-table row i.  One group of 16 lanes per
+// (request, k, kv head); groups past the request's accepted count return.
+__global__ void __launch_bounds__(256) commit_kernel(const CommitArgs a) {
+  const int64_t item = ((int64_t)blockIdx.x * blockDim.x + threadIdx.x) >> 4;
+  const int lane = threadIdx.x & 15;
+  const int64_t per_req = (int64_t)a.max_accepted * a.num_kv_heads;
+  if (item >= (int64_t)a.batch_size * per_req) return;
+  const int i = (int)(item / per_req);
+  const int rem = (int)(item - (int64_t)i * per_req);
+  const int k = rem / a.num_kv_heads;
+  const int g = rem - k * a.num_kv_heads;
+  const int a0 = a.accepted_indptr[i];
+  if (k >= a.accepted_indptr[i + 1] - a0) return;
+  const int r = a.accepted_rows[a0 + k];
+  bool ok = r >= 0 && r < a.total_rows;
+  int64_t src = -1, dst = -1;
+  if (ok) {
+    src = draft_offset(a.kv, a.branch_qo_indptr, a.draft_page_table, a.draft_page_table_stride,
+                       a.draft_start, 0, a.num_branches, r, g);
+    const int slot = a.cache_seqlens[i] + k;
+    if (slot >= 0 && (slot >> a.kv.log2_page) < a.page_table_stride)
+      dst = paged_offset(a.kv, a.page_table + (int64_t)i * a.page_table_stride, slot, g);
+    ok = src >= 0 && dst >= 0;
+  }
+  if (!ok) {
+    if (lane == 0) atomicOr(&g_device_error, r >= 0 && r < a.total_rows ? kErrPage : kErrRow);
+    return;
+  }
+  uint16_t* k_pool = const_cast<uint16_t*>(a.kv.k);
+  uint16_t* v_pool = const_cast<uint16_t*>(a.kv.v);
+  for (int c = lane * 8; c < a.head_dim; c += 128) {
+    *reinterpret_cast<u32x4*>(k_pool + dst + c) = *reinterpret_cast<const u32x4*>(k_pool + src + c);
+    *reinterpret_cast<u32x4*>(v_pool + dst + c) = *reinterpret_cast<const u32x4*>(v_pool + src + c);
+  }
+}
+
+// Lengths after the commit (a launch of its own, after every copy has read
+// the old lengths): L_i += accepted count of request i.
+__global__ void __launch_bounds__(256) commit_lengths_kernel(const CommitArgs a) {
+  const int i = blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= a.batch_size) return;
+  a.cache_seqlens_out[i] = a.cache_seqlens[i] + (a.accepted_indptr[i + 1] - a.accepted_indptr[i]);
+}
+
+hipError_t launch_append_kv(const AppendArgs& a, hipStream_t s) {
+  const int64_t lanes = (int64_t)a.total_rows * a.num_kv_heads * 16;
+  if (lanes == 0) return hipSuccess;
+  hipLaunchKernelGGL(append_kv_kernel, dim3((unsigned)((lanes + 255) / 256)), dim3(256), 0, s, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_commit(const CommitArgs& a, hipStream_t s) {
+  if (a.batch_size == 0) return hipSuccess;
+  const int64_t lanes = (int64_t)a.batch_size * a.max_accepted * a.num_kv_heads * 16;
+  if (lanes > 0) hipLaunchKernelGGL(commit_kernel, dim3((unsigned)((lanes + 255) / 256)), dim3(256), 0, s, a);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(commit_lengths_kernel, dim3((unsigned)((a.batch_size + 255) / 256)), dim3(256), 0, s, a);
+  return hipGetLastError();
+}
+
 hipError_t launch_merge(const MergeArgs& a, hipStream_t s) {
   const int64_t n = a.rows * (a.head_dim / 4);
   if (n == 0) return hipSuccess;

@@ -208,6 +208,36 @@ CASCADE_API cascade_status cascade_debug_mask(const cascade_tree *tree, int32_t 
  * kernel met a page id or row outside its bounds.  Synchronises the device. */
 CASCADE_API cascade_status cascade_device_error(int32_t *flag_out, int32_t clear);
 
+/* The serving step around verification (tutorial page, sections 5.2 and 8):
+ *
+ * cascade_append_draft_kv writes the K and V of every query row's draft token
+ * into its page before the verify pass reads them: row r, position u of branch
+ * j, goes to logical slot draft_start[j] + u of draft block-table row j.
+ * k_new, v_new: bf16 [total_rows, num_kv_heads, head_dim], element (r, g, c) at
+ * k_new + r*new_row_stride + g*new_head_stride + c (strides multiples of 8
+ * elements, 16-byte aligned, device); total_rows must be branch_qo_indptr[
+ * num_branches].  Rows whose slot has no valid page are skipped and raise the
+ * sticky device flag.  Asynchronous on stream; the pool is written in place.
+ *
+ * cascade_commit_accepted appends the accepted drafts to the prefixes after
+ * verification: for request i the rows accepted_rows[accepted_indptr[i] ..
+ * accepted_indptr[i+1]) (global query rows, in path order, device int32) have
+ * their draft K/V copied to logical slots L_i, L_i + 1, ... of block-table row
+ * i (those slots must already be mapped: the caller owns page allocation), then
+ * cache_seqlens_out[i] = L_i + their count (cache_seqlens_out may be
+ * t->cache_seqlens itself: the lengths are updated in place by a second
+ * launch).  max_accepted >= every request's count.  A destination slot may be
+ * the row's own draft slot (drafts continuing the prefix pages) but must not be
+ * the draft slot of another accepted row.  Rejected drafts cost nothing: their
+ * slots are rewritten by the next append.  Both calls are graph-capturable. */
+CASCADE_API cascade_status cascade_append_draft_kv(const cascade_paged_kv *kv, const cascade_tree *t,
+                                       int32_t total_rows, const void *k_new, const void *v_new,
+                                       int64_t new_row_stride, int64_t new_head_stride, void *stream);
+CASCADE_API cascade_status cascade_commit_accepted(const cascade_paged_kv *kv, const cascade_tree *t,
+                                       int32_t total_rows, const int32_t *accepted_indptr,
+                                       const int32_t *accepted_rows, int32_t max_accepted,
+                                       int32_t *cache_seqlens_out, void *stream);
+
 /* Kernel timing, for measurement tools.  With enable != 0, every later
  * cascade_verify_attn call on this thread launches its kernels with HIP events
  * recorded by the command processor immediately around them (the first
