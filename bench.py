@@ -24,7 +24,9 @@ its kernel (cascade_kernel_timing), i.e. without the dispatch latency that an
 event pair around the call also measures.
 
 The line also carries the same shapes with one 20-node random draft tree per
-request (tree attention mask), an 8-layer step (draft-KV append + verify per
+request (tree attention mask), the ragged configuration against its mixed
+roofline, the KV rate as a share of a plain 1 GiB streaming read measured on
+the same box, an 8-layer step (draft-KV append + verify per
 layer) eager and graph-captured, and the prefix-hit suffix prefill (B=4, N=8192, hit ratio
 h = 0, 0.5, 0.9; three calls, cold protocol) beside the closed-form work
 ratio 1 - H(H+1)/(N(N+1)), unless --no-prefix-hit.
@@ -148,6 +150,68 @@ def cpu_baseline(wl, kv_bytes, budget_s):
             "query_tok_per_s": wl.total_rows / dt}
 
 
+def ragged_timing(B, W, torch, flush, steps=10, warmup=3):
+    """The ragged configuration (B=64, L log-uniform in [512, 32768], topk in
+    {2,4,8}, S in {3..8}, Hq=64, Hkv=8, d=128): fused verify, cold protocol,
+    against the mixed roofline sum_i max(bytes_i / 8 TB/s, flops_i / 2.5 PFLOP/s)
+    (bytes_i: request i's prefix and drafts once, K+V bf16; flops_i: 4 d per
+    visible (query row, key) pair and query head)."""
+    wl = W.ragged()
+    kv_bytes, _, q_bytes, o_bytes = workload_bytes(wl)
+    Hkv, d, Hq = wl.num_kv_heads, wl.head_dim, wl.num_qo_heads
+    rb, qo = wl.req_branch_indptr, wl.branch_qo_indptr
+    t_roof = 0.0
+    for i in range(wl.batch_size):
+        L = int(wl.cache_seqlens[i])
+        S = [int(qo[j + 1] - qo[j]) for j in range(int(rb[i]), int(rb[i + 1]))]
+        bytes_i = (L + sum(S)) * Hkv * d * 4
+        pairs = sum(s_ * L + s_ * (s_ + 1) // 2 for s_ in S)
+        flops_i = 4.0 * d * Hq * pairs
+        t_roof += max(bytes_i / (HBM_PEAK_GBS * 1e9), flops_i / 2.5e15)
+    x = B.to_device(wl, "cuda", layout="HND")
+    ws = B.workspace_for(x)
+    o = torch.empty(wl.q.shape, dtype=torch.bfloat16, device="cuda")
+    lse = torch.empty(wl.q.shape[:2], dtype=torch.float32, device="cuda")
+
+    def verify():
+        B.cascade_verify_attn(x, o=o, lse=lse, workspace=ws)
+
+    ms, _ = time_steps(verify, steps, warmup, flush, torch)
+    k_ms = time_kernel(verify, steps, flush, B)
+    t, kt = float(np.median(ms)), float(np.mean(k_ms))
+    out = {"workload": "ragged: B=64, L log-uniform [512, 32768], topk {2,4,8}, S {3..8}, Hq=64, Hkv=8, "
+                       "d=128, page 16, HND",
+           "total_prefix_tokens": int(wl.cache_seqlens.sum()), "query_rows": wl.total_rows,
+           "median_ms": t, "kernel_ms": kt, "kv_GBps": kv_bytes / (t * 1e-3) / 1e9,
+           "query_tok_per_s": wl.total_rows / (t * 1e-3),
+           "mixed_roofline_ms": t_roof * 1e3, "frac_of_mixed_roofline": t_roof / (kt * 1e-3)}
+    del x, ws, o, lse
+    torch.cuda.empty_cache()
+    return out
+
+
+def streaming_read_GBps(B, torch, steps=10):
+    """A plain streaming read on the same box (the library's reference read
+    kernel over a 1 GiB buffer, another 1 GiB read between runs to evict it),
+    median of the event-timed runs."""
+    a = torch.ones(1 << 28, dtype=torch.float32, device="cuda")
+    b = torch.ones(1 << 28, dtype=torch.float32, device="cuda")
+    sink = torch.zeros(4, dtype=torch.int32, device="cuda")
+    ts = []
+    for k in range(steps + 2):
+        B.cascade_stream_read(b, sink)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        B.cascade_stream_read(a, sink)
+        e1.record()
+        torch.cuda.synchronize()
+        if k >= 2:
+            ts.append(e0.elapsed_time(e1))
+    del a, b
+    torch.cuda.empty_cache()
+    return (1 << 30) / (float(np.median(ts)) * 1e-3) / 1e9
+
+
 def graph_step_timing(B, torch, flush, wl, x0, n_layers=8, steps=10, warmup=3):
     """A multi-layer verify step at the headline shapes: for each of n_layers
     layers (own K/V pools, same tables) the drafts' K/V are appended into their
@@ -259,6 +323,8 @@ def main():
     ap.add_argument("--only-verify", action="store_true", help="time only the fused verify call")
     ap.add_argument("--layout", choices=("HND", "NHD"), default="HND",
                     help="page layout of the KV pool on the device (same logical content)")
+    ap.add_argument("--no-ragged", action="store_true",
+                    help="skip the ragged configuration")
     ap.add_argument("--no-graph-step", action="store_true",
                     help="skip the multi-layer graph-captured step")
     ap.add_argument("--no-draft-tree", action="store_true",
@@ -383,6 +449,13 @@ def main():
                                       "(hipExtLaunchKernel), mean of K cold steps"},
     }
     line.update(extra)
+    if not args.only_verify:
+        sr = streaming_read_GBps(B, torch)
+        line["streaming_read_GBps"] = sr
+        line["pct_streaming_read"] = 100.0 * kv_gbs / sr
+    if not args.no_ragged and not args.only_verify:
+        print("bench: timing the ragged configuration", file=sys.stderr, flush=True)
+        line["ragged"] = ragged_timing(B, W, torch, flush)
     if not args.no_graph_step and not args.only_verify:
         print("bench: timing an 8-layer step (append + verify per layer), eager and graph",
               file=sys.stderr, flush=True)

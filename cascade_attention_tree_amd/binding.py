@@ -34,7 +34,7 @@ EXPORTED = (
     "cascade_verify_attn", "naive_expand", "cascade_status_string", "cascade_last_error",
     "cascade_debug_gather", "cascade_debug_mask", "cascade_device_error",
     "cascade_kernel_timing", "cascade_last_verify_ms", "cascade_append_draft_kv",
-    "cascade_commit_accepted",
+    "cascade_commit_accepted", "cascade_stream_read",
 )
 
 
@@ -111,6 +111,8 @@ def lib() -> ctypes.CDLL:
         L.cascade_commit_accepted.argtypes = [P(PagedKV), P(Tree), ctypes.c_int32, vp, vp,
                                               ctypes.c_int32, vp, vp]
         L.cascade_commit_accepted.restype = st
+        L.cascade_stream_read.argtypes = [vp, ctypes.c_size_t, vp, vp]
+        L.cascade_stream_read.restype = st
         L.cascade_kernel_timing.argtypes = [ctypes.c_int32]
         L.cascade_kernel_timing.restype = st
         L.cascade_last_verify_ms.argtypes = [P(ctypes.c_float)]
@@ -357,3 +359,9 @@ def cascade_commit_accepted(x: DeviceInputs, accepted_indptr: torch.Tensor, acce
     _check(lib().cascade_commit_accepted(ctypes.byref(x.kv), ctypes.byref(x.tree), x.total_rows,
                                          accepted_indptr.data_ptr(), _ptr(accepted_rows),
                                          int(max_accepted), out.data_ptr(), _stream(stream)))
+
+
+def cascade_stream_read(buf: torch.Tensor, sink: torch.Tensor, stream=None) -> None:
+    """Plain streaming read of ``buf`` (a measurement reference)."""
+    _check(lib().cascade_stream_read(buf.data_ptr(), buf.numel() * buf.element_size(), sink.data_ptr(),
+                                     _stream(stream)))

@@ -588,6 +588,15 @@ cascade_status cascade_commit_accepted(const cascade_paged_kv* kv, const cascade
   return CASCADE_OK;
 }
 
+cascade_status cascade_stream_read(const void* buf, size_t bytes, uint32_t* sink, void* stream) {
+  if (bytes == 0) return CASCADE_OK;
+  if (!buf || !sink) return fail(CASCADE_ERR_NULL, "buf / sink is NULL");
+  if (!aligned16(buf) || bytes % 16) return fail(CASCADE_ERR_UNSUPPORTED, "buf must be 16-byte aligned, bytes a multiple of 16");
+  const hipError_t e = casc::launch_stream_read(buf, bytes, sink, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "stream read launch");
+  return CASCADE_OK;
+}
+
 cascade_status cascade_kernel_timing(int32_t enable) {
   if (enable && !g_timing.start) {
     hipError_t e = hipEventCreate(&g_timing.start);

@@ -17,6 +17,7 @@ hipError_t launch_attn_d128(int mode, int rb, const AttnArgs& a, int grid, hipSt
 
 hipError_t launch_merge(const MergeArgs& a, hipStream_t s);
 hipError_t launch_append_kv(const AppendArgs& a, hipStream_t s);
+hipError_t launch_stream_read(const void* buf, size_t bytes, unsigned int* sink, hipStream_t s);
 hipError_t launch_commit(const CommitArgs& a, hipStream_t s);
 hipError_t launch_debug_gather(const DebugArgs& a, hipStream_t s);
 hipError_t launch_debug_mask(const DebugArgs& a, hipStream_t s);

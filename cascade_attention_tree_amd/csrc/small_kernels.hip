@@ -188,6 +188,36 @@ hipError_t launch_commit(const CommitArgs& a, hipStream_t s) {
   return hipGetLastError();
 }
 
+// Plain streaming read (a measurement reference): every 16-byte chunk of the
+// buffer is loaded once, eight loads in flight per lane, folded with XOR; the
+// fold is stored only if it equals an unlikely pattern (the store keeps the
+// loads alive).  512 workgroups of 256 lanes, contiguous per workgroup.
+__global__ void __launch_bounds__(256) stream_read_kernel(const u32x4* __restrict__ buf, int64_t n16,
+                                                          unsigned int* sink) {
+  const int64_t per = (n16 + gridDim.x - 1) / gridDim.x;
+  const int64_t b0 = (int64_t)blockIdx.x * per;
+  const int64_t b1 = b0 + per < n16 ? b0 + per : n16;
+  u32x4 acc = {0u, 0u, 0u, 0u};
+  for (int64_t i = b0 + threadIdx.x; i < b1; i += 256 * 8) {
+    u32x4 x[8];
+#pragma unroll
+    for (int d = 0; d < 8; ++d) {
+      const int64_t j = i + d * 256;
+      x[d] = j < b1 ? __builtin_nontemporal_load(buf + j) : u32x4{0u, 0u, 0u, 0u};
+    }
+#pragma unroll
+    for (int d = 0; d < 8; ++d) acc ^= x[d];
+  }
+  if (acc[0] == 0x9e3779b9u && acc[1] == 0x7f4a7c15u) sink[0] = acc[2];
+}
+
+hipError_t launch_stream_read(const void* buf, size_t bytes, unsigned int* sink, hipStream_t s) {
+  const int64_t n16 = (int64_t)(bytes / 16);
+  if (n16 == 0) return hipSuccess;
+  hipLaunchKernelGGL(stream_read_kernel, dim3(512), dim3(256), 0, s, static_cast<const u32x4*>(buf), n16, sink);
+  return hipGetLastError();
+}
+
 hipError_t launch_merge(const MergeArgs& a, hipStream_t s) {
   const int64_t n = a.rows * (a.head_dim / 4);
   if (n == 0) return hipSuccess;

@@ -238,6 +238,12 @@ CASCADE_API cascade_status cascade_commit_accepted(const cascade_paged_kv *kv, c
                                        const int32_t *accepted_rows, int32_t max_accepted,
                                        int32_t *cache_seqlens_out, void *stream);
 
+/* Measurement reference: a plain streaming read of `bytes` (multiple of 16) of
+ * device memory at buf (16-byte aligned), nothing written except, in a case
+ * that does not occur for real data, one word at sink (device, 4 bytes).
+ * Asynchronous on stream. */
+CASCADE_API cascade_status cascade_stream_read(const void *buf, size_t bytes, uint32_t *sink, void *stream);
+
 /* Kernel timing, for measurement tools.  With enable != 0, every later
  * cascade_verify_attn call on this thread launches its kernels with HIP events
  * recorded by the command processor immediately around them (the first

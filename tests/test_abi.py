@@ -151,3 +151,15 @@ def test_draft_tree_limits():
     t.draft_mask = ctypes.addressof(mask) + 4
     assert call_verify(q, kv, t) == B.CASCADE_ERR_UNSUPPORTED
     assert b"8-byte aligned" in B.lib().cascade_last_error()
+
+
+def test_stream_read_checks():
+    lib = B.lib()
+    assert lib.cascade_stream_read(None, 0, None, None) == 0
+    assert lib.cascade_stream_read(None, 64, None, None) == B.CASCADE_ERR_NULL
+    buf = (ctypes.c_uint8 * 128)()
+    base = ctypes.addressof(buf)
+    aligned = base + (-base) % 16
+    sink = (ctypes.c_uint32 * 4)()
+    assert lib.cascade_stream_read(aligned + 4, 64, ctypes.addressof(sink), None) == B.CASCADE_ERR_UNSUPPORTED
+    assert lib.cascade_stream_read(aligned, 60, ctypes.addressof(sink), None) == B.CASCADE_ERR_UNSUPPORTED

@@ -178,3 +178,12 @@ def test_graph_captured_multi_layer_step(B):
     ro, rl = O.cascade(w0)
     o = o_e[0].float().cpu().numpy().astype(np.float64)
     assert np.max(np.abs(o - ro)) <= 1e-2
+
+
+def test_stream_read_reference(B):
+    buf = torch.arange(1 << 20, dtype=torch.int32, device="cuda")
+    sink = torch.zeros(4, dtype=torch.int32, device="cuda")
+    note("stream read")
+    B.cascade_stream_read(buf, sink)
+    torch.cuda.synchronize()
+    assert int(sink.abs().sum()) == 0
