@@ -180,9 +180,14 @@ attn_kernel(const AttnArgs a) {
   const int g4 = lane >> 4;
 
   // ---- work item -------------------------------------------------------
+  // Key splits vary slowest and row chunks fastest, so that consecutive
+  // workgroups -- which go to different XCDs round-robin -- take different
+  // chunks, heads and requests of one split: every XCD gets a like share of
+  // the (uneven) work when requests differ in length and row count.
   int item = blockIdx.x;
-  const int split = item % a.grid_splits;
-  item /= a.grid_splits;
+  const int per_split = (int)gridDim.x / a.grid_splits;
+  const int split = item / per_split;
+  item -= split * per_split;
   const int chunk = item % a.n_chunks;
   item /= a.n_chunks;
   const int g = item % a.num_kv_heads;
