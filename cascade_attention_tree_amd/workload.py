@@ -82,6 +82,13 @@ class Workload:
     # breadth-first order, so a parent always precedes its children.
     draft_parent: Optional[np.ndarray] = None
     draft_mask: Optional[np.ndarray] = None
+    # FP8 KV (None: the pools are bf16).  E4M3 codes (uint8, same shape as
+    # k_pool / v_pool) and the per-tensor scales: element x of the pool is held
+    # as code(x / scale).  k_pool / v_pool keep the unquantised values.
+    k_codes: Optional[np.ndarray] = None
+    v_codes: Optional[np.ndarray] = None
+    k_scale: float = 1.0
+    v_scale: float = 1.0
     # Logical (unpaged) copies, kept only when asked for: per request the prefix
     # tokens [L_i, Hkv, d], per branch its draft tokens [S_j, Hkv, d].
     prefix_k: Optional[List[np.ndarray]] = None
@@ -361,3 +368,26 @@ CONFIGS = {
     "headline": headline,
     "ragged": ragged,
 }
+
+
+def with_fp8_kv(wl: Workload, headroom: float = 440.0) -> Workload:
+    """The same workload with FP8 KV: per-tensor scales amax(|pool|) / headroom
+    (rounded to float32) and E4M3 codes of pool / scale, rounded to nearest
+    even by torch's float8_e4m3fn cast.  NaN slots (never-written tokens and
+    spare pages) stay NaN codes.  headroom < 448 keeps every finite value
+    below the largest code, so nothing saturates."""
+    import dataclasses
+
+    import torch
+
+    def encode(pool):
+        fin = np.isfinite(pool)
+        amax = float(np.max(np.abs(pool[fin]))) if fin.any() else 1.0
+        scale = float(np.float32(amax / headroom if amax > 0 else 1.0))
+        x = torch.from_numpy(np.ascontiguousarray(pool, np.float32) / np.float32(scale))
+        codes = x.to(torch.float8_e4m3fn).view(torch.uint8).numpy().copy()
+        return codes, scale
+
+    kc, ks = encode(wl.k_pool)
+    vc, vs = encode(wl.v_pool)
+    return dataclasses.replace(wl, name=wl.name + "_fp8", k_codes=kc, v_codes=vc, k_scale=ks, v_scale=vs)

@@ -43,6 +43,9 @@ Readings taken where the pages leave a step open:
   section 8.2), and a request's tree is one branch holding all of its nodes.
 * Draft token u of branch j lives at logical slot draft_start[j] + u of the
   block-table row draft_page_table[j].
+* FP8 KV (tutorial page, section 4.5, per-tensor granularity): a pool element
+  is an OCP E4M3 code c and stands for value(c) * scale, one scale for all of
+  K and one for all of V; the attention is then the one over those values.
 
 Parity pins: every function here is checked in tests/test_oracle_pins.py
 against closed forms, library routines, brute force on tiny inputs, or the
@@ -52,6 +55,37 @@ numbers the pages print.  No function is parity-unpinned.
 from __future__ import annotations
 
 import numpy as np
+
+
+# ---------------------------------------------------------------------------
+# FP8 KV (tutorial page, section 4.5: FP8 KV cache, per-tensor scale)
+# ---------------------------------------------------------------------------
+
+def e4m3_value(codes):
+    """Values of OCP FP8 E4M3 codes (uint8), float64: sign bit 7, exponent bits
+    6..3 with bias 7, mantissa bits 2..0.  Exponent field e > 0 gives
+    (-1)^s 2^(e-7) (1 + m/8); e = 0 gives the subnormal (-1)^s 2^-6 (m/8).
+    There are no infinities; e = 15 with m = 7 (0x7F, 0xFF) is NaN, so the
+    largest finite magnitude is 2^8 * 1.75 = 448."""
+    c = np.asarray(codes, dtype=np.uint8).astype(np.int64)
+    sign = np.where(c & 0x80, -1.0, 1.0)
+    e = (c >> 3) & 0xF
+    m = (c & 0x7).astype(np.float64)
+    mag = np.where(e > 0, np.ldexp(1.0 + m / 8.0, (e - 7).astype(np.int32)), np.ldexp(m / 8.0, -6))
+    val = sign * mag
+    return np.where((e == 15) & ((c & 0x7) == 7), np.nan, val)
+
+
+def dequantize_kv(wl):
+    """The workload with its K/V pools replaced by the values its FP8 codes
+    stand for (value(code) * scale, float64).  A workload without codes is
+    returned unchanged."""
+    import dataclasses
+    if getattr(wl, "k_codes", None) is None:
+        return wl
+    return dataclasses.replace(wl, k_pool=e4m3_value(wl.k_codes) * float(wl.k_scale),
+                               v_pool=e4m3_value(wl.v_codes) * float(wl.v_scale),
+                               prefix_k=None, prefix_v=None, draft_k=None, draft_v=None)
 
 
 # ---------------------------------------------------------------------------

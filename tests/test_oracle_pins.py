@@ -473,7 +473,57 @@ def pin_block_table_sharing(O):
     assert np.array_equal(o[0], o[1]) and np.array_equal(l[0], l[1])
 
 
-ALL_PINS = [pin_gather, pin_single_key, pin_attention_vs_library, pin_merge_identity,
+def pin_e4m3_values(O):
+    """FP8 E4M3 decode: values fixed by the format's definition, then every
+    code against torch's float8_e4m3fn conversion (a library routine)."""
+    fixed = {0x00: 0.0, 0x80: -0.0, 0x38: 1.0, 0xB8: -1.0, 0x40: 2.0, 0x3C: 1.5,
+             0x7E: 448.0, 0xFE: -448.0, 0x08: 2.0 ** -6, 0x07: 7 * 2.0 ** -9,
+             0x01: 2.0 ** -9, 0x81: -(2.0 ** -9), 0x30: 0.5, 0x28: 0.25, 0x77: 240.0}
+    codes = np.array(sorted(fixed), np.uint8)
+    got = O.e4m3_value(codes)
+    want = np.array([fixed[int(c)] for c in codes])
+    assert np.array_equal(got, want) and np.array_equal(np.signbit(got), np.signbit(want))
+    assert np.all(np.isnan(O.e4m3_value(np.array([0x7F, 0xFF], np.uint8))))
+    allc = np.arange(256, dtype=np.uint8)
+    lib = torch.from_numpy(allc.copy()).view(torch.float8_e4m3fn).to(torch.float64).numpy()
+    ours = O.e4m3_value(allc)
+    assert np.array_equal(np.isnan(ours), np.isnan(lib))
+    fin = ~np.isnan(lib)
+    assert np.array_equal(ours[fin], lib[fin])
+
+
+def wl_fp8(seed=15):
+    wl = W.build_workload("fp8", [37, 0, 70], [[3, 2], [4], [1, 5]], 4, 2, 16, 16, seed=seed,
+                          values="fp32")
+    wl.v_pool = wl.v_pool * np.float32(3.0)   # distinct K and V scales
+    return W.with_fp8_kv(wl)
+
+
+def pin_fp8_dequantize(O):
+    """The dequantised pools are the codes' values times the per-tensor scales
+    (torch's decode of the same codes), and lie within the format's rounding
+    bound of the values that were quantised: half a unit in the last place,
+    i.e. 2^-4 relative for normal codes, 2^-10 * scale for subnormal ones."""
+    wl = wl_fp8()
+    assert wl.k_scale != wl.v_scale
+    dq = O.dequantize_kv(wl)
+    for codes, scale, pool, ref in ((wl.k_codes, wl.k_scale, dq.k_pool, wl.k_pool),
+                                    (wl.v_codes, wl.v_scale, dq.v_pool, wl.v_pool)):
+        lib = torch.from_numpy(codes.copy()).view(torch.float8_e4m3fn).to(torch.float64).numpy() * scale
+        assert np.array_equal(np.isnan(pool), np.isnan(lib))
+        fin = ~np.isnan(lib)
+        assert np.array_equal(pool[fin], lib[fin])
+        assert np.array_equal(np.isnan(pool), np.isnan(ref))
+        x = ref[fin].astype(np.float64)
+        bound = np.maximum(np.abs(x) * 2.0 ** -4, scale * 2.0 ** -10) * (1 + 1e-12)
+        assert np.all(np.abs(pool[fin] - x) <= bound)
+    # A code of 1.0 stands for the scale itself.
+    wl.v_codes[0, 0, 0, :2] = [0x38, 0xB8]
+    dq = O.dequantize_kv(wl)
+    assert dq.v_pool[0, 0, 0, 0] == wl.v_scale and dq.v_pool[0, 0, 0, 1] == -wl.v_scale
+
+
+ALL_PINS = [pin_e4m3_values, pin_fp8_dequantize, pin_gather, pin_single_key, pin_attention_vs_library, pin_merge_identity,
             pin_merge_closed_forms, pin_brute_force, pin_topk1_is_causal, pin_zero_query,
             pin_chain_as_tree, pin_append_commit, pin_read_counts, pin_prefix_hit_pairs,
             pin_block_table_sharing]
@@ -503,6 +553,11 @@ MUTATIONS = {
     "causal pairs strict": ("if t <= p:", "if t < p:"),
     "commit at the wrong slot": ("k_pool = scatter_slots(k_pool, wl.page_table[i], L, np.array(ks), wl.page_size)",
                                  "k_pool = scatter_slots(k_pool, wl.page_table[i], L + 1, np.array(ks), wl.page_size)"),
+    "e4m3 exponent bias 8": ("np.ldexp(1.0 + m / 8.0, (e - 7).astype(np.int32))", "np.ldexp(1.0 + m / 8.0, (e - 8).astype(np.int32))"),
+    "e4m3 subnormals as normals": ("np.ldexp(m / 8.0, -6)", "np.ldexp(1.0 + m / 8.0, -7)"),
+    "e4m3 sign ignored": ("sign = np.where(c & 0x80, -1.0, 1.0)", "sign = np.where(c & 0x40, -1.0, 1.0)"),
+    "fp8 scale dropped": ("k_pool=e4m3_value(wl.k_codes) * float(wl.k_scale)", "k_pool=e4m3_value(wl.k_codes)"),
+    "fp8 V takes the K scale": ("v_pool=e4m3_value(wl.v_codes) * float(wl.v_scale)", "v_pool=e4m3_value(wl.v_codes) * float(wl.k_scale)"),
     "append ignores draft_start": ("k_pool = scatter_slots(k_pool, wl.draft_page_table[j], int(wl.draft_start[j]),",
                                    "k_pool = scatter_slots(k_pool, wl.draft_page_table[j], 0,"),
 }
