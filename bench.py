@@ -62,9 +62,9 @@ def kernel_source_hash() -> str:
     return h.hexdigest()[:16]
 
 
-def workload_bytes(wl):
+def workload_bytes(wl, kv_elem_bytes=2):
     Hkv, d = wl.num_kv_heads, wl.head_dim
-    per_tok = Hkv * d * 2 * 2
+    per_tok = Hkv * d * 2 * kv_elem_bytes
     L = wl.cache_seqlens.astype(np.int64)
     S = np.diff(wl.branch_qo_indptr.astype(np.int64))
     req_of = wl.request_of_branch()
@@ -276,6 +276,40 @@ def draft_tree_timing(B, W, torch, flush, steps, warmup):
             "roofline_frac": (kv_bytes + q_bytes + o_bytes) / (kt * 1e-3) / 1e9 / HBM_PEAK_GBS}
 
 
+def fp8_timing(B, W, torch, flush, wl_bf16, t_bf16_ms, steps, warmup, layout):
+    """The headline workload with FP8 E4M3 KV (per-tensor scales): fused
+    verify and naive expansion, cold protocol, plus the verify kernel's own
+    time against its roofline (KV bytes halve; Q and the output do not)."""
+    wl = W.with_fp8_kv(wl_bf16)
+    kv_bytes, kv_naive, q_bytes, o_bytes = workload_bytes(wl, kv_elem_bytes=1)
+    x = B.to_device(wl, "cuda", layout=layout)
+    ws = B.workspace_for(x)
+    o = torch.empty(wl.q.shape, dtype=torch.bfloat16, device="cuda")
+    lse = torch.empty(wl.q.shape[:2], dtype=torch.float32, device="cuda")
+
+    def verify():
+        B.cascade_verify_attn(x, o=o, lse=lse, workspace=ws)
+
+    def naive():
+        B.naive_expand(x, o=o, lse=lse)
+
+    ms, _ = time_steps(verify, steps, warmup, flush, torch)
+    k_ms = time_kernel(verify, steps, flush, B)
+    ms_n, _ = time_steps(naive, steps, warmup, flush, torch)
+    t, kt, tn = float(np.mean(ms)), float(np.mean(k_ms)), float(np.mean(ms_n))
+    compulsory = kv_bytes + q_bytes + o_bytes
+    return {"workload": "headline shapes, K/V as FP8 E4M3 codes with per-tensor scales, "
+                        f"page 16, {layout}",
+            "ms_per_step": t, "median_ms": float(np.median(ms)), "kv_bytes": kv_bytes,
+            "kv_GBps": kv_bytes / (t * 1e-3) / 1e9,
+            "query_tok_per_s": wl.total_rows / (t * 1e-3),
+            "kernel_ms": kt, "kernel_median_ms": float(np.median(k_ms)),
+            "roofline_frac": compulsory / (kt * 1e-3) / 1e9 / HBM_PEAK_GBS,
+            "algorithmic_bytes_per_launch": compulsory,
+            "speedup_vs_bf16_verify": t_bf16_ms / t,
+            "naive_ms": tn, "speedup_vs_naive_fp8": tn / t}
+
+
 def prefix_hit_timings(B, W, torch, flush, steps=5, warmup=2):
     """Prefix-hit suffix prefill (B=4 requests of N=8192 tokens, a hit of
     H = floor(h N)): pass A over the hit, pass B causal over the suffix, merge
@@ -331,6 +365,10 @@ def main():
                     help="skip the draft-tree variant of the headline shapes")
     ap.add_argument("--no-prefix-hit", action="store_true",
                     help="skip the prefix-hit (suffix prefill) timings")
+    ap.add_argument("--no-fp8", action="store_true",
+                    help="skip the FP8 KV variant of the headline")
+    ap.add_argument("--fp8-only", action="store_true",
+                    help="for profiling: only the FP8 headline verify (cold steps)")
     ap.add_argument("--traffic-probe", action="store_true",
                     help="for hardware-counter runs: one plain 256 MiB device copy (known bytes), "
                          "then a few flushed verify steps; prints nothing else")
@@ -371,6 +409,23 @@ def main():
         B.cascade_prefix_attn(x, o_a=oa, lse_a=la, workspace=ws)
         B.cascade_draft_attn(x, o_b=ob, lse_b=lb)
         B.merge_state(oa, la, ob, lb, out_dtype=torch.bfloat16, o=o, lse=lse)
+
+    if args.fp8_only:
+        wl8 = W.with_fp8_kv(wl)
+        x8 = B.to_device(wl8, "cuda", layout=args.layout)
+        ws8 = B.workspace_for(x8)
+        del x
+        print("bench: FP8 headline verify only", file=sys.stderr, flush=True)
+        if args.traffic_probe:
+            src = torch.ones(1 << 26, dtype=torch.float32, device="cuda")   # 256 MiB
+            dst = torch.empty_like(src)
+            flush()
+            dst.copy_(src)
+        ms, _ = time_steps(lambda: B.cascade_verify_attn(x8, o=o, lse=lse, workspace=ws8),
+                           args.steps, args.warmup, flush, torch)
+        print(json.dumps({"fp8_only": True, "ms_per_step": float(np.mean(ms)),
+                          "kernel_hash": kernel_source_hash()}), flush=True)
+        return
 
     if args.traffic_probe:
         src = torch.ones(1 << 26, dtype=torch.float32, device="cuda")   # 256 MiB
@@ -463,6 +518,9 @@ def main():
     if not args.no_draft_tree and not args.only_verify:
         print("bench: timing the draft-tree variant", file=sys.stderr, flush=True)
         line["draft_tree"] = draft_tree_timing(B, W, torch, flush, args.steps, args.warmup)
+    if not args.no_fp8 and not args.only_verify:
+        print("bench: timing the FP8 KV variant", file=sys.stderr, flush=True)
+        line["fp8_kv"] = fp8_timing(B, W, torch, flush, wl, t_ms, args.steps, args.warmup, args.layout)
     if not args.no_prefix_hit and not args.only_verify:
         print("bench: timing prefix-hit suffix prefill (h = 0, 0.5, 0.9)", file=sys.stderr, flush=True)
         line["prefix_hit"] = prefix_hit_timings(B, W, torch, flush)

@@ -43,7 +43,12 @@ class PagedKV(ctypes.Structure):
                 ("num_pages", ctypes.c_int32), ("page_size", ctypes.c_int32),
                 ("num_kv_heads", ctypes.c_int32), ("head_dim", ctypes.c_int32),
                 ("page_stride", ctypes.c_int64), ("token_stride", ctypes.c_int64),
-                ("head_stride", ctypes.c_int64)]
+                ("head_stride", ctypes.c_int64), ("dtype", ctypes.c_int32),
+                ("k_scale", ctypes.c_float), ("v_scale", ctypes.c_float)]
+
+
+KV_BF16 = 0
+KV_FP8_E4M3 = 1
 
 
 class Query(ctypes.Structure):
@@ -144,7 +149,7 @@ def _stream(stream) -> Optional[int]:
 class DeviceInputs:
     """A workload's arrays on the GPU, plus the C structs that point at them."""
     q: torch.Tensor            # bf16 [R, Hq, d]
-    k_pool: torch.Tensor       # bf16 [pages, P, Hkv, d]
+    k_pool: torch.Tensor       # bf16 (or uint8 E4M3 codes) [pages, P, Hkv, d]
     v_pool: torch.Tensor
     page_table: torch.Tensor   # int32
     cache_seqlens: torch.Tensor
@@ -170,9 +175,11 @@ def _bf16_tensor(x: np.ndarray, device) -> torch.Tensor:
 def make_structs(q, k_pool, v_pool, page_table, cache_seqlens, req_branch_indptr,
                  branch_qo_indptr, draft_page_table, draft_start, sm_scale,
                  max_prefix_len, max_request_rows, max_draft_len, layout="NHD",
-                 draft_mask=None):
+                 draft_mask=None, k_scale=1.0, v_scale=1.0):
     """layout "NHD": pools are [pages, P, Hkv, d]; "HND": [pages, Hkv, P, d].
-    draft_mask: optional 64-bit ancestor masks per row (draft trees)."""
+    Pools are bf16, or uint8 / float8_e4m3fn E4M3 codes with the per-tensor
+    scales k_scale, v_scale.  draft_mask: optional 64-bit ancestor masks per
+    row (draft trees)."""
     R, Hq, d = q.shape
     assert k_pool.stride() == v_pool.stride()
     if layout == "NHD":
@@ -184,7 +191,11 @@ def make_structs(q, k_pool, v_pool, page_table, cache_seqlens, req_branch_indptr
     else:
         raise ValueError(layout)
     query = Query(q.data_ptr(), q.stride(0), q.stride(1), Hq, R, float(sm_scale))
-    kv = PagedKV(k_pool.data_ptr(), v_pool.data_ptr(), num_pages, P, Hkv, d, ps, ts, hs)
+    fp8 = k_pool.dtype in (torch.uint8, torch.float8_e4m3fn)
+    assert k_pool.dtype == v_pool.dtype and (fp8 or k_pool.dtype == torch.bfloat16)
+    kv = PagedKV(k_pool.data_ptr(), v_pool.data_ptr(), num_pages, P, Hkv, d, ps, ts, hs,
+                 KV_FP8_E4M3 if fp8 else KV_BF16, float(k_scale) if fp8 else 0.0,
+                 float(v_scale) if fp8 else 0.0)
     tree = Tree(int(cache_seqlens.shape[0]), int(branch_qo_indptr.shape[0] - 1),
                 page_table.data_ptr(), page_table.stride(0), cache_seqlens.data_ptr(),
                 req_branch_indptr.data_ptr(), branch_qo_indptr.data_ptr(),
@@ -195,15 +206,21 @@ def make_structs(q, k_pool, v_pool, page_table, cache_seqlens, req_branch_indptr
 
 
 def to_device(wl: "_wl.Workload", device="cuda", layout="NHD") -> DeviceInputs:
-    """Uploads a workload (bf16 values, int32 tables) and builds its C structs.
+    """Uploads a workload (bf16 values, or its E4M3 codes when it has FP8 KV;
+    int32 tables) and builds its C structs.
 
     layout "NHD" keeps the generator's token-major pages [pages, P, Hkv, d];
     "HND" stores each page head-major, [pages, Hkv, P, d], so that one kv head's
     tokens of a page are one contiguous run (same logical content)."""
     i32 = lambda a: torch.from_numpy(np.ascontiguousarray(a, np.int32)).to(device)
     q = _bf16_tensor(wl.q, device)
-    k = _bf16_tensor(wl.k_pool, device)
-    v = _bf16_tensor(wl.v_pool, device)
+    fp8 = getattr(wl, "k_codes", None) is not None
+    if fp8:
+        k = torch.from_numpy(np.ascontiguousarray(wl.k_codes, np.uint8)).to(device)
+        v = torch.from_numpy(np.ascontiguousarray(wl.v_codes, np.uint8)).to(device)
+    else:
+        k = _bf16_tensor(wl.k_pool, device)
+        v = _bf16_tensor(wl.v_pool, device)
     if layout == "HND":
         k = k.permute(0, 2, 1, 3).contiguous()
         v = v.permute(0, 2, 1, 3).contiguous()
@@ -214,7 +231,8 @@ def to_device(wl: "_wl.Workload", device="cuda", layout="NHD") -> DeviceInputs:
         dm = torch.from_numpy(np.ascontiguousarray(wl.draft_mask, np.uint64).view(np.int64)).to(device)
     query, kv, tree = make_structs(q, k, v, pt, cs, rb, qo, dpt, ds, wl.sm_scale,
                                    wl.max_prefix_len(), wl.max_rows_per_request(),
-                                   wl.max_draft_len(), layout, draft_mask=dm)
+                                   wl.max_draft_len(), layout, draft_mask=dm,
+                                   k_scale=wl.k_scale if fp8 else 1.0, v_scale=wl.v_scale if fp8 else 1.0)
     return DeviceInputs(q, k, v, pt, cs, rb, qo, dpt, ds, query, kv, tree, dm)
 
 
@@ -340,9 +358,10 @@ def cascade_last_verify_ms() -> float:
 
 
 def cascade_append_draft_kv(x: DeviceInputs, k_new: torch.Tensor, v_new: torch.Tensor, stream=None) -> None:
-    """Writes every query row's draft K/V (bf16 [total_rows, Hkv, d]) into its
-    slot of the paged pool of ``x`` (in place)."""
-    assert k_new.dtype == torch.bfloat16 and v_new.dtype == torch.bfloat16
+    """Writes every query row's draft K/V ([total_rows, Hkv, d] in the pool's
+    element type: bf16, or E4M3 codes for an FP8 pool) into its slot of the
+    paged pool of ``x`` (in place)."""
+    assert k_new.dtype == x.k_pool.dtype and v_new.dtype == x.k_pool.dtype
     assert k_new.stride() == v_new.stride() and k_new.shape == v_new.shape
     _check(lib().cascade_append_draft_kv(ctypes.byref(x.kv), ctypes.byref(x.tree), x.total_rows,
                                          k_new.data_ptr(), v_new.data_ptr(), k_new.stride(0),

@@ -76,10 +76,27 @@ void plan_splits(Plan& p, int max_len) {
   p.n_splits = (int)cdiv(len, p.split_len);
 }
 
+bool kv_fp8(const cascade_paged_kv* kv) { return kv->dtype == CASCADE_KV_FP8_E4M3; }
+int elem_bytes(const cascade_paged_kv* kv) { return kv_fp8(kv) ? 1 : 2; }
+
 // Bytes from the start of a page to the end of its last (token, head) row.
 int64_t page_extent_bytes(const cascade_paged_kv* kv) {
   return ((int64_t)(kv->page_size - 1) * kv->token_stride +
-          (int64_t)(kv->num_kv_heads - 1) * kv->head_stride + kv->head_dim) * 2;
+          (int64_t)(kv->num_kv_heads - 1) * kv->head_stride + kv->head_dim) * elem_bytes(kv);
+}
+
+casc::KvView kv_view(const cascade_paged_kv* kv) {
+  casc::KvView v{};
+  v.k = static_cast<const uint16_t*>(kv->k);
+  v.v = static_cast<const uint16_t*>(kv->v);
+  v.page_stride = kv->page_stride;
+  v.token_stride = kv->token_stride;
+  v.head_stride = kv->head_stride;
+  v.num_pages = kv->num_pages;
+  v.log2_page = ilog2(kv->page_size);
+  v.page_bytes = (int32_t)page_extent_bytes(kv);
+  v.elem_bytes = elem_bytes(kv);
+  return v;
 }
 
 cascade_status check_kv(const cascade_paged_kv* kv) {
@@ -87,6 +104,11 @@ cascade_status check_kv(const cascade_paged_kv* kv) {
   if (!kv->k || !kv->v) return fail(CASCADE_ERR_NULL, "kv->k or kv->v is NULL");
   if (kv->num_kv_heads <= 0) return fail(CASCADE_ERR_SHAPE, "num_kv_heads must be > 0");
   if (kv->num_pages <= 0) return fail(CASCADE_ERR_SHAPE, "num_pages must be > 0");
+  if (kv->dtype != CASCADE_KV_BF16 && kv->dtype != CASCADE_KV_FP8_E4M3)
+    return fail(CASCADE_ERR_UNSUPPORTED, "kv dtype %d not supported (bf16 or fp8 e4m3)", (int)kv->dtype);
+  if (kv_fp8(kv) && !(std::isfinite(kv->k_scale) && kv->k_scale > 0.f && std::isfinite(kv->v_scale) &&
+                      kv->v_scale > 0.f))
+    return fail(CASCADE_ERR_SHAPE, "fp8 kv needs finite k_scale and v_scale > 0");
   if (kv->head_dim != 64 && kv->head_dim != 128)
     return fail(CASCADE_ERR_UNSUPPORTED, "head_dim %d not supported (64 or 128)", kv->head_dim);
   if (!is_pow2(kv->page_size) || kv->page_size < 16 || kv->page_size > 4096)
@@ -170,15 +192,13 @@ casc::AttnArgs make_args(const cascade_query* q, const cascade_paged_kv* kv, con
   a.num_qo_heads = q->num_qo_heads;
   a.group = p.group;
   a.total_rows = q->total_rows;
-  a.scale_log2 = q->sm_scale * 1.4426950408889634f;
-  a.kv.k = static_cast<const uint16_t*>(kv->k);
-  a.kv.v = static_cast<const uint16_t*>(kv->v);
-  a.kv.page_stride = kv->page_stride;
-  a.kv.token_stride = kv->token_stride;
-  a.kv.head_stride = kv->head_stride;
-  a.kv.num_pages = kv->num_pages;
-  a.kv.log2_page = ilog2(kv->page_size);
-  a.kv.page_bytes = (int32_t)page_extent_bytes(kv);
+  // FP8 pools: scores are sm_scale * k_scale * (q . codes), the V scale
+  // multiplies the normalised output (a per-tensor scale factors out of both
+  // sums).
+  const double k_scale = kv_fp8(kv) ? (double)kv->k_scale : 1.0;
+  a.scale_log2 = (float)((double)q->sm_scale * k_scale * 1.4426950408889634);
+  a.v_scale = kv_fp8(kv) ? kv->v_scale : 1.f;
+  a.kv = kv_view(kv);
   a.num_kv_heads = kv->num_kv_heads;
   a.batch_size = t->batch_size;
   a.page_table = t->page_table;
@@ -225,8 +245,13 @@ WsLayout ws_layout(const cascade_query* q, const cascade_paged_kv* kv, const Pla
 hipError_t launch(int mode, int head_dim, int rb, const casc::AttnArgs& a, int64_t grid, hipStream_t s,
                   hipEvent_t e0 = nullptr, hipEvent_t e1 = nullptr) {
   if (grid <= 0) return hipSuccess;
-  if (head_dim == 64) return casc::launch_attn_d64(mode, rb, a, (int)grid, s, e0, e1);
-  return casc::launch_attn_d128(mode, rb, a, (int)grid, s, e0, e1);
+  // The split merges read only the fp32 workspace: one kernel for both pool types.
+  const bool fp8 = a.kv.elem_bytes == 1 && mode != casc::kModePrefixFinish && mode != casc::kModeVerifyFinish;
+  if (head_dim == 64)
+    return fp8 ? casc::launch_attn_d64_fp8(mode, rb, a, (int)grid, s, e0, e1)
+               : casc::launch_attn_d64(mode, rb, a, (int)grid, s, e0, e1);
+  return fp8 ? casc::launch_attn_d128_fp8(mode, rb, a, (int)grid, s, e0, e1)
+             : casc::launch_attn_d128(mode, rb, a, (int)grid, s, e0, e1);
 }
 
 // Kernel timing of cascade_verify_attn (per thread; see the header).
@@ -436,13 +461,7 @@ cascade_status cascade_debug_gather(const cascade_paged_kv* kv, const cascade_tr
   if (e != hipSuccess) return hip_fail(e, "reading sequence length");
   if (count < 0) return fail(CASCADE_ERR_SHAPE, "negative sequence length");
   casc::DebugArgs a{};
-  a.kv.k = static_cast<const uint16_t*>(kv->k);
-  a.kv.v = static_cast<const uint16_t*>(kv->v);
-  a.kv.page_stride = kv->page_stride;
-  a.kv.token_stride = kv->token_stride;
-  a.kv.head_stride = kv->head_stride;
-  a.kv.num_pages = kv->num_pages;
-  a.kv.log2_page = ilog2(kv->page_size);
+  a.kv = kv_view(kv);
   a.head_dim = kv->head_dim;
   a.batch_size = t->batch_size;
   a.page_table = t->page_table;
@@ -497,28 +516,18 @@ cascade_status cascade_device_error(int32_t* flag_out, int32_t clear) {
   if (!flag_out) return fail(CASCADE_ERR_NULL, "flag_out is NULL");
   hipError_t e = hipDeviceSynchronize();
   if (e != hipSuccess) return hip_fail(e, "synchronise");
-  int v64 = 0, v128 = 0, vs = 0;
-  if ((e = casc::read_error_d64(&v64, clear)) != hipSuccess) return hip_fail(e, "read error word");
-  if ((e = casc::read_error_d128(&v128, clear)) != hipSuccess) return hip_fail(e, "read error word");
-  if ((e = casc::read_error_small(&vs, clear)) != hipSuccess) return hip_fail(e, "read error word");
-  *flag_out = v64 | v128 | vs;
+  int flags = 0;
+  hipError_t (*const readers[])(int*, int) = {casc::read_error_d64, casc::read_error_d128,
+                                              casc::read_error_d64_fp8, casc::read_error_d128_fp8,
+                                              casc::read_error_small};
+  for (auto* rd : readers) {
+    int v = 0;
+    if ((e = rd(&v, clear)) != hipSuccess) return hip_fail(e, "read error word");
+    flags |= v;
+  }
+  *flag_out = flags;
   return CASCADE_OK;
 }
-
-namespace {
-casc::KvView kv_view(const cascade_paged_kv* kv) {
-  casc::KvView v{};
-  v.k = static_cast<const uint16_t*>(kv->k);
-  v.v = static_cast<const uint16_t*>(kv->v);
-  v.page_stride = kv->page_stride;
-  v.token_stride = kv->token_stride;
-  v.head_stride = kv->head_stride;
-  v.num_pages = kv->num_pages;
-  v.log2_page = ilog2(kv->page_size);
-  v.page_bytes = (int32_t)page_extent_bytes(kv);
-  return v;
-}
-}  // namespace
 
 cascade_status cascade_append_draft_kv(const cascade_paged_kv* kv, const cascade_tree* t, int32_t total_rows,
                                        const void* k_new, const void* v_new, int64_t new_row_stride,
@@ -543,8 +552,8 @@ cascade_status cascade_append_draft_kv(const cascade_paged_kv* kv, const cascade
   a.draft_page_table = t->draft_page_table;
   a.draft_page_table_stride = t->draft_page_table_stride;
   a.draft_start = t->draft_start;
-  a.k_new = static_cast<const uint16_t*>(k_new);
-  a.v_new = static_cast<const uint16_t*>(v_new);
+  a.k_new = k_new;
+  a.v_new = v_new;
   a.new_row_stride = new_row_stride;
   a.new_head_stride = new_head_stride;
   const hipError_t e = casc::launch_append_kv(a, static_cast<hipStream_t>(stream));

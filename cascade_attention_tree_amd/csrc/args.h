@@ -18,6 +18,8 @@ struct KvView {
   int32_t log2_page;
   int32_t page_bytes;  // bytes spanned by one page of K (or V): the range of
                        // its buffer descriptor, so reads past it return zero
+  int32_t elem_bytes;  // 2: bf16 elements; 1: FP8 E4M3 codes (offsets above
+                       // count elements, so they are byte offsets for FP8)
 };
 
 enum AttnMode : int {
@@ -36,7 +38,8 @@ struct AttnArgs {
   int32_t num_qo_heads;
   int32_t group;
   int32_t total_rows;
-  float scale_log2;  // sm_scale * log2(e): scores are kept in base 2
+  float scale_log2;  // sm_scale * k_scale * log2(e): scores are kept in base 2
+  float v_scale;     // FP8 pools: the V scale, applied to normalised outputs
   KvView kv;
   int32_t num_kv_heads;
   int32_t batch_size;
@@ -85,8 +88,8 @@ struct AppendArgs {
   const int32_t* draft_page_table;
   int32_t draft_page_table_stride;
   const int32_t* draft_start;
-  const uint16_t* k_new;  // bf16 [total_rows, Hkv, d] (strided)
-  const uint16_t* v_new;
+  const void* k_new;  // [total_rows, Hkv, d] in the pool element type (strided)
+  const void* v_new;
   int64_t new_row_stride;
   int64_t new_head_stride;
 };

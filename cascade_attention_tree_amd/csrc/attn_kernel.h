@@ -124,7 +124,9 @@ __device__ __forceinline__ i16x4 lds_read_tr16(const uint16_t* p) {
   return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(p));
 }
 
-template <int D, int RB, int MODE>
+// KV8: the pools hold FP8 E4M3 codes (half the bytes per key); each chunk is
+// widened to bf16 when staged, so everything from the LDS stage on is shared.
+template <int D, int RB, int MODE, bool KV8 = false>
 __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
 attn_kernel(const AttnArgs a) {
   constexpr int KS = D / 32;        // k-steps of the Q K^T contraction
@@ -134,6 +136,9 @@ attn_kernel(const AttnArgs a) {
   constexpr int NI = D / 16;        // 16-byte loads per lane for one 32-key tile of K (or V)
   constexpr int CPR = D / 8;        // 16-byte chunks per key row
   constexpr int TPI = 64 / CPR;     // key rows covered by one row-shaped load
+  // Bytes per pool element, and one chunk of 8 channels as loaded.
+  constexpr int EB = KV8 ? 1 : 2;
+  typedef typename KvChunk<KV8>::T Raw;
   // LDS row stride (bf16) of staged K and V tiles.  D + 16 puts consecutive
   // rows 8 banks apart: the A-fragment reads (16 B of 8 consecutive keys per
   // pass) and the transposed V reads (8 B of 4 consecutive keys x 4 column
@@ -319,8 +324,10 @@ attn_kernel(const AttnArgs a) {
   int lane_off[NV];
 #pragma unroll
   for (int i = 0; i < NV; ++i)
-    lane_off[i] = (int)(((int64_t)(i * TPI + lane / CPR) * kv.token_stride + head_off + (lane % CPR) * 8) * 2);
-  auto load_rows = [&](const int (&pg)[2], int base, int end, u32x4 (&kr)[NI], u32x4 (&vr)[NI]) {
+    lane_off[i] = (int)(((int64_t)(i * TPI + lane / CPR) * kv.token_stride + head_off + (lane % CPR) * 8) * EB);
+  const unsigned char* const k_bytes = reinterpret_cast<const unsigned char*>(kv.k);
+  const unsigned char* const v_bytes = reinterpret_cast<const unsigned char*>(kv.v);
+  auto load_rows = [&](const int (&pg)[2], int base, int end, Raw (&kr)[NI], Raw (&vr)[NI]) {
     __amdgpu_buffer_rsrc_t rk[2], rv[2];
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
@@ -328,15 +335,15 @@ attn_kernel(const AttnArgs a) {
       const int nvalid = min(max(end - first, 0), 16);
       const bool ok = pg[kb] >= 0 && nvalid > 0;
       const int64_t hbase = (int64_t)(ok ? pg[kb] : 0) * kv.page_stride + (int64_t)(first & pmask) * kv.token_stride;
-      const int bytes = ok ? (int)(((int64_t)(nvalid - 1) * kv.token_stride + head_off + D) * 2) : 0;
-      rk[kb] = page_rsrc(kv.k + hbase, bytes);
-      rv[kb] = page_rsrc(kv.v + hbase, bytes);
+      const int bytes = ok ? (int)(((int64_t)(nvalid - 1) * kv.token_stride + head_off + D) * EB) : 0;
+      rk[kb] = page_rsrc(k_bytes + hbase * EB, bytes);
+      rv[kb] = page_rsrc(v_bytes + hbase * EB, bytes);
     }
 #pragma unroll
     for (int n = 0; n < NI; ++n) {
       const int kb = (n * TPI) / 16;
-      kr[n] = buf_load16(rk[kb], lane_off[n % NV]);
-      vr[n] = buf_load16(rv[kb], lane_off[n % NV]);
+      kr[n] = buf_load_chunk(rk[kb], lane_off[n % NV], (Raw*)nullptr);
+      vr[n] = buf_load_chunk(rv[kb], lane_off[n % NV], (Raw*)nullptr);
     }
   };
   auto page_id = [&](int id) {  // -1 (and the error flag) for ids outside the pool
@@ -413,7 +420,7 @@ attn_kernel(const AttnArgs a) {
   }
 
   // The first prefix tile goes out after Q, which the first scores need.
-  u32x4 kr[NI], vr[NI];
+  Raw kr[NI], vr[NI];
   int pg[2] = {-1, -1};
   if constexpr (kMainLoop) {
     if (w < npt) {
@@ -538,7 +545,7 @@ attn_kernel(const AttnArgs a) {
   // Lanes without a key load nothing (all such lanes of all workgroups would
   // otherwise hit one row) and hold zeros; their K is masked later and their
   // V is zero (bit kb of `ok` also zeroes it when staged).
-  auto load_draft_at = [&](const int64_t (&off)[2], u32x4 (&kr)[NI], u32x4 (&vr)[NI], int& ok) {
+  auto load_draft_at = [&](const int64_t (&off)[2], Raw (&kr)[NI], Raw (&vr)[NI], int& ok) {
     ok = 0;
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
@@ -548,29 +555,29 @@ attn_kernel(const AttnArgs a) {
         const int64_t o2 = off[kb] + g4 * 8;
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks) {
-          kr[kb * KS + ks] = *reinterpret_cast<const u32x4*>(kv.k + o2 + ks * 32);
-          vr[kb * KS + ks] = *reinterpret_cast<const u32x4*>(kv.v + o2 + ks * 32);
+          kr[kb * KS + ks] = *reinterpret_cast<const Raw*>(k_bytes + (o2 + ks * 32) * EB);
+          vr[kb * KS + ks] = *reinterpret_cast<const Raw*>(v_bytes + (o2 + ks * 32) * EB);
         }
       } else {
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks) {
-          kr[kb * KS + ks] = u32x4{0u, 0u, 0u, 0u};
-          vr[kb * KS + ks] = u32x4{0u, 0u, 0u, 0u};
+          kr[kb * KS + ks] = Raw{};
+          vr[kb * KS + ks] = Raw{};
         }
       }
     }
   };
-  auto load_draft = [&](int base, int end, u32x4 (&kr)[NI], u32x4 (&vr)[NI], int& ok) {
+  auto load_draft = [&](int base, int end, Raw (&kr)[NI], Raw (&vr)[NI], int& ok) {
     int64_t off[2];
     draft_offsets(base, end, off);
     load_draft_at(off, kr, vr, ok);
   };
   // Writes a tile's K and V rows into the wave's stage (row = key, RS stride).
-  auto stage = [&](const u32x4 (&kr)[NI], const u32x4 (&vr)[NI], bool rows, int ok, uint16_t* st) {
+  auto stage = [&](const Raw (&kr)[NI], const Raw (&vr)[NI], bool rows, int ok, uint16_t* st) {
 #pragma unroll
     for (int r = 0; r < NI; ++r) {
       int key, ch;
-      u32x4 v = vr[r];
+      u32x4 v = widen_bf16(vr[r]);
       if (rows) {
         key = r * TPI + lane / CPR;
         ch = lane % CPR;
@@ -579,7 +586,7 @@ attn_kernel(const AttnArgs a) {
         ch = (r % KS) * 4 + g4;
         if (!((ok >> (r / KS)) & 1)) v = u32x4{0u, 0u, 0u, 0u};
       }
-      *reinterpret_cast<u32x4*>(st + key * RS + ch * 8) = kr[r];
+      *reinterpret_cast<u32x4*>(st + key * RS + ch * 8) = widen_bf16(kr[r]);
       *reinterpret_cast<u32x4*>(st + 32 * RS + key * RS + ch * 8) = v;
     }
   };
@@ -875,7 +882,8 @@ attn_kernel(const AttnArgs a) {
 #pragma unroll
       for (int w2 = 0; w2 < 4; ++w2)
         tot += ml[(w2 * ROWS + r) * 2 + 1] * fast_exp2(ml[(w2 * ROWS + r) * 2] - ms);
-      const float f = tot > 0.f ? fast_exp2(m[rb] - ms) / tot : 0.f;
+      // FP8 pools: the V scale multiplies every normalised output once, here.
+      const float f = tot > 0.f ? fast_exp2(m[rb] - ms) / tot * (KV8 ? a.v_scale : 1.f) : 0.f;
       lse2[rb] = tot > 0.f ? M + fast_log2(tot) : kNegInf;
 #pragma unroll
       for (int db = 0; db < DB; ++db) o[rb][db] *= f;

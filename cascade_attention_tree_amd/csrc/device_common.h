@@ -112,11 +112,42 @@ __device__ __forceinline__ int64_t draft_offset(const KvView& kv, const int32_t*
 // `bytes` reads zeros, so a partially valid tile needs neither branches nor
 // selects.
 constexpr int kBufFlags = 0x00020000;
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t page_rsrc(const uint16_t* base, int bytes) {
-  return __builtin_amdgcn_make_buffer_rsrc((void*)base, 0, bytes, kBufFlags);
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t page_rsrc(const void* base, int bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, bytes, kBufFlags);
 }
 __device__ __forceinline__ u32x4 buf_load16(__amdgpu_buffer_rsrc_t r, int byte_off) {
   return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, byte_off, 0, 0));
+}
+__device__ __forceinline__ u32x2 buf_load8(__amdgpu_buffer_rsrc_t r, int byte_off) {
+  return __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(r, byte_off, 0, 0));
+}
+
+// Eight consecutive K or V channels as they sit in the pool: eight bf16
+// values (16 bytes), or eight FP8 E4M3 codes (8 bytes; KV-cache page,
+// section 4.5 -- FP8 KV with a per-tensor scale).
+template <bool KV8> struct KvChunk { typedef u32x4 T; };
+template <> struct KvChunk<true> { typedef u32x2 T; };
+
+__device__ __forceinline__ u32x4 buf_load_chunk(__amdgpu_buffer_rsrc_t r, int byte_off, u32x4*) {
+  return buf_load16(r, byte_off);
+}
+__device__ __forceinline__ u32x2 buf_load_chunk(__amdgpu_buffer_rsrc_t r, int byte_off, u32x2*) {
+  return buf_load8(r, byte_off);
+}
+
+// The eight channels as bf16.  E4M3 (1 sign, 4 exponent bits with bias 7,
+// 3 mantissa bits; no infinities) embeds exactly in bf16, so the widening
+// conversion (scale 1) rounds nothing; the per-tensor scales are applied in
+// fp32 outside (the K scale with the softmax scale, the V scale on the
+// normalised output).  Byte b of the chunk becomes element b.
+__device__ __forceinline__ u32x4 widen_bf16(u32x4 x) { return x; }
+__device__ __forceinline__ u32x4 widen_bf16(u32x2 x) {
+  u32x4 r;
+  r[0] = __builtin_bit_cast(unsigned, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(x[0], 1.0f, false));
+  r[1] = __builtin_bit_cast(unsigned, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(x[0], 1.0f, true));
+  r[2] = __builtin_bit_cast(unsigned, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(x[1], 1.0f, false));
+  r[3] = __builtin_bit_cast(unsigned, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(x[1], 1.0f, true));
+  return r;
 }
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }

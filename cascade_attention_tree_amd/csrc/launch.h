@@ -14,6 +14,11 @@ hipError_t launch_attn_d64(int mode, int rb, const AttnArgs& a, int grid, hipStr
                            hipEvent_t ev_start, hipEvent_t ev_stop);
 hipError_t launch_attn_d128(int mode, int rb, const AttnArgs& a, int grid, hipStream_t s,
                             hipEvent_t ev_start, hipEvent_t ev_stop);
+// The same over FP8 E4M3 pools (modes that read keys only).
+hipError_t launch_attn_d64_fp8(int mode, int rb, const AttnArgs& a, int grid, hipStream_t s,
+                               hipEvent_t ev_start, hipEvent_t ev_stop);
+hipError_t launch_attn_d128_fp8(int mode, int rb, const AttnArgs& a, int grid, hipStream_t s,
+                                hipEvent_t ev_start, hipEvent_t ev_stop);
 
 hipError_t launch_merge(const MergeArgs& a, hipStream_t s);
 hipError_t launch_append_kv(const AppendArgs& a, hipStream_t s);
@@ -25,6 +30,8 @@ hipError_t launch_debug_mask(const DebugArgs& a, hipStream_t s);
 // Sticky device error words of each translation unit (read, optionally clear).
 hipError_t read_error_d64(int* v, int clear);
 hipError_t read_error_d128(int* v, int clear);
+hipError_t read_error_d64_fp8(int* v, int clear);
+hipError_t read_error_d128_fp8(int* v, int clear);
 hipError_t read_error_small(int* v, int clear);
 
 }  // namespace casc

@@ -43,7 +43,8 @@ __global__ void __launch_bounds__(256) merge_state_kernel(const MergeArgs a) {
 // Copies `count` tokens of one kv head through the same address helpers the
 // attention kernels use: which == 0, the prefix of request `index`
 // (paged_offset on its block-table row); which == 1, the drafts of branch
-// `index` (draft_offset).  One thread per 8 channels of one token.
+// `index` (draft_offset).  FP8 codes are widened to bf16 by the conversion
+// the attention kernels stage with.  One thread per 8 channels of one token.
 __global__ void __launch_bounds__(256) debug_gather_kernel(const DebugArgs a) {
   const int c8 = a.head_dim >> 3;
   const int idx = blockIdx.x * blockDim.x + threadIdx.x;
@@ -60,7 +61,10 @@ __global__ void __launch_bounds__(256) debug_gather_kernel(const DebugArgs a) {
                        a.draft_start, a.index, a.index + 1, t, a.kv_head);
   }
   u32x4 k = {0u, 0u, 0u, 0u}, v = {0u, 0u, 0u, 0u};
-  if (off >= 0) {
+  if (off >= 0 && a.kv.elem_bytes == 1) {
+    k = widen_bf16(*reinterpret_cast<const u32x2*>(reinterpret_cast<const unsigned char*>(a.kv.k) + off + c));
+    v = widen_bf16(*reinterpret_cast<const u32x2*>(reinterpret_cast<const unsigned char*>(a.kv.v) + off + c));
+  } else if (off >= 0) {
     k = *reinterpret_cast<const u32x4*>(a.kv.k + off + c);
     v = *reinterpret_cast<const u32x4*>(a.kv.v + off + c);
   } else {
@@ -98,9 +102,27 @@ __global__ void __launch_bounds__(256) debug_mask_kernel(const DebugArgs a) {
   a.mask_out[idx] = vis;
 }
 
+// Copies one token's head_dim elements (element offsets, elem_bytes each)
+// with the 16 lanes of a group: 16-byte steps for bf16, 8-byte steps for FP8
+// codes (whose rows are only 8-byte aligned).
+__device__ __forceinline__ void copy_row(void* dst, const void* src, int64_t dst_off, int64_t src_off,
+                                         int head_dim, int elem_bytes, int lane) {
+  unsigned char* d = static_cast<unsigned char*>(dst) + dst_off * elem_bytes;
+  const unsigned char* q = static_cast<const unsigned char*>(src) + src_off * elem_bytes;
+  const int bytes = head_dim * elem_bytes;
+  if (elem_bytes == 2) {
+    for (int b = lane * 16; b < bytes; b += 256)
+      *reinterpret_cast<u32x4*>(d + b) = *reinterpret_cast<const u32x4*>(q + b);
+  } else {
+    for (int b = lane * 8; b < bytes; b += 128)
+      *reinterpret_cast<u32x2*>(d + b) = *reinterpret_cast<const u32x2*>(q + b);
+  }
+}
+
 // Draft-KV append: query row r, position u of branch j, has its K and V
 // written at logical slot draft_start[j] + u of draft block-table row j.  One
-// group of 16 lanes per (row, kv head), 16 bytes per lane and step.
+// group of 16 lanes per (row, kv head).  The new rows are in the pool's
+// element type (FP8 pools take E4M3 codes, quantised by the caller).
 __global__ void __launch_bounds__(256) append_kv_kernel(const AppendArgs a) {
   const int64_t item = ((int64_t)blockIdx.x * blockDim.x + threadIdx.x) >> 4;
   const int lane = threadIdx.x & 15;
@@ -117,13 +139,9 @@ __global__ void __launch_bounds__(256) append_kv_kernel(const AppendArgs a) {
     if (lane == 0) atomicOr(&g_device_error, kErrPage);
     return;
   }
-  uint16_t* dk = const_cast<uint16_t*>(a.kv.k) + off;
-  uint16_t* dv = const_cast<uint16_t*>(a.kv.v) + off;
   const int64_t src = (int64_t)r * a.new_row_stride + (int64_t)g * a.new_head_stride;
-  for (int c = lane * 8; c < a.head_dim; c += 128) {
-    *reinterpret_cast<u32x4*>(dk + c) = *reinterpret_cast<const u32x4*>(a.k_new + src + c);
-    *reinterpret_cast<u32x4*>(dv + c) = *reinterpret_cast<const u32x4*>(a.v_new + src + c);
-  }
+  copy_row(const_cast<uint16_t*>(a.kv.k), a.k_new, off, src, a.head_dim, a.kv.elem_bytes, lane);
+  copy_row(const_cast<uint16_t*>(a.kv.v), a.v_new, off, src, a.head_dim, a.kv.elem_bytes, lane);
 }
 
 // Commit: the k-th accepted row of request i has its draft K/V copied to
@@ -155,12 +173,8 @@ __global__ void __launch_bounds__(256) commit_kernel(const CommitArgs a) {
     if (lane == 0) atomicOr(&g_device_error, r >= 0 && r < a.total_rows ? kErrPage : kErrRow);
     return;
   }
-  uint16_t* k_pool = const_cast<uint16_t*>(a.kv.k);
-  uint16_t* v_pool = const_cast<uint16_t*>(a.kv.v);
-  for (int c = lane * 8; c < a.head_dim; c += 128) {
-    *reinterpret_cast<u32x4*>(k_pool + dst + c) = *reinterpret_cast<const u32x4*>(k_pool + src + c);
-    *reinterpret_cast<u32x4*>(v_pool + dst + c) = *reinterpret_cast<const u32x4*>(v_pool + src + c);
-  }
+  copy_row(const_cast<uint16_t*>(a.kv.k), a.kv.k, dst, src, a.head_dim, a.kv.elem_bytes, lane);
+  copy_row(const_cast<uint16_t*>(a.kv.v), a.kv.v, dst, src, a.head_dim, a.kv.elem_bytes, lane);
 }
 
 // Lengths after the commit (a launch of its own, after every copy has read

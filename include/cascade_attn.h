@@ -65,11 +65,20 @@ typedef enum {
 
 typedef enum { CASCADE_F32 = 0, CASCADE_BF16 = 1 } cascade_dtype;
 
-/* One layer's paged K and V (bf16).  Element (page, slot, kv_head, c) of K is at
- * k + page*page_stride + slot*token_stride + kv_head*head_stride + c.
+/* Element type of the K/V pools.  FP8 KV (KV-cache tutorial page, section
+ * 4.5: FP8 KV cache with a per-tensor scale): each element is an OCP FP8
+ * E4M3 code (1 sign bit, 4 exponent bits with bias 7, 3 mantissa bits; no
+ * infinities; 0x7F and 0xFF are NaN; largest finite 448), and stands for
+ * code_value * k_scale in K, code_value * v_scale in V. */
+typedef enum { CASCADE_KV_BF16 = 0, CASCADE_KV_FP8_E4M3 = 1 } cascade_kv_dtype;
+
+/* One layer's paged K and V.  Element (page, slot, kv_head, c) of K is at
+ * element offset page*page_stride + slot*token_stride + kv_head*head_stride + c
+ * from k (elements of 2 bytes for bf16, 1 byte for FP8).
  * Requirements: head_dim in {64, 128}; page_size a power of two in [16, 4096];
  * the three strides are multiples of 8 elements, token_stride >= head_dim;
- * k and v 16-byte aligned.
+ * k and v 16-byte aligned.  dtype is a cascade_kv_dtype (0 = bf16); for FP8,
+ * k_scale and v_scale must be finite and > 0 (they are ignored for bf16).
  * The default layout [num_pages, page_size, Hkv, head_dim] has
  * page_stride = page_size*Hkv*head_dim, token_stride = Hkv*head_dim,
  * head_stride = head_dim. */
@@ -83,6 +92,9 @@ typedef struct {
   int64_t page_stride;
   int64_t token_stride;
   int64_t head_stride;
+  int32_t dtype;
+  float k_scale;
+  float v_scale;
 } cascade_paged_kv;
 
 /* Queries, bf16 [total_rows, Hq, head_dim]; element (row, h, c) at
@@ -195,7 +207,9 @@ CASCADE_API const char *cascade_last_error(void);
 /* Test hooks, built on the same index helpers the attention kernels use.
  * cascade_debug_gather: which = 0 copies request `index`'s L_i prefix tokens,
  * which = 1 branch `index`'s S_j draft tokens, of kv head `kv_head`, into k_out
- * and v_out (bf16 [count, head_dim], device, sized by the caller).
+ * and v_out (bf16 [count, head_dim], device, sized by the caller).  FP8 codes
+ * come out widened to bf16 (exact; scales not applied) by the conversion the
+ * attention kernels use.
  * cascade_debug_mask: branch `branch`'s visibility over [its request's prefix ;
  * its drafts] as uint8 [S_j, L_i + S_j] (1 = visible), device, sized by the caller. */
 CASCADE_API cascade_status cascade_debug_gather(const cascade_paged_kv *kv, const cascade_tree *tree,
@@ -213,9 +227,11 @@ CASCADE_API cascade_status cascade_device_error(int32_t *flag_out, int32_t clear
  * cascade_append_draft_kv writes the K and V of every query row's draft token
  * into its page before the verify pass reads them: row r, position u of branch
  * j, goes to logical slot draft_start[j] + u of draft block-table row j.
- * k_new, v_new: bf16 [total_rows, num_kv_heads, head_dim], element (r, g, c) at
- * k_new + r*new_row_stride + g*new_head_stride + c (strides multiples of 8
- * elements, 16-byte aligned, device); total_rows must be branch_qo_indptr[
+ * k_new, v_new: [total_rows, num_kv_heads, head_dim] in the pool's element
+ * type (bf16, or FP8 E4M3 codes that the caller quantised with the pool's
+ * scales), element (r, g, c) at element offset r*new_row_stride +
+ * g*new_head_stride + c (strides multiples of 8 elements, 16-byte aligned,
+ * device); total_rows must be branch_qo_indptr[
  * num_branches].  Rows whose slot has no valid page are skipped and raise the
  * sticky device flag.  Asynchronous on stream; the pool is written in place.
  *

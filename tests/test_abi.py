@@ -163,3 +163,22 @@ def test_stream_read_checks():
     sink = (ctypes.c_uint32 * 4)()
     assert lib.cascade_stream_read(aligned + 4, 64, ctypes.addressof(sink), None) == B.CASCADE_ERR_UNSUPPORTED
     assert lib.cascade_stream_read(aligned, 60, ctypes.addressof(sink), None) == B.CASCADE_ERR_UNSUPPORTED
+
+
+def test_fp8_kv_checks():
+    """FP8 pools: the element type must be known and both scales finite and
+    positive; bf16 pools ignore the scales (zero is fine there)."""
+    q, kv, t = make()
+    kv.dtype = 7
+    assert call_verify(q, kv, t) == B.CASCADE_ERR_UNSUPPORTED
+    assert b"dtype" in B.lib().cascade_last_error()
+    for ks, vs in ((0.0, 1.0), (1.0, -2.0), (float("inf"), 1.0), (1.0, float("nan"))):
+        q, kv, t = make()
+        kv.dtype, kv.k_scale, kv.v_scale = B.KV_FP8_E4M3, ks, vs
+        assert call_verify(q, kv, t) == B.CASCADE_ERR_SHAPE
+        assert b"k_scale" in B.lib().cascade_last_error()
+    q, kv, t = make()
+    assert kv.dtype == B.KV_BF16 and kv.k_scale == 0.0
+    kv.head_dim = 96   # a later check still runs: the scales were not the problem
+    assert call_verify(q, kv, t) == B.CASCADE_ERR_UNSUPPORTED
+    assert b"head_dim" in B.lib().cascade_last_error()
