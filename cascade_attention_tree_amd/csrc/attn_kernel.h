@@ -671,8 +671,8 @@ attn_kernel(const AttnArgs a) {
   // A row's max only moves when the max over its 32 keys exceeds m + slack;
   // each lane checks its own 8 keys first, and only when some lane of the
   // wave finds such a key are the row maxima formed across lanes.
-  auto softmax = [&](f32x4 (&s)[RB][2], float (&m)[RB], float (&l)[RB], float (&alpha)[RB],
-                     bf16x8 (&pf)[RB]) -> bool {
+  // First half: the carried max and alpha.
+  auto softmax_max = [&](const f32x4 (&s)[RB][2], float (&m)[RB], float (&alpha)[RB]) -> bool {
     float lm[RB];
     bool raise = false;
 #pragma unroll
@@ -697,6 +697,12 @@ attn_kernel(const AttnArgs a) {
 #pragma unroll
       for (int rb = 0; rb < RB; ++rb) alpha[rb] = 1.f;
     }
+    return rescale;
+  };
+  // Second half: the weights as P^T fragments and the row sums (straight-line
+  // VALU code, so that matrix instructions can be interleaved with it).
+  auto softmax_exp = [&](const f32x4 (&s)[RB][2], const float (&m)[RB], float (&l)[RB],
+                         const float (&alpha)[RB], bf16x8 (&pf)[RB]) {
 #pragma unroll
     for (int rb = 0; rb < RB; ++rb) {
       const float ms = m[rb] == kNegInf ? 0.f : m[rb];
@@ -715,6 +721,11 @@ attn_kernel(const AttnArgs a) {
                         pack_bf16x2(p[6], p[7])};
       pf[rb] = __builtin_bit_cast(bf16x8, pk);
     }
+  };
+  auto softmax = [&](const f32x4 (&s)[RB][2], float (&m)[RB], float (&l)[RB], float (&alpha)[RB],
+                     bf16x8 (&pf)[RB]) -> bool {
+    const bool rescale = softmax_max(s, m, alpha);
+    softmax_exp(s, m, l, alpha, pf);
     return rescale;
   };
 
@@ -788,11 +799,37 @@ attn_kernel(const AttnArgs a) {
     // place of the prefetch past its last prefix tile.
     const bool verify_drafts = MODE == kModeVerify && split == 0 && dlo < dhi && w == kDraftWave;
     if (verify_drafts && w >= nt) load_draft(dlo, dhi, kr, vr, ok);
+    // Each tile's P·V is issued one iteration late, in one block with the
+    // next tile's softmax exponentials, so that the matrix pipe works through
+    // it while the VALU computes the weights (one wave per SIMD has no other
+    // wave to overlap with).  The deferred tile keeps its P^T fragments, its
+    // V^T fragments (read out of the stage before the stage is overwritten)
+    // and the rescale the following softmax asks for; the rescale is applied
+    // before that tile's P·V, since its P is relative to the raised max.
+    // Before the first tile the deferred operands are zeros: an exact no-op.
+    bf16x8 pv_p[RB], pv_v[DB];
+    float pv_alpha[RB];
+    bool pv_rescale = false;
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb) pv_p[rb] = bf16x8{};
+    auto rescale_o = [&](const float (&alpha)[RB]) {
+#pragma unroll
+      for (int rb = 0; rb < RB; ++rb)
+#pragma unroll
+        for (int db = 0; db < DB; ++db) o[rb][db] *= alpha[rb];
+    };
     for (int tau = w; tau < nt; tau += 4) {
       const int nxt = tau + 4;
       const bool is_prefix = tau < npt;
       const int base = is_prefix ? p0 + tau * 32 : d0 + (tau - npt) * 32;
       const int end = is_prefix ? p1 : d1;
+      // V of the deferred tile leaves the stage (zeros before the first tile).
+      const bool first = tau == w;
+#pragma unroll
+      for (int db = 0; db < DB; ++db) {
+        const bf16x8 vf = vt_frag(st, db);
+        pv_v[db] = first ? bf16x8{} : vf;
+      }
       // Stage this tile, then reuse its registers for the next tile's loads,
       // which then have a whole iteration to land.
       stage(kr, vr, is_prefix, ok, st);
@@ -808,6 +845,7 @@ attn_kernel(const AttnArgs a) {
         if (nxt < nt) issue(nxt);
         if (nxt + 4 < nt) pages_of(nxt + 4, pg);
       }
+      if (pv_rescale) rescale_o(pv_alpha);
       f32x4 s[RB][2];
       scores(st, s);
       if (!is_prefix) {
@@ -816,21 +854,38 @@ attn_kernel(const AttnArgs a) {
         mask_prefix(base, end, s);
       }
       float alpha[RB];
+      const bool resc = __any(softmax_max(s, m, alpha));
       bf16x8 pf[RB];
-      if (__any(softmax(s, m, l, alpha, pf))) {
+      softmax_exp(s, m, l, alpha, pf);
 #pragma unroll
-        for (int rb = 0; rb < RB; ++rb)
+      for (int db = 0; db < DB; ++db)
 #pragma unroll
-          for (int db = 0; db < DB; ++db) o[rb][db] *= alpha[rb];
+        for (int rb = 0; rb < RB; ++rb) o[rb][db] = mfma16(pv_v[db], pv_p[rb], o[rb][db]);
+      // Interleave: one matrix instruction, then a few VALU instructions.
+#pragma unroll
+      for (int i = 0; i < RB * DB; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x002, 3, 0);
       }
+#pragma unroll
+      for (int rb = 0; rb < RB; ++rb) {
+        pv_p[rb] = pf[rb];
+        pv_alpha[rb] = alpha[rb];
+      }
+      pv_rescale = resc;
+    }
+    // The last tile's P·V (its V is still in the stage).
+    if (w < nt) {
+      mfma_drain();
+      if (pv_rescale) rescale_o(pv_alpha);
 #pragma unroll
       for (int db = 0; db < DB; ++db) {
         const bf16x8 vf = vt_frag(st, db);
 #pragma unroll
-        for (int rb = 0; rb < RB; ++rb) o[rb][db] = mfma16(vf, pf[rb], o[rb][db]);
+        for (int rb = 0; rb < RB; ++rb) o[rb][db] = mfma16(vf, pv_p[rb], o[rb][db]);
       }
+      mfma_drain();
     }
-
     if (verify_drafts) {
       // Pass B of the chunk's rows into this wave's state: its visible draft
       // tiles (usually one), under the in-branch ancestor mask.
