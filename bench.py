@@ -371,7 +371,7 @@ def main():
                     help="for profiling: only the FP8 headline verify (cold steps)")
     ap.add_argument("--traffic-probe", action="store_true",
                     help="for hardware-counter runs: one plain 256 MiB device copy (known bytes), "
-                         "then a few flushed verify steps; prints nothing else")
+                         "then a few flushed verify steps and naive-expand steps; prints nothing else")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}); "
@@ -435,6 +435,9 @@ def main():
         for _ in range(3):
             flush()
             verify()
+        for _ in range(3):
+            flush()
+            naive()
         torch.cuda.synchronize()
         print(json.dumps({"traffic_probe": True, "copy_bytes": src.numel() * 4,
                           "kernel_hash": kernel_source_hash()}), flush=True)
