@@ -232,6 +232,14 @@ attn_kernel(const AttnArgs a) {
       if (stride > 0) pt_first[kb] = pt_row[idx < stride ? idx : stride - 1];  // clamped: used only if in range
     }
   }
+  // A key split that starts at or past the request's length has no keys
+  // (split 0 always runs: it holds the drafts of the fused launch and the
+  // row checks).  Such a workgroup leaves after the first round of small
+  // loads instead of the second: launches planned from the longest request
+  // hold many of them when lengths vary.
+  if constexpr (MODE == kModePrefix || MODE == kModeVerify) {
+    if (split != 0 && (int64_t)split * a.split_len >= L_in) return;
+  }
   const int tok0 = cqo[jb];
   const int tok1 = cqo[je];
   // Keeps the length load in the same round trip as the branch-range loads

@@ -5,6 +5,7 @@ max |LSE - LSE_ref| <= 1e-3 where LSE_ref is finite; LSE_ref = -inf must be
 -inf exactly.  Gather and mask hooks are compared bit for bit.
 """
 
+import dataclasses
 import math
 import sys
 
@@ -214,6 +215,31 @@ def test_prefix_hit_small_all_rows(B, h):
     torch.cuda.synchronize()
     cmp(o, l, ro, rl)
     cmp(o3, l3, ro, rl)
+
+
+@pytest.mark.parametrize("h", [0.5, 0.9])
+def test_draft_pass_ignores_slots_in_front_of_the_branch(B, h):
+    """Pass B of a prefix hit reads the suffix like a prefix, from tiles that
+    start at a multiple of 32 slots; with H not such a multiple, its first tile
+    also covers up to 31 prefix slots in front of the suffix.  Those slots are
+    set to NaN here: pass B must not let them into its result."""
+    wl = W.prefix_hit(h, batch=2, n_tokens=300, seed=43)
+    P = wl.page_size
+    k, v = wl.k_pool.copy(), wl.v_pool.copy()
+    for j in range(wl.num_branches):
+        hs = int(wl.draft_start[j])
+        assert hs % 32 != 0
+        for t in range(hs - hs % 32, hs):
+            pg = wl.draft_page_table[j][t // P]
+            k[pg, t % P] = np.nan
+            v[pg, t % P] = np.nan
+    wl = dataclasses.replace(wl, k_pool=k, v_pool=v)
+    note(f"draft_attn prefix-hit h={h}, NaN in front of the suffix")
+    x = B.to_device(wl)
+    o, l = B.cascade_draft_attn(x)
+    torch.cuda.synchronize()
+    ro, rl = O.draft_pass(wl)
+    cmp(o, l, ro, rl)
 
 
 @pytest.mark.parametrize("h", [0.0, 0.5, 0.9])
