@@ -22,6 +22,10 @@ struct KvView {
                        // count elements, so they are byte offsets for FP8)
 };
 
+// Query rows per work item of the row-split kernel (pass A and the fused
+// verify pass at head_dim 128): 8 waves of at most 16 rows.
+constexpr int kRowsPerItem = 128;
+
 enum AttnMode : int {
   kModePrefix = 0,        // pass A: unsplit -> (o_A, LSE_A); split -> partial states
   kModeDraft = 1,         // pass B -> (o_B, LSE_B)

@@ -7,6 +7,7 @@
 
 #include "attn_kernel.h"
 #include "launch.h"
+#include "rows_kernel.h"
 
 namespace casc {
 
@@ -39,6 +40,21 @@ static hipError_t launch_rb(int mode, const AttnArgs& a, int grid, hipStream_t s
       if constexpr (KV8) return hipErrorInvalidValue;
       else go(attn_kernel<D, RB, kModeVerifyFinish>, g, b, s, e0, e1, a);
       break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+// Row-split kernel (head_dim 128, pass A and the fused verify pass): tiles
+// requested this many steps ahead.
+constexpr int kRowDepth = 4;
+
+static inline hipError_t launch_rows(int mode, const AttnArgs& a, int grid, hipStream_t s, hipEvent_t e0,
+                                     hipEvent_t e1) {
+  const dim3 g(grid), b(512);
+  switch (mode) {
+    case kModePrefix: go(rows_kernel<kModePrefix, kRowDepth>, g, b, s, e0, e1, a); break;
+    case kModeVerify: go(rows_kernel<kModeVerify, kRowDepth>, g, b, s, e0, e1, a); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();

@@ -1,0 +1,428 @@
+// Row-split attention kernel for the prefix-only launches (pass A and the
+// fused verify pass), head_dim 128, bf16 pools.
+//
+// One workgroup of 8 waves (two per SIMD) handles one work item
+//   (request, kv head g, chunk of at most 128 query rows, key split).
+// The chunk's rows -- the request's query tokens times the query heads that
+// share kv head g -- are dealt out to the 8 waves, at most 16 per wave (one
+// MFMA row block), so every wave keeps its own rows' complete online softmax
+// state and no state is merged across waves.  All 8 waves go through the
+// same 32-key tiles in lock step:
+//   * each thread loads one 16-byte chunk of K and one of V per tile (the
+//     workgroup's 512 threads cover the 32 keys x 16 chunks of a tile; the 64
+//     lanes of a wave read four whole 256-byte key rows of one page), DEPTH
+//     tiles ahead, into a ring of DEPTH register slots -- a handful of
+//     registers per tile, so many tiles are in flight;
+//   * per step the workgroup writes the next tile into one of two LDS
+//     stages, computes the current tile out of the other, and meets at one
+//     barrier;
+//   * a wave reads K back as MFMA A-fragments (S^T = K Q^T with
+//     v_mfma_f32_16x16x32_bf16, its rows' Q as B-fragments in registers),
+//     updates its rows' base-2 online softmax, and reads V back transposed
+//     (ds_read_b64_tr_b16) for O^T += V^T P^T; P^T stays in the lanes that
+//     computed S^T.
+// In the fused verify launch the request's draft tiles (pass B, under the
+// in-branch ancestor mask) follow the prefix tiles as further steps of the
+// same online softmax, so passes A and B meet in one state: the merge of the
+// two passes is the online softmax itself (cascade page, splittability: the
+// same LSE identity).
+#pragma once
+
+#include "attn_kernel.h"
+
+namespace casc {
+
+constexpr int kRowWaves = 8;
+static_assert(kRowsPerItem == 16 * kRowWaves, "one 16-row block per wave");
+
+template <int MODE, int DEPTH>
+__global__ void __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2)))
+rows_kernel(const AttnArgs a) {
+  static_assert(MODE == kModePrefix || MODE == kModeVerify, "prefix-only launches");
+  static_assert(DEPTH % 2 == 0, "the two LDS stages alternate within the unrolled ring");
+  constexpr int D = 128;
+  constexpr int KS = D / 32;   // k-steps of the Q K^T contraction
+  constexpr int DB = D / 16;   // 16-channel blocks of the head dim
+  constexpr int CPR = D / 8;   // 8-channel chunks per key row (16)
+  constexpr int RS = D + 16;   // LDS row stride: rows 8 banks apart
+  constexpr int STAGE = 2 * 32 * RS;  // bf16 elements of one stage: K tile, then V tile
+  constexpr int EB = 2;  // bf16 pools
+  typedef u32x4 Raw;
+  constexpr bool kVerify = MODE == kModeVerify;
+  constexpr int NBCAP = 128;   // branches of a request resolved in LDS
+  constexpr int KEYCAP = 512;  // draft keys of a chunk resolved in LDS
+
+  __shared__ __attribute__((aligned(16))) uint16_t stg[2][STAGE];
+  __shared__ int64_t t_doff[kVerify ? KEYCAP : 1];
+  __shared__ int t_bnd[kVerify ? NBCAP + 1 : 1];
+  __shared__ int t_dst[kVerify ? NBCAP : 1];
+  __shared__ int t_rbs[kVerify ? kRowsPerItem : 1];
+
+  const int tid = (int)threadIdx.x;
+  const int lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int l16 = lane & 15;
+  const int g4 = lane >> 4;
+
+  // ---- work item: key splits slowest, row chunks fastest (as attn_kernel) --
+  int item = blockIdx.x;
+  const int per_split = (int)gridDim.x / a.grid_splits;
+  const int split = item / per_split;
+  item -= split * per_split;
+  const int chunk = item % a.n_chunks;
+  item /= a.n_chunks;
+  const int g = item % a.num_kv_heads;
+  const int req = item / a.num_kv_heads;
+  cint32* crb = as_const(a.req_branch_indptr);
+  cint32* cqo = as_const(a.branch_qo_indptr);
+  const int jb = crb[req];
+  const int je = crb[req + 1];
+  const int L_in = as_const(a.cache_seqlens)[req];
+  cint32* pt_row = as_const(a.page_table + (int64_t)req * a.page_table_stride);
+  // A key split at or past the request's length has no keys (split 0 always
+  // runs: it holds the drafts of the fused launch and the row checks).
+  if (split != 0 && (int64_t)split * a.split_len >= L_in) return;
+  const int tok0 = cqo[jb];
+  const int tok1 = cqo[je];
+  asm volatile("" ::"s"(L_in));
+  if (tok0 < 0 || tok1 < tok0 || tok1 > a.total_rows) {
+    if (tid == 0) atomicOr(&g_device_error, kErrRow);
+    return;
+  }
+  const int nrows = (tok1 - tok0) * a.group;
+  const int row0 = chunk * kRowsPerItem;
+  if (chunk == 0 && split == 0 && tid == 0 && nrows > a.n_chunks * kRowsPerItem)
+    atomicOr(&g_device_error, kErrRow);  // rows past the planned chunks are not computed
+  if (row0 >= nrows) return;
+  const int nrc = min(nrows - row0, kRowsPerItem);  // rows of this chunk
+
+  int L = L_in;
+  {
+    const int cap = a.page_table_stride << a.kv.log2_page;
+    if (L > cap) {
+      if (tid == 0) atomicOr(&g_device_error, kErrLen);
+      L = cap;
+    }
+    if (L < 0) L = 0;
+    const int planned = a.n_splits * a.split_len;
+    if (L > planned) {
+      if (tid == 0) atomicOr(&g_device_error, kErrLen);
+      L = planned;
+    }
+  }
+  // Uniform by construction; stated so that the buffer descriptors built
+  // from them live in scalar registers (the flag stores above are per lane).
+  L = __builtin_amdgcn_readfirstlane(L);
+  const int p0 = split * a.split_len;
+  int p1 = min(L, p0 + a.split_len);
+  if (a.n_splits > 1 && p0 >= L && (MODE == kModePrefix || split != 0)) return;
+  if (p1 < p0) p1 = p0;
+  p1 = __builtin_amdgcn_readfirstlane(p1);
+  const int nt = (p1 - p0 + 31) >> 5;  // prefix tiles of this split
+
+  const KvView kv = a.kv;
+  const float c2 = a.scale_log2;
+  const int pmask = (1 << kv.log2_page) - 1;
+  const int64_t head_off = (int64_t)g * kv.head_stride;
+
+  // ---- this lane's row: wave w holds chunk rows [16w, 16w + 16) ------------
+  // Rows fill whole 16-row blocks from wave 0 on (waves past the last block
+  // only load and stage): spreading them thinner would pad every block and
+  // make more waves read each tile out of LDS.
+  const int rpw = 16;
+  const bool wave_rows = w * rpw < nrc;               // uniform
+  const int rw = w * rpw + l16;
+  const bool rvalid = l16 < rpw && rw < nrc;
+  const int rho = row0 + (rvalid ? rw : 0);  // row within (request, kv head)
+  const int rtok = rho / a.group;            // request token of the row
+  const int hq = g * a.group + (rho - rtok * a.group);
+  const int64_t orow = (int64_t)(tok0 + rtok) * a.num_qo_heads + hq;
+
+  // Q B-fragments: channels ks*32 + g4*8 .. +8 of the lane's row.
+  bf16x8 qf[KS];
+  {
+    const uint16_t* qp = a.q + (int64_t)(tok0 + rtok) * a.q_row_stride + (int64_t)hq * a.q_head_stride + g4 * 8;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks)
+      qf[ks] = rvalid ? *reinterpret_cast<const bf16x8*>(qp + ks * 32) : bf16x8{};
+  }
+
+  // ---- prefix tile loads -------------------------------------------------
+  // Thread tid loads chunk tid % 16 of key tid / 16 of a tile: the wave's four
+  // keys (w % 4)*4 .. +4 lie in the tile's 16-key half w / 4, whose page id is
+  // wave-uniform.  The half's buffer descriptors start at its first key and
+  // end after the row of its last valid key, so keys past `p1` (and bad pages)
+  // read zeros.
+  const int half = w >> 2;
+  const int lane_off = (int)((((int64_t)((w & 3) * 4 + g4) * kv.token_stride) + head_off + l16 * 8) * EB);
+  const unsigned char* const k_bytes = reinterpret_cast<const unsigned char*>(kv.k);
+  const unsigned char* const v_bytes = reinterpret_cast<const unsigned char*>(kv.v);
+  // Page ids outside the pool are noted here and flagged once at the end: a
+  // store in the key loop would count on the same counter as the K/V loads
+  // and blur the loop's wait counts.
+  bool bad_page = false;
+  auto page_of = [&](int tile) -> int {  // page id of this wave's half of a tile, -1 if none
+    const int first = p0 + tile * 32 + half * 16;
+    int id = first < p1 ? pt_row[first >> kv.log2_page] : -1;
+    id = __builtin_amdgcn_readfirstlane(id);
+    bad_page |= id >= kv.num_pages;
+    return (uint32_t)id < (uint32_t)kv.num_pages ? id : -1;
+  };
+  auto load_tile = [&](int tile, int pg, Raw& kr, Raw& vr) {
+    const int first = p0 + tile * 32 + half * 16;
+    const int nvalid = min(max(p1 - first, 0), 16);
+    const bool ok = pg >= 0 && nvalid > 0;
+    const int64_t hbase = (int64_t)(ok ? pg : 0) * kv.page_stride + (int64_t)(first & pmask) * kv.token_stride;
+    const int bytes = ok ? (int)(((int64_t)(nvalid - 1) * kv.token_stride + head_off + D) * EB) : 0;
+    kr = buf_load_chunk(page_rsrc(k_bytes + hbase * EB, bytes), lane_off, (Raw*)nullptr);
+    vr = buf_load_chunk(page_rsrc(v_bytes + hbase * EB, bytes), lane_off, (Raw*)nullptr);
+  };
+  // Thread tid's chunk of a tile into a stage (zeros where `keep` is false).
+  const int skey = tid >> 4, sch = tid & 15;
+  auto stage = [&](const Raw& kr, const Raw& vr, bool keep, uint16_t* st) {
+    u32x4 k = widen_bf16(kr), v = widen_bf16(vr);
+    if (!keep) {
+      k = u32x4{0u, 0u, 0u, 0u};
+      v = u32x4{0u, 0u, 0u, 0u};
+    }
+    *reinterpret_cast<u32x4*>(st + skey * RS + sch * 8) = k;
+    *reinterpret_cast<u32x4*>(st + 32 * RS + skey * RS + sch * 8) = v;
+  };
+
+  // DEPTH tiles requested before the first one is staged; `pgn` holds the
+  // page of the next tile to be requested.
+  Raw kq[DEPTH], vq[DEPTH];
+  int pgn = page_of(0);
+#pragma unroll
+  for (int k = 0; k < DEPTH; ++k) {
+    load_tile(k, pgn, kq[k], vq[k]);
+    pgn = page_of(k + 1);
+  }
+
+  // ---- tree tables (fused verify, split 0): drafts of the chunk's tokens ---
+  const int tok_first = row0 / a.group;
+  const int tok_last = (row0 + nrc - 1) / a.group;
+  const bool drafts = kVerify && split == 0;
+  const int nb = je - jb;
+  const bool lds_bnd = nb <= NBCAP;
+  int dlo = 0;
+  const int dhi = tok_last + 1;
+  Raw dk, dv;  // the first draft tile, requested after the tables
+  bool dkeep = false;
+  auto branch_at = [&](int x) -> int {  // local branch of request token x
+    if (lds_bnd) {
+      int lo = 0, hi = nb - 1;
+      while (lo < hi) {
+        const int mid = (lo + hi + 1) >> 1;
+        if (t_bnd[mid] - tok0 <= x) lo = mid; else hi = mid - 1;
+      }
+      return lo;
+    }
+    return branch_of_row(a.branch_qo_indptr, jb, je, tok0 + x) - jb;
+  };
+  auto branch_start = [&](int jl) { return (lds_bnd ? t_bnd[jl] : a.branch_qo_indptr[jb + jl]) - tok0; };
+  auto branch_dstart = [&](int jl) {
+    return lds_bnd ? t_dst[jl] : (a.draft_start ? a.draft_start[jb + jl] : 0);
+  };
+  // Key base + tid / 16 of a draft tile (request tokens), chunk tid % 16;
+  // zeros for keys past dhi and for bad slots or pages (flagged).
+  auto load_draft = [&](int base, Raw& kr, Raw& vr, bool& keep) {
+    const int x = base + skey;
+    int64_t off = -2;  // element offset of the key's row (kv head included)
+    if (x < dhi) {
+      if (x - dlo < KEYCAP) {
+        off = t_doff[x - dlo];
+        if (off >= 0) off += head_off;
+      } else {
+        off = draft_offset(kv, a.branch_qo_indptr, a.draft_page_table, a.draft_page_table_stride,
+                           a.draft_start, jb, je, x, g);
+      }
+      if (off == -1) atomicOr(&g_device_error, kErrPage);
+    }
+    keep = off >= 0;
+    const int64_t e = (keep ? off : 0) + sch * 8;
+    kr = keep ? *reinterpret_cast<const Raw*>(k_bytes + e * EB) : Raw{};
+    vr = keep ? *reinterpret_cast<const Raw*>(v_bytes + e * EB) : Raw{};
+  };
+  if constexpr (kVerify) {
+    if (drafts) {
+      if (lds_bnd) {
+        for (int t = tid; t <= nb; t += 512) t_bnd[t] = a.branch_qo_indptr[jb + t];
+        for (int t = tid; t < nb; t += 512) t_dst[t] = a.draft_start ? a.draft_start[jb + t] : 0;
+      }
+      __syncthreads();
+      dlo = __builtin_amdgcn_readfirstlane(branch_start(branch_at(tok_first)));
+      for (int t = tid; t <= tok_last - tok_first; t += 512) t_rbs[t] = branch_start(branch_at(tok_first + t));
+      const int nk = min(dhi - dlo, KEYCAP);
+      const int dstride = a.draft_page_table_stride;
+      for (int t = tid; t < nk; t += 512) {
+        const int x = dlo + t;
+        const int jl = branch_at(x);
+        const int slot = branch_dstart(jl) + (x - branch_start(jl));
+        int64_t off = -1;
+        if (slot >= 0 && (slot >> kv.log2_page) < dstride) {
+          const int page = a.draft_page_table[(int64_t)(jb + jl) * dstride + (slot >> kv.log2_page)];
+          if ((uint32_t)page < (uint32_t)kv.num_pages)
+            off = (int64_t)page * kv.page_stride + (int64_t)(slot & pmask) * kv.token_stride;
+        }
+        t_doff[t] = off;
+      }
+      __syncthreads();
+      load_draft(dlo, dk, dv, dkeep);
+    }
+  }
+
+  // ---- the key loop ---------------------------------------------------------
+  float m = kNegInf, l = 0.f;
+  f32x4 o[DB];
+#pragma unroll
+  for (int db = 0; db < DB; ++db) o[db] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  auto kfrag = [&](const uint16_t* st, int kb, int ks) -> bf16x8 {
+    return *reinterpret_cast<const bf16x8*>(st + (kb * 16 + l16) * RS + (ks * 4 + g4) * 8);
+  };
+  auto vt_frag = [&](const uint16_t* st, int db) -> bf16x8 {
+    const uint16_t* vb = st + 32 * RS + (4 * g4 + (l16 >> 2)) * RS + db * 16 + 4 * (l16 & 3);
+    const i16x4 lo = lds_read_tr16(vb);
+    const i16x4 hi = lds_read_tr16(vb + 16 * RS);
+    return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+  };
+  // The lane's row's draft visibility (fused verify): request token, start of
+  // its branch, ancestor set for general trees.
+  int rbs = 0;
+  uint64_t ranc = 0;
+  const bool tree = a.draft_mask != nullptr;
+  // One tile out of a stage into the lane's row state.  kind 0: prefix keys
+  // [base, end); kind 1: draft keys under the ancestor rule.
+  auto compute = [&](const uint16_t* st, int base, int end, int kind) {
+    f32x4 s[2];
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) acc = mfma16(kfrag(st, kb, ks), qf[ks], acc);
+      s[kb] = acc;
+    }
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) asm volatile("" : "+v"(s[kb]));
+    if (kind == 1) {
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int key = base + kb * 16 + g4 * 4 + i;
+          const bool vis = (key < end) & (tree ? draft_visible_tree(ranc, rbs, key) : draft_visible(rtok, rbs, key));
+          s[kb][i] = vis ? s[kb][i] : kNegInf;
+        }
+    } else if (base + 32 > end) {
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) s[kb][i] = base + kb * 16 + g4 * 4 + i < end ? s[kb][i] : kNegInf;
+    }
+    // Online softmax in base 2; the carried max is raised only past a slack.
+    const float lm = fmaxf(fmaxf(fmaxf(s[0][0], s[0][1]), fmaxf(s[0][2], s[0][3])),
+                           fmaxf(fmaxf(s[1][0], s[1][1]), fmaxf(s[1][2], s[1][3])));
+    if (__any(lm * c2 > m + kMaxSlack)) {
+      const float mx = rowgroup_max(lm) * c2;
+      const float mnew = mx > m + kMaxSlack ? mx : m;
+      const float ms = mnew == kNegInf ? 0.f : mnew;
+      const float alpha = mnew == m ? 1.f : fast_exp2(m - ms);
+      const bool resc = mnew != m && m != kNegInf;
+      m = mnew;
+      l *= alpha;
+      if (__any(resc)) {
+#pragma unroll
+        for (int db = 0; db < DB; ++db) o[db] *= alpha;
+      }
+    }
+    const float ms = m == kNegInf ? 0.f : m;
+    float p[8];
+    float sum = 0.f;
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        p[kb * 4 + i] = fast_exp2(s[kb][i] * c2 - ms);
+        sum += p[kb * 4 + i];
+      }
+    l += sum;
+    const u32x4 pk = {pack_bf16x2(p[0], p[1]), pack_bf16x2(p[2], p[3]), pack_bf16x2(p[4], p[5]),
+                      pack_bf16x2(p[6], p[7])};
+    const bf16x8 pf = __builtin_bit_cast(bf16x8, pk);
+#pragma unroll
+    for (int db = 0; db < DB; ++db) o[db] = mfma16(vt_frag(st, db), pf, o[db]);
+  };
+
+  // Tile 0 into stage 0; its slot then requests tile DEPTH.
+  stage(kq[0], vq[0], true, stg[0]);
+  load_tile(DEPTH, pgn, kq[0], vq[0]);
+  pgn = page_of(DEPTH + 1);
+  __syncthreads();
+  // Step t: stage tile t+1 (slot (t+1) % DEPTH) into stage (t+1) & 1, request
+  // tile t+1+DEPTH into that slot, compute tile t out of stage t & 1, barrier.
+  // Tiles past the split are empty ranges: no memory access, zeros staged.
+  // Whole rings of DEPTH steps, with no exit inside a ring: every back edge
+  // then carries the same ring state as the entry, and each stage waits for
+  // its own slot only.  Steps past the last tile stage zeros and compute
+  // nothing.
+  for (int t0 = 0; t0 < nt; t0 += DEPTH) {
+#pragma unroll
+    for (int k = 0; k < DEPTH; ++k) {
+      const int t = t0 + k;
+      const int sn = (k + 1) % DEPTH;
+      stage(kq[sn], vq[sn], true, stg[(k + 1) & 1]);
+      load_tile(t + 1 + DEPTH, pgn, kq[sn], vq[sn]);
+      pgn = page_of(t + 2 + DEPTH);
+      if (wave_rows && t < nt) compute(stg[k & 1], p0 + t * 32, p1, 0);
+      __syncthreads();
+    }
+  }
+
+  // ---- pass B of the fused verify launch: the chunk's visible draft tiles ---
+  if constexpr (kVerify) {
+    if (drafts) {
+      if (rvalid) {
+        rbs = t_rbs[rtok - tok_first];
+        if (tree) ranc = a.draft_mask[tok0 + rtok];
+      }
+      for (int base = dlo; base < dhi; base += 32) {
+        if (base != dlo) load_draft(base, dk, dv, dkeep);
+        stage(dk, dv, dkeep, stg[0]);
+        __syncthreads();
+        if (wave_rows) compute(stg[0], base, dhi, 1);
+        __syncthreads();
+      }
+    }
+  }
+  mfma_drain();
+  if (bad_page && lane == 0) atomicOr(&g_device_error, kErrPage);
+
+  // ---- output ----------------------------------------------------------------
+  l = rowgroup_sum(l);
+  if (!rvalid) return;
+  const float lse2 = l > 0.f ? m + fast_log2(l) : kNegInf;
+  const float f = l > 0.f ? 1.f / l : 0.f;
+  const int64_t plane = (int64_t)a.total_rows * a.num_qo_heads;
+  if (a.n_splits > 1) {
+#pragma unroll
+    for (int db = 0; db < DB; ++db)
+      *reinterpret_cast<f32x4*>(a.ws_o + (split * plane + orow) * D + db * 16 + g4 * 4) = o[db] * f;
+    if (g4 == 0) a.ws_lse[split * plane + orow] = lse2;
+    return;
+  }
+#pragma unroll
+  for (int db = 0; db < DB; ++db) {
+    const f32x4 x = o[db] * f;
+    const int c = db * 16 + g4 * 4;
+    if (a.o_bf16) {
+      *reinterpret_cast<u32x2*>(reinterpret_cast<uint16_t*>(a.o) + orow * D + c) =
+          u32x2{pack_bf16x2(x[0], x[1]), pack_bf16x2(x[2], x[3])};
+    } else {
+      *reinterpret_cast<f32x4*>(reinterpret_cast<float*>(a.o) + orow * D + c) = x;
+    }
+  }
+  if (g4 == 0 && a.lse) a.lse[orow] = lse2 * kLn2;
+}
+
+}  // namespace casc

@@ -74,6 +74,17 @@ def small_cases():
             W.build_workload("draft_tree", [75, 0, 300], [[12], [7], [20]], 8, 2, 128, 16, seed=27), 28),
         "draft_tree_big": lambda: W.attach_random_trees(
             W.build_workload("draft_tree_big", [200, 40], [[64], [33]], 16, 2, 64, 16, seed=29), 30),
+        # At least 1024 query rows per (request, kv head) at d = 128: pass A
+        # and the fused verify pass run the row-split kernel.  Chains whose
+        # 40-token branches span several draft tiles of a 128-row chunk, an
+        # empty prefix, a one-token request among large ones; a 64-node tree
+        # with 16 query heads per kv head; a long prefix split over workgroups
+        # (partials merged by the split-merge pass).
+        "rows_chains": lambda: W.build_workload("rows_chains", [700, 0, 45], [[40] * 4, [30] * 5, [1]],
+                                                16, 2, 128, 16, seed=31),
+        "rows_tree": lambda: W.attach_random_trees(
+            W.build_workload("rows_tree", [300, 90], [[64], [50]], 32, 2, 128, 16, seed=32), 33),
+        "rows_split": lambda: W.build_workload("rows_split", [9000], [[64, 64]], 16, 2, 128, 16, seed=34),
     }
 
 
