@@ -254,19 +254,19 @@ hipError_t launch(int mode, int head_dim, int rb, const casc::AttnArgs& a, int64
              : casc::launch_attn_d128(mode, rb, a, (int)grid, s, e0, e1);
 }
 
-// Query rows per (request, kv head) from which pass A and the fused verify
-// pass run the row-split kernel: at least eight full work items of
+// Query rows per (request, kv head) from which pass A, the fused verify pass
+// and pass B run the row-split kernel: at least eight full work items of
 // kRowsPerItem rows, where its two waves per SIMD keep the matrix pipes
 // busy (a prefix-hit suffix prefill).  Below it the key-split kernel, one
 // wave per SIMD over the whole row tile, is as fast or faster (measured on
 // the verify workloads).
 constexpr int64_t kRowKernelMinRows = 8 * casc::kRowsPerItem;
 
-// Pass A and the fused verify pass (`mode`), unsplit or one launch of the
-// splits: the row-split kernel (head dim 128, bf16 pools, row-heavy
+// Pass A, the fused verify pass or pass B (`mode`), unsplit or one launch of
+// the splits: the row-split kernel (head dim 128, bf16 pools, row-heavy
 // requests) over chunks of up to kRowsPerItem query rows, else the key-split
 // kernel of the plan.
-hipError_t launch_prefix_modes(int mode, const cascade_paged_kv* kv,
+hipError_t launch_row_modes(int mode, const cascade_paged_kv* kv,
                                const cascade_tree* t, const Plan& p, casc::AttnArgs a, int splits,
                                hipStream_t s, hipEvent_t e0 = nullptr, hipEvent_t e1 = nullptr) {
   const int64_t rows = (int64_t)t->max_request_rows * p.group;
@@ -339,13 +339,13 @@ cascade_status cascade_prefix_attn(const cascade_query* q, const cascade_paged_k
     a.ws_o = static_cast<float*>(ws);
     a.ws_lse = reinterpret_cast<float*>(static_cast<char*>(ws) + wl.lse_off);
     a.grid_splits = p.n_splits;
-    e = launch_prefix_modes(casc::kModePrefix, kv, t, p, a, p.n_splits, s);
+    e = launch_row_modes(casc::kModePrefix, kv, t, p, a, p.n_splits, s);
     if (e != hipSuccess) return hip_fail(e, "prefix pass launch");
     a.grid_splits = 1;
     e = launch(casc::kModePrefixFinish, kv->head_dim, p.rb, a, p.items, s);
     if (e != hipSuccess) return hip_fail(e, "prefix split merge launch");
   } else {
-    e = launch_prefix_modes(casc::kModePrefix, kv, t, p, a, 1, s);
+    e = launch_row_modes(casc::kModePrefix, kv, t, p, a, 1, s);
     if (e != hipSuccess) return hip_fail(e, "prefix pass launch");
   }
   return CASCADE_OK;
@@ -365,7 +365,7 @@ cascade_status cascade_draft_attn(const cascade_query* q, const cascade_paged_kv
   a.o = o_b;
   a.o_bf16 = 0;
   a.lse = lse_b;
-  const hipError_t e = launch(casc::kModeDraft, kv->head_dim, p.rb, a, p.items, static_cast<hipStream_t>(stream));
+  const hipError_t e = launch_row_modes(casc::kModeDraft, kv, t, p, a, 1, static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return hip_fail(e, "draft pass launch");
   return CASCADE_OK;
 }
@@ -422,13 +422,13 @@ cascade_status cascade_verify_attn(const cascade_query* q, const cascade_paged_k
     a.ws_o = static_cast<float*>(ws);
     a.ws_lse = reinterpret_cast<float*>(static_cast<char*>(ws) + wl.lse_off);
     a.grid_splits = p.n_splits;
-    e = launch_prefix_modes(casc::kModeVerify, kv, t, p, a, p.n_splits, s, e0, nullptr);
+    e = launch_row_modes(casc::kModeVerify, kv, t, p, a, p.n_splits, s, e0, nullptr);
     if (e != hipSuccess) return hip_fail(e, "verify prefix launch");
     a.grid_splits = 1;
     e = launch(casc::kModeVerifyFinish, kv->head_dim, p.rb, a, p.items, s, nullptr, e1);
     if (e != hipSuccess) return hip_fail(e, "verify merge launch");
   } else {
-    e = launch_prefix_modes(casc::kModeVerify, kv, t, p, a, 1, s, e0, e1);
+    e = launch_row_modes(casc::kModeVerify, kv, t, p, a, 1, s, e0, e1);
     if (e != hipSuccess) return hip_fail(e, "verify launch");
   }
   if (g_timing.enabled) g_timing.recorded = true;

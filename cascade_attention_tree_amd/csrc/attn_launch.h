@@ -45,8 +45,8 @@ static hipError_t launch_rb(int mode, const AttnArgs& a, int grid, hipStream_t s
   return hipGetLastError();
 }
 
-// Row-split kernel (head_dim 128, pass A and the fused verify pass): tiles
-// requested this many steps ahead.
+// Row-split kernel (head_dim 128: pass A, the fused verify pass, pass B):
+// tiles requested this many steps ahead.
 constexpr int kRowDepth = 4;
 
 static inline hipError_t launch_rows(int mode, const AttnArgs& a, int grid, hipStream_t s, hipEvent_t e0,
@@ -55,6 +55,7 @@ static inline hipError_t launch_rows(int mode, const AttnArgs& a, int grid, hipS
   switch (mode) {
     case kModePrefix: go(rows_kernel<kModePrefix, kRowDepth>, g, b, s, e0, e1, a); break;
     case kModeVerify: go(rows_kernel<kModeVerify, kRowDepth>, g, b, s, e0, e1, a); break;
+    case kModeDraft: go(rows_kernel<kModeDraft, kRowDepth>, g, b, s, e0, e1, a); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();

@@ -38,7 +38,7 @@ static_assert(kRowsPerItem == 16 * kRowWaves, "one 16-row block per wave");
 template <int MODE, int DEPTH>
 __global__ void __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2)))
 rows_kernel(const AttnArgs a) {
-  static_assert(MODE == kModePrefix || MODE == kModeVerify, "prefix-only launches");
+  static_assert(MODE == kModePrefix || MODE == kModeVerify || MODE == kModeDraft, "pass A, verify, pass B");
   static_assert(DEPTH % 2 == 0, "the two LDS stages alternate within the unrolled ring");
   constexpr int D = 128;
   constexpr int KS = D / 32;   // k-steps of the Q K^T contraction
@@ -49,14 +49,16 @@ rows_kernel(const AttnArgs a) {
   constexpr int EB = 2;  // bf16 pools
   typedef u32x4 Raw;
   constexpr bool kVerify = MODE == kModeVerify;
+  constexpr bool kDraft = MODE == kModeDraft;
+  constexpr bool kTables = kVerify || kDraft;
   constexpr int NBCAP = 128;   // branches of a request resolved in LDS
   constexpr int KEYCAP = 512;  // draft keys of a chunk resolved in LDS
 
   __shared__ __attribute__((aligned(16))) uint16_t stg[2][STAGE];
-  __shared__ int64_t t_doff[kVerify ? KEYCAP : 1];
-  __shared__ int t_bnd[kVerify ? NBCAP + 1 : 1];
-  __shared__ int t_dst[kVerify ? NBCAP : 1];
-  __shared__ int t_rbs[kVerify ? kRowsPerItem : 1];
+  __shared__ int64_t t_doff[kTables ? KEYCAP : 1];
+  __shared__ int t_bnd[kTables ? NBCAP + 1 : 1];
+  __shared__ int t_dst[kTables ? NBCAP : 1];
+  __shared__ int t_rbs[kTables ? kRowsPerItem : 1];
 
   const int tid = (int)threadIdx.x;
   const int lane = tid & 63;
@@ -79,6 +81,7 @@ rows_kernel(const AttnArgs a) {
   const int je = crb[req + 1];
   const int L_in = as_const(a.cache_seqlens)[req];
   cint32* pt_row = as_const(a.page_table + (int64_t)req * a.page_table_stride);
+  const int nb = je - jb;
   // A key split at or past the request's length has no keys (split 0 always
   // runs: it holds the drafts of the fused launch and the row checks).
   if (split != 0 && (int64_t)split * a.split_len >= L_in) return;
@@ -95,7 +98,36 @@ rows_kernel(const AttnArgs a) {
     atomicOr(&g_device_error, kErrRow);  // rows past the planned chunks are not computed
   if (row0 >= nrows) return;
   const int nrc = min(nrows - row0, kRowsPerItem);  // rows of this chunk
+  const int tok_first = row0 / a.group;
+  const int tok_last = (row0 + nrc - 1) / a.group;
+  const int dhi = tok_last + 1;  // draft keys the chunk's rows can see end here
 
+  // Pass B of a request with a single branch (a prefix-hit suffix, a draft
+  // tree): its draft keys are consecutive slots of one block-table row
+  // (token x at slot ds0 + x), so the key loop streams them like a prefix,
+  // from the 32-slot boundary at or below ds0; the keys in front of the
+  // branch are staged as zeros and masked.  Other requests take their draft
+  // tiles through per-key offset tables (the draft phase below).
+  bool slot_mode = false;
+  int ds0 = 0;
+  int p0 = 0, p1 = 0;
+  if constexpr (kDraft) {
+    const int64_t cap = (int64_t)a.draft_page_table_stride << a.kv.log2_page;
+    if (nb == 1 && cap > 0) {
+      ds0 = a.draft_start ? as_const(a.draft_start)[jb] : 0;
+      slot_mode = ds0 >= 0 && ds0 < cap;
+    }
+    if (slot_mode) {
+      pt_row = as_const(a.draft_page_table + (int64_t)jb * a.draft_page_table_stride);
+      int64_t se = (int64_t)ds0 + dhi;
+      if (se > cap) {
+        if (tid == 0) atomicOr(&g_device_error, kErrPage);
+        se = cap;
+      }
+      p0 = ds0 & ~31;
+      p1 = (int)se;
+    }
+  } else {
   int L = L_in;
   {
     const int cap = a.page_table_stride << a.kv.log2_page;
@@ -113,12 +145,19 @@ rows_kernel(const AttnArgs a) {
   // Uniform by construction; stated so that the buffer descriptors built
   // from them live in scalar registers (the flag stores above are per lane).
   L = __builtin_amdgcn_readfirstlane(L);
-  const int p0 = split * a.split_len;
-  int p1 = min(L, p0 + a.split_len);
+  p0 = split * a.split_len;
+  p1 = min(L, p0 + a.split_len);
   if (a.n_splits > 1 && p0 >= L && (MODE == kModePrefix || split != 0)) return;
   if (p1 < p0) p1 = p0;
+  }
+  p0 = __builtin_amdgcn_readfirstlane(p0);
   p1 = __builtin_amdgcn_readfirstlane(p1);
-  const int nt = (p1 - p0 + 31) >> 5;  // prefix tiles of this split
+  const int nt = (p1 - p0 + 31) >> 5;  // tiles of the key loop
+  // Key loop tiles as the mask sees them: prefix keys [p0, p1), or the draft
+  // tokens of a slot-mode branch (slot - ds0, negative in front of it).
+  const int kshift = kDraft ? ds0 : 0;
+  const int kind = kDraft ? 1 : 0;
+  const int kend = kDraft ? dhi : p1;
 
   const KvView kv = a.kv;
   const float c2 = a.scale_log2;
@@ -199,14 +238,10 @@ rows_kernel(const AttnArgs a) {
     pgn = page_of(k + 1);
   }
 
-  // ---- tree tables (fused verify, split 0): drafts of the chunk's tokens ---
-  const int tok_first = row0 / a.group;
-  const int tok_last = (row0 + nrc - 1) / a.group;
-  const bool drafts = kVerify && split == 0;
-  const int nb = je - jb;
+  // ---- tree tables (fused verify split 0, pass B not in slot mode) ---------
+  const bool drafts = (kVerify && split == 0) || (kDraft && !slot_mode);
   const bool lds_bnd = nb <= NBCAP;
   int dlo = 0;
-  const int dhi = tok_last + 1;
   Raw dk, dv;  // the first draft tile, requested after the tables
   bool dkeep = false;
   auto branch_at = [&](int x) -> int {  // local branch of request token x
@@ -244,7 +279,7 @@ rows_kernel(const AttnArgs a) {
     kr = keep ? *reinterpret_cast<const Raw*>(k_bytes + e * EB) : Raw{};
     vr = keep ? *reinterpret_cast<const Raw*>(v_bytes + e * EB) : Raw{};
   };
-  if constexpr (kVerify) {
+  if constexpr (kTables) {
     if (drafts) {
       if (lds_bnd) {
         for (int t = tid; t <= nb; t += 512) t_bnd[t] = a.branch_qo_indptr[jb + t];
@@ -354,8 +389,11 @@ rows_kernel(const AttnArgs a) {
     for (int db = 0; db < DB; ++db) o[db] = mfma16(vt_frag(st, db), pf, o[db]);
   };
 
-  // Tile 0 into stage 0; its slot then requests tile DEPTH.
-  stage(kq[0], vq[0], true, stg[0]);
+  // Slot-mode pass B: every row's branch starts at request token 0.
+  if (kDraft && slot_mode && rvalid && tree) ranc = a.draft_mask[tok0 + rtok];
+  // Tile 0 into stage 0 (keys in front of a slot-mode branch as zeros); its
+  // slot then requests tile DEPTH.
+  stage(kq[0], vq[0], !kDraft || p0 + skey >= ds0, stg[0]);
   load_tile(DEPTH, pgn, kq[0], vq[0]);
   pgn = page_of(DEPTH + 1);
   __syncthreads();
@@ -374,13 +412,13 @@ rows_kernel(const AttnArgs a) {
       stage(kq[sn], vq[sn], true, stg[(k + 1) & 1]);
       load_tile(t + 1 + DEPTH, pgn, kq[sn], vq[sn]);
       pgn = page_of(t + 2 + DEPTH);
-      if (wave_rows && t < nt) compute(stg[k & 1], p0 + t * 32, p1, 0);
+      if (wave_rows && t < nt) compute(stg[k & 1], p0 + t * 32 - kshift, kend, kind);
       __syncthreads();
     }
   }
 
-  // ---- pass B of the fused verify launch: the chunk's visible draft tiles ---
-  if constexpr (kVerify) {
+  // ---- pass B through the offset tables: the chunk's visible draft tiles ---
+  if constexpr (kTables) {
     if (drafts) {
       if (rvalid) {
         rbs = t_rbs[rtok - tok_first];

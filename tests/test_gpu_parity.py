@@ -228,13 +228,15 @@ def test_prefix_hit_small_all_rows(B, h):
     cmp(o3, l3, ro, rl)
 
 
+@pytest.mark.parametrize("n_tokens", [300, 600])
 @pytest.mark.parametrize("h", [0.5, 0.9])
-def test_draft_pass_ignores_slots_in_front_of_the_branch(B, h):
-    """Pass B of a prefix hit reads the suffix like a prefix, from tiles that
-    start at a multiple of 32 slots; with H not such a multiple, its first tile
-    also covers up to 31 prefix slots in front of the suffix.  Those slots are
-    set to NaN here: pass B must not let them into its result."""
-    wl = W.prefix_hit(h, batch=2, n_tokens=300, seed=43)
+def test_draft_pass_ignores_slots_in_front_of_the_branch(B, h, n_tokens):
+    """The prefix slots just in front of a prefix-hit suffix are set to NaN:
+    pass B must not let them into its result.  At 600 tokens (1200 query rows
+    per kv head) pass B streams the suffix like a prefix from tiles that start
+    at a multiple of 32 slots, so its first tile covers those slots (H is not
+    such a multiple here)."""
+    wl = W.prefix_hit(h, batch=2, n_tokens=n_tokens, seed=43)
     P = wl.page_size
     k, v = wl.k_pool.copy(), wl.v_pool.copy()
     for j in range(wl.num_branches):
@@ -245,7 +247,7 @@ def test_draft_pass_ignores_slots_in_front_of_the_branch(B, h):
             k[pg, t % P] = np.nan
             v[pg, t % P] = np.nan
     wl = dataclasses.replace(wl, k_pool=k, v_pool=v)
-    note(f"draft_attn prefix-hit h={h}, NaN in front of the suffix")
+    note(f"draft_attn prefix-hit h={h} N={n_tokens}, NaN in front of the suffix")
     x = B.to_device(wl)
     o, l = B.cascade_draft_attn(x)
     torch.cuda.synchronize()
