@@ -255,12 +255,12 @@ hipError_t launch(int mode, int head_dim, int rb, const casc::AttnArgs& a, int64
 }
 
 // Query rows per (request, kv head) from which pass A, the fused verify pass
-// and pass B run the row-split kernel: at least eight full work items of
+// and pass B run the row-split kernel: at least four full work items of
 // kRowsPerItem rows, where its two waves per SIMD keep the matrix pipes
 // busy (a prefix-hit suffix prefill).  Below it the key-split kernel, one
 // wave per SIMD over the whole row tile, is as fast or faster (measured on
 // the verify workloads).
-constexpr int64_t kRowKernelMinRows = 8 * casc::kRowsPerItem;
+constexpr int64_t kRowKernelMinRows = 1024;
 
 // Pass A, the fused verify pass or pass B (`mode`), unsplit or one launch of
 // the splits: the row-split kernel (head dim 128, bf16 pools, row-heavy

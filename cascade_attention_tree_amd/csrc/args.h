@@ -22,9 +22,9 @@ struct KvView {
                        // count elements, so they are byte offsets for FP8)
 };
 
-// Query rows per work item of the row-split kernel (pass A and the fused
-// verify pass at head_dim 128): 8 waves of at most 16 rows.
-constexpr int kRowsPerItem = 128;
+// Query rows per work item of the row-split kernel (head_dim 128): 8 waves
+// of at most 32 rows (two 16-row MFMA blocks each).
+constexpr int kRowsPerItem = 256;
 
 enum AttnMode : int {
   kModePrefix = 0,        // pass A: unsplit -> (o_A, LSE_A); split -> partial states

@@ -33,13 +33,14 @@
 namespace casc {
 
 constexpr int kRowWaves = 8;
-static_assert(kRowsPerItem == 16 * kRowWaves, "one 16-row block per wave");
 
-template <int MODE, int DEPTH>
+template <int MODE, int DEPTH, int RBW>
 __global__ void __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2)))
 rows_kernel(const AttnArgs a) {
   static_assert(MODE == kModePrefix || MODE == kModeVerify || MODE == kModeDraft, "pass A, verify, pass B");
   static_assert(DEPTH % 2 == 0, "the two LDS stages alternate within the unrolled ring");
+  static_assert(kRowsPerItem == kRowWaves * 16 * RBW, "RBW 16-row blocks per wave");
+  constexpr int ROWS_W = 16 * RBW;  // query rows per wave
   constexpr int D = 128;
   constexpr int KS = D / 32;   // k-steps of the Q K^T contraction
   constexpr int DB = D / 16;   // 16-channel blocks of the head dim
@@ -164,26 +165,28 @@ rows_kernel(const AttnArgs a) {
   const int pmask = (1 << kv.log2_page) - 1;
   const int64_t head_off = (int64_t)g * kv.head_stride;
 
-  // ---- this lane's row: wave w holds chunk rows [16w, 16w + 16) ------------
-  // Rows fill whole 16-row blocks from wave 0 on (waves past the last block
-  // only load and stage): spreading them thinner would pad every block and
-  // make more waves read each tile out of LDS.
-  const int rpw = 16;
-  const bool wave_rows = w * rpw < nrc;               // uniform
-  const int rw = w * rpw + l16;
-  const bool rvalid = l16 < rpw && rw < nrc;
-  const int rho = row0 + (rvalid ? rw : 0);  // row within (request, kv head)
-  const int rtok = rho / a.group;            // request token of the row
-  const int hq = g * a.group + (rho - rtok * a.group);
-  const int64_t orow = (int64_t)(tok0 + rtok) * a.num_qo_heads + hq;
-
-  // Q B-fragments: channels ks*32 + g4*8 .. +8 of the lane's row.
-  bf16x8 qf[KS];
-  {
-    const uint16_t* qp = a.q + (int64_t)(tok0 + rtok) * a.q_row_stride + (int64_t)hq * a.q_head_stride + g4 * 8;
+  // ---- this lane's rows: wave w holds chunk rows [ROWS_W w, ROWS_W (w+1)) --
+  // Rows fill whole waves from wave 0 on (waves past the last row only load
+  // and stage): spreading them thinner would pad every 16-row block and make
+  // more waves read each tile out of LDS.  Row block rb of the wave: rows
+  // ROWS_W w + 16 rb + l16.
+  const bool wave_rows = w * ROWS_W < nrc;  // uniform
+  bool rvalid[RBW];
+  int rtok[RBW];
+  int64_t orow[RBW];
+  bf16x8 qf[RBW][KS];  // Q B-fragments: channels ks*32 + g4*8 .. +8 of the row
+#pragma unroll
+  for (int rb = 0; rb < RBW; ++rb) {
+    const int rw = w * ROWS_W + rb * 16 + l16;
+    rvalid[rb] = rw < nrc;
+    const int rho = row0 + (rvalid[rb] ? rw : 0);  // row within (request, kv head)
+    rtok[rb] = rho / a.group;                      // request token of the row
+    const int hq = g * a.group + (rho - rtok[rb] * a.group);
+    orow[rb] = (int64_t)(tok0 + rtok[rb]) * a.num_qo_heads + hq;
+    const uint16_t* qp = a.q + (int64_t)(tok0 + rtok[rb]) * a.q_row_stride + (int64_t)hq * a.q_head_stride + g4 * 8;
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks)
-      qf[ks] = rvalid ? *reinterpret_cast<const bf16x8*>(qp + ks * 32) : bf16x8{};
+      qf[rb][ks] = rvalid[rb] ? *reinterpret_cast<const bf16x8*>(qp + ks * 32) : bf16x8{};
   }
 
   // ---- prefix tile loads -------------------------------------------------
@@ -308,10 +311,15 @@ rows_kernel(const AttnArgs a) {
   }
 
   // ---- the key loop ---------------------------------------------------------
-  float m = kNegInf, l = 0.f;
-  f32x4 o[DB];
+  float m[RBW], l[RBW];
+  f32x4 o[RBW][DB];
 #pragma unroll
-  for (int db = 0; db < DB; ++db) o[db] = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int rb = 0; rb < RBW; ++rb) {
+    m[rb] = kNegInf;
+    l[rb] = 0.f;
+#pragma unroll
+    for (int db = 0; db < DB; ++db) o[rb][db] = f32x4{0.f, 0.f, 0.f, 0.f};
+  }
 
   auto kfrag = [&](const uint16_t* st, int kb, int ks) -> bf16x8 {
     return *reinterpret_cast<const bf16x8*>(st + (kb * 16 + l16) * RS + (ks * 4 + g4) * 8);
@@ -324,73 +332,93 @@ rows_kernel(const AttnArgs a) {
   };
   // The lane's row's draft visibility (fused verify): request token, start of
   // its branch, ancestor set for general trees.
-  int rbs = 0;
-  uint64_t ranc = 0;
+  int rbs[RBW] = {};
+  uint64_t ranc[RBW] = {};
   const bool tree = a.draft_mask != nullptr;
   // One tile out of a stage into the lane's row state.  kind 0: prefix keys
   // [base, end); kind 1: draft keys under the ancestor rule.
   auto compute = [&](const uint16_t* st, int base, int end, int kind) {
-    f32x4 s[2];
+    f32x4 s[RBW][2];
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
-      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+    for (int rb = 0; rb < RBW; ++rb)
 #pragma unroll
-      for (int ks = 0; ks < KS; ++ks) acc = mfma16(kfrag(st, kb, ks), qf[ks], acc);
-      s[kb] = acc;
-    }
+      for (int kb = 0; kb < 2; ++kb) s[rb][kb] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb) asm volatile("" : "+v"(s[kb]));
-    if (kind == 1) {
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) {
+        const bf16x8 kf = kfrag(st, kb, ks);
+#pragma unroll
+        for (int rb = 0; rb < RBW; ++rb) s[rb][kb] = mfma16(kf, qf[rb][ks], s[rb][kb]);
+      }
+#pragma unroll
+    for (int rb = 0; rb < RBW; ++rb)
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) asm volatile("" : "+v"(s[rb][kb]));
+    bf16x8 pf[RBW];
+#pragma unroll
+    for (int rb = 0; rb < RBW; ++rb) {
+      if (kind == 1) {
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const int key = base + kb * 16 + g4 * 4 + i;
+            const bool vis = (key < end) & (tree ? draft_visible_tree(ranc[rb], rbs[rb], key)
+                                                 : draft_visible(rtok[rb], rbs[rb], key));
+            s[rb][kb][i] = vis ? s[rb][kb][i] : kNegInf;
+          }
+      } else if (base + 32 > end) {
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) s[rb][kb][i] = base + kb * 16 + g4 * 4 + i < end ? s[rb][kb][i] : kNegInf;
+      }
+      // Online softmax in base 2; the carried max is raised only past a slack.
+      const float lm = fmaxf(fmaxf(fmaxf(s[rb][0][0], s[rb][0][1]), fmaxf(s[rb][0][2], s[rb][0][3])),
+                             fmaxf(fmaxf(s[rb][1][0], s[rb][1][1]), fmaxf(s[rb][1][2], s[rb][1][3])));
+      if (__any(lm * c2 > m[rb] + kMaxSlack)) {
+        const float mx = rowgroup_max(lm) * c2;
+        const float mnew = mx > m[rb] + kMaxSlack ? mx : m[rb];
+        const float ms = mnew == kNegInf ? 0.f : mnew;
+        const float alpha = mnew == m[rb] ? 1.f : fast_exp2(m[rb] - ms);
+        const bool resc = mnew != m[rb] && m[rb] != kNegInf;
+        m[rb] = mnew;
+        l[rb] *= alpha;
+        if (__any(resc)) {
+#pragma unroll
+          for (int db = 0; db < DB; ++db) o[rb][db] *= alpha;
+        }
+      }
+      const float ms = m[rb] == kNegInf ? 0.f : m[rb];
+      float p[8];
+      float sum = 0.f;
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          const int key = base + kb * 16 + g4 * 4 + i;
-          const bool vis = (key < end) & (tree ? draft_visible_tree(ranc, rbs, key) : draft_visible(rtok, rbs, key));
-          s[kb][i] = vis ? s[kb][i] : kNegInf;
+          p[kb * 4 + i] = fast_exp2(s[rb][kb][i] * c2 - ms);
+          sum += p[kb * 4 + i];
         }
-    } else if (base + 32 > end) {
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) s[kb][i] = base + kb * 16 + g4 * 4 + i < end ? s[kb][i] : kNegInf;
+      l[rb] += sum;
+      const u32x4 pk = {pack_bf16x2(p[0], p[1]), pack_bf16x2(p[2], p[3]), pack_bf16x2(p[4], p[5]),
+                        pack_bf16x2(p[6], p[7])};
+      pf[rb] = __builtin_bit_cast(bf16x8, pk);
     }
-    // Online softmax in base 2; the carried max is raised only past a slack.
-    const float lm = fmaxf(fmaxf(fmaxf(s[0][0], s[0][1]), fmaxf(s[0][2], s[0][3])),
-                           fmaxf(fmaxf(s[1][0], s[1][1]), fmaxf(s[1][2], s[1][3])));
-    if (__any(lm * c2 > m + kMaxSlack)) {
-      const float mx = rowgroup_max(lm) * c2;
-      const float mnew = mx > m + kMaxSlack ? mx : m;
-      const float ms = mnew == kNegInf ? 0.f : mnew;
-      const float alpha = mnew == m ? 1.f : fast_exp2(m - ms);
-      const bool resc = mnew != m && m != kNegInf;
-      m = mnew;
-      l *= alpha;
-      if (__any(resc)) {
 #pragma unroll
-        for (int db = 0; db < DB; ++db) o[db] *= alpha;
-      }
+    for (int db = 0; db < DB; ++db) {
+      const bf16x8 vf = vt_frag(st, db);
+#pragma unroll
+      for (int rb = 0; rb < RBW; ++rb) o[rb][db] = mfma16(vf, pf[rb], o[rb][db]);
     }
-    const float ms = m == kNegInf ? 0.f : m;
-    float p[8];
-    float sum = 0.f;
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        p[kb * 4 + i] = fast_exp2(s[kb][i] * c2 - ms);
-        sum += p[kb * 4 + i];
-      }
-    l += sum;
-    const u32x4 pk = {pack_bf16x2(p[0], p[1]), pack_bf16x2(p[2], p[3]), pack_bf16x2(p[4], p[5]),
-                      pack_bf16x2(p[6], p[7])};
-    const bf16x8 pf = __builtin_bit_cast(bf16x8, pk);
-#pragma unroll
-    for (int db = 0; db < DB; ++db) o[db] = mfma16(vt_frag(st, db), pf, o[db]);
   };
 
   // Slot-mode pass B: every row's branch starts at request token 0.
-  if (kDraft && slot_mode && rvalid && tree) ranc = a.draft_mask[tok0 + rtok];
+  if (kDraft && slot_mode && tree) {
+#pragma unroll
+    for (int rb = 0; rb < RBW; ++rb)
+      if (rvalid[rb]) ranc[rb] = a.draft_mask[tok0 + rtok[rb]];
+  }
   // Tile 0 into stage 0 (keys in front of a slot-mode branch as zeros); its
   // slot then requests tile DEPTH.
   stage(kq[0], vq[0], !kDraft || p0 + skey >= ds0, stg[0]);
@@ -420,10 +448,12 @@ rows_kernel(const AttnArgs a) {
   // ---- pass B through the offset tables: the chunk's visible draft tiles ---
   if constexpr (kTables) {
     if (drafts) {
-      if (rvalid) {
-        rbs = t_rbs[rtok - tok_first];
-        if (tree) ranc = a.draft_mask[tok0 + rtok];
-      }
+#pragma unroll
+      for (int rb = 0; rb < RBW; ++rb)
+        if (rvalid[rb]) {
+          rbs[rb] = t_rbs[rtok[rb] - tok_first];
+          if (tree) ranc[rb] = a.draft_mask[tok0 + rtok[rb]];
+        }
       for (int base = dlo; base < dhi; base += 32) {
         if (base != dlo) load_draft(base, dk, dv, dkeep);
         stage(dk, dv, dkeep, stg[0]);
@@ -437,30 +467,33 @@ rows_kernel(const AttnArgs a) {
   if (bad_page && lane == 0) atomicOr(&g_device_error, kErrPage);
 
   // ---- output ----------------------------------------------------------------
-  l = rowgroup_sum(l);
-  if (!rvalid) return;
-  const float lse2 = l > 0.f ? m + fast_log2(l) : kNegInf;
-  const float f = l > 0.f ? 1.f / l : 0.f;
   const int64_t plane = (int64_t)a.total_rows * a.num_qo_heads;
-  if (a.n_splits > 1) {
 #pragma unroll
-    for (int db = 0; db < DB; ++db)
-      *reinterpret_cast<f32x4*>(a.ws_o + (split * plane + orow) * D + db * 16 + g4 * 4) = o[db] * f;
-    if (g4 == 0) a.ws_lse[split * plane + orow] = lse2;
-    return;
-  }
+  for (int rb = 0; rb < RBW; ++rb) {
+    l[rb] = rowgroup_sum(l[rb]);
+    if (!rvalid[rb]) continue;
+    const float lse2 = l[rb] > 0.f ? m[rb] + fast_log2(l[rb]) : kNegInf;
+    const float f = l[rb] > 0.f ? 1.f / l[rb] : 0.f;
+    if (a.n_splits > 1) {
 #pragma unroll
-  for (int db = 0; db < DB; ++db) {
-    const f32x4 x = o[db] * f;
-    const int c = db * 16 + g4 * 4;
-    if (a.o_bf16) {
-      *reinterpret_cast<u32x2*>(reinterpret_cast<uint16_t*>(a.o) + orow * D + c) =
-          u32x2{pack_bf16x2(x[0], x[1]), pack_bf16x2(x[2], x[3])};
-    } else {
-      *reinterpret_cast<f32x4*>(reinterpret_cast<float*>(a.o) + orow * D + c) = x;
+      for (int db = 0; db < DB; ++db)
+        *reinterpret_cast<f32x4*>(a.ws_o + (split * plane + orow[rb]) * D + db * 16 + g4 * 4) = o[rb][db] * f;
+      if (g4 == 0) a.ws_lse[split * plane + orow[rb]] = lse2;
+      continue;
     }
+#pragma unroll
+    for (int db = 0; db < DB; ++db) {
+      const f32x4 x = o[rb][db] * f;
+      const int c = db * 16 + g4 * 4;
+      if (a.o_bf16) {
+        *reinterpret_cast<u32x2*>(reinterpret_cast<uint16_t*>(a.o) + orow[rb] * D + c) =
+            u32x2{pack_bf16x2(x[0], x[1]), pack_bf16x2(x[2], x[3])};
+      } else {
+        *reinterpret_cast<f32x4*>(reinterpret_cast<float*>(a.o) + orow[rb] * D + c) = x;
+      }
+    }
+    if (g4 == 0 && a.lse) a.lse[orow[rb]] = lse2 * kLn2;
   }
-  if (g4 == 0 && a.lse) a.lse[orow] = lse2 * kLn2;
 }
 
 }  // namespace casc
