@@ -85,6 +85,13 @@ def small_cases():
         "rows_tree": lambda: W.attach_random_trees(
             W.build_workload("rows_tree", [300, 90], [[64], [50]], 32, 2, 128, 16, seed=32), 33),
         "rows_split": lambda: W.build_workload("rows_split", [9000], [[64, 64]], 16, 2, 128, 16, seed=34),
+        # The row-split kernel over 64-token pages: several branches per
+        # request; one long branch whose tokens continue its prefix pages from
+        # slot 600 (not a multiple of 32), read like a prefix in pass B.
+        "rows_page64": lambda: W.build_workload("rows_page64", [1500, 333], [[48, 48, 48], [20] * 5],
+                                                16, 2, 128, 64, seed=35),
+        "rows_suffix_p64": lambda: W.build_workload("rows_suffix_p64", [600], [[200]], 16, 2, 128, 64,
+                                                    seed=36, suffix_in_prefix_pages=True),
     }
 
 
