@@ -72,7 +72,10 @@ rows_kernel(const AttnArgs a) {
   const int per_split = (int)gridDim.x / a.grid_splits;
   const int split = item / per_split;
   item -= split * per_split;
-  const int chunk = item % a.n_chunks;
+  // Pass B is causal: a chunk's keys end at its last token, so later chunks
+  // are longer.  They are handed out longest first, so that the short ones
+  // fill in behind them instead of the long ones forming the launch's tail.
+  const int chunk = kDraft ? a.n_chunks - 1 - item % a.n_chunks : item % a.n_chunks;
   item /= a.n_chunks;
   const int g = item % a.num_kv_heads;
   const int req = item / a.num_kv_heads;
@@ -413,6 +416,8 @@ rows_kernel(const AttnArgs a) {
     }
   };
 
+  // Request token of the wave's first row (its rows' tokens are not smaller).
+  const int wave_tok = (row0 + w * ROWS_W) / a.group;
   // Slot-mode pass B: every row's branch starts at request token 0.
   if (kDraft && slot_mode && tree) {
 #pragma unroll
@@ -440,7 +445,13 @@ rows_kernel(const AttnArgs a) {
       stage(kq[sn], vq[sn], true, stg[(k + 1) & 1]);
       load_tile(t + 1 + DEPTH, pgn, kq[sn], vq[sn]);
       pgn = page_of(t + 2 + DEPTH);
-      if (wave_rows && t < nt) compute(stg[k & 1], p0 + t * 32 - kshift, kend, kind);
+      if (wave_rows && t < nt) {
+        // A slot-mode chain tile that ends at or before the wave's first row
+        // token is visible to all of the wave's rows: no mask.
+        const int tb = p0 + t * 32 - kshift;
+        const bool open = kDraft && slot_mode && !tree && tb >= 0 && tb + 32 <= wave_tok + 1;
+        compute(stg[k & 1], tb, open ? tb + 32 : kend, open ? 0 : kind);
+      }
       __syncthreads();
     }
   }
