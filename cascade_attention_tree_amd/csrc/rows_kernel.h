@@ -361,14 +361,23 @@ rows_kernel(const AttnArgs a) {
     bf16x8 pf[RBW];
 #pragma unroll
     for (int rb = 0; rb < RBW; ++rb) {
-      if (kind == 1) {
+      // One uniform branch per tile picks the rule (tree masks or chains).
+      if (kind == 1 && tree) {
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
             const int key = base + kb * 16 + g4 * 4 + i;
-            const bool vis = (key < end) & (tree ? draft_visible_tree(ranc[rb], rbs[rb], key)
-                                                 : draft_visible(rtok[rb], rbs[rb], key));
+            const bool vis = (key < end) & draft_visible_tree(ranc[rb], rbs[rb], key);
+            s[rb][kb][i] = vis ? s[rb][kb][i] : kNegInf;
+          }
+      } else if (kind == 1) {
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const int key = base + kb * 16 + g4 * 4 + i;
+            const bool vis = (key < end) & draft_visible(rtok[rb], rbs[rb], key);
             s[rb][kb][i] = vis ? s[rb][kb][i] : kNegInf;
           }
       } else if (base + 32 > end) {
