@@ -313,7 +313,8 @@ def fp8_timing(B, W, torch, flush, wl_bf16, t_bf16_ms, steps, warmup, layout):
 def prefix_hit_timings(B, W, torch, flush, steps=5, warmup=2):
     """Prefix-hit suffix prefill (B=4 requests of N=8192 tokens, a hit of
     H = floor(h N)): pass A over the hit, pass B causal over the suffix, merge
-    (three calls), cold protocol.  Reported beside the closed-form work ratio
+    (three calls), cold protocol; and the same split and merge as one fused
+    verify launch (`fused_*`).  Reported beside the closed-form work ratio
     1 - H(H+1)/(N(N+1)) and against the dense bf16 MFMA peak (2.5 PFLOP/s)."""
     out = {}
     base = None
@@ -333,15 +334,21 @@ def prefix_hit_timings(B, W, torch, flush, steps=5, warmup=2):
             B.cascade_draft_attn(x, o_b=ob, lse_b=lb)
             B.merge_state(oa, la, ob, lb, out_dtype=torch.bfloat16, o=o, lse=lse)
 
+        def fused():
+            B.cascade_verify_attn(x, o=o, lse=lse, workspace=ws)
+
         ms, _ = time_steps(step, steps, warmup, flush, torch)
+        ms_f, _ = time_steps(fused, steps, warmup, flush, torch)
         t = float(np.median(ms))
+        t_f = float(np.median(ms_f))
         base = t if base is None else base
         pairs = wl.batch_size * (M * H + M * (M + 1) // 2)           # visible (query, key) pairs per head
         flops = 4.0 * wl.head_dim * wl.num_qo_heads * pairs
         out[f"h{h}"] = {"H": H, "M": M, "median_ms": t, "tflops": flops / (t * 1e-3) / 1e12,
                         "mfma_frac": flops / (t * 1e-3) / 2.5e15,
                         "time_ratio_vs_h0": t / base,
-                        "work_ratio_closed_form": 1.0 - H * (H + 1) / (N * (N + 1))}
+                        "work_ratio_closed_form": 1.0 - H * (H + 1) / (N * (N + 1)),
+                        "fused_median_ms": t_f, "fused_tflops": flops / (t_f * 1e-3) / 1e12}
         del x, ws, oa, la, ob, lb, o, lse
         torch.cuda.empty_cache()
     return out

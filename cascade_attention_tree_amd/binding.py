@@ -255,11 +255,23 @@ def _out_shape(x: DeviceInputs):
     return (R, Hq, d), (R, Hq)
 
 
+def _out(t, shape, dtypes, like):
+    """An output buffer: a new one of dtypes[0], or the caller's, which must have
+    the shape, one of the element types, contiguity and device the kernels write
+    (the C ABI cannot check a buffer's extent)."""
+    if t is None:
+        return torch.empty(shape, dtype=dtypes[0], device=like.device)
+    if tuple(t.shape) != tuple(shape) or t.dtype not in dtypes or not t.is_contiguous() or t.device != like.device:
+        raise ValueError(f"output buffer {tuple(t.shape)} {t.dtype} on {t.device}: expected a contiguous "
+                         f"{tuple(shape)} tensor of {[str(d) for d in dtypes]} on {like.device}")
+    return t
+
+
 def cascade_prefix_attn(x: DeviceInputs, o_a=None, lse_a=None, workspace=None, stream=None):
     """Pass A.  Returns (o_A float32 [R, Hq, d], LSE_A float32 [R, Hq])."""
     so, sl = _out_shape(x)
-    o_a = torch.empty(so, dtype=torch.float32, device=x.q.device) if o_a is None else o_a
-    lse_a = torch.empty(sl, dtype=torch.float32, device=x.q.device) if lse_a is None else lse_a
+    o_a = _out(o_a, so, (torch.float32,), x.q)
+    lse_a = _out(lse_a, sl, (torch.float32,), x.q)
     if workspace is None:
         workspace = workspace_for(x)
     nbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
@@ -272,8 +284,8 @@ def cascade_prefix_attn(x: DeviceInputs, o_a=None, lse_a=None, workspace=None, s
 def cascade_draft_attn(x: DeviceInputs, o_b=None, lse_b=None, stream=None):
     """Pass B.  Returns (o_B float32 [R, Hq, d], LSE_B float32 [R, Hq])."""
     so, sl = _out_shape(x)
-    o_b = torch.empty(so, dtype=torch.float32, device=x.q.device) if o_b is None else o_b
-    lse_b = torch.empty(sl, dtype=torch.float32, device=x.q.device) if lse_b is None else lse_b
+    o_b = _out(o_b, so, (torch.float32,), x.q)
+    lse_b = _out(lse_b, sl, (torch.float32,), x.q)
     _check(lib().cascade_draft_attn(ctypes.byref(x.query), ctypes.byref(x.kv), ctypes.byref(x.tree),
                                     o_b.data_ptr(), lse_b.data_ptr(), _stream(stream)))
     return o_b, lse_b
@@ -289,9 +301,12 @@ def merge_state(o_a, lse_a, o_b, lse_b, out_dtype=torch.float32, o=None, lse=Non
     rows = o_a.numel() // (H * d)
     o = torch.empty(o_a.shape, dtype=out_dtype, device=o_a.device) if o is None else o
     lse = torch.empty(lse_a.shape, dtype=torch.float32, device=o_a.device) if lse is None else lse
+    # The element type written is the one of `o` (a given `o` overrides out_dtype).
+    assert o.dtype in (torch.float32, torch.bfloat16) and o.is_contiguous() and o.numel() == o_a.numel()
+    assert lse.dtype == torch.float32 and lse.is_contiguous() and lse.numel() == lse_a.numel()
     _check(lib().merge_state(o_a.data_ptr(), lse_a.data_ptr(), o_b.data_ptr(), lse_b.data_ptr(),
                              rows, H, d, o.data_ptr(),
-                             CASCADE_BF16 if out_dtype == torch.bfloat16 else CASCADE_F32,
+                             CASCADE_BF16 if o.dtype == torch.bfloat16 else CASCADE_F32,
                              _ptr(lse), _stream(stream)))
     return o, lse
 
@@ -300,9 +315,9 @@ def cascade_verify_attn(x: DeviceInputs, out_dtype=torch.float32, o=None, lse=No
                         stream=None, want_lse=True):
     """Pass A + pass B + merge.  Returns (o [R, Hq, d], LSE float32 [R, Hq] or None)."""
     so, sl = _out_shape(x)
-    o = torch.empty(so, dtype=out_dtype, device=x.q.device) if o is None else o
-    if lse is None and want_lse:
-        lse = torch.empty(sl, dtype=torch.float32, device=x.q.device)
+    o = _out(o, so, (out_dtype, torch.bfloat16 if out_dtype == torch.float32 else torch.float32), x.q)
+    if lse is not None or want_lse:
+        lse = _out(lse, sl, (torch.float32,), x.q)
     if workspace is None:
         workspace = workspace_for(x)
     nbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
@@ -317,9 +332,9 @@ def naive_expand(x: DeviceInputs, out_dtype=torch.float32, o=None, lse=None, str
                  want_lse=True):
     """Baseline: one softmax per branch over prefix + own drafts."""
     so, sl = _out_shape(x)
-    o = torch.empty(so, dtype=out_dtype, device=x.q.device) if o is None else o
-    if lse is None and want_lse:
-        lse = torch.empty(sl, dtype=torch.float32, device=x.q.device)
+    o = _out(o, so, (out_dtype, torch.bfloat16 if out_dtype == torch.float32 else torch.float32), x.q)
+    if lse is not None or want_lse:
+        lse = _out(lse, sl, (torch.float32,), x.q)
     _check(lib().naive_expand(ctypes.byref(x.query), ctypes.byref(x.kv), ctypes.byref(x.tree),
                               o.data_ptr(), CASCADE_BF16 if o.dtype == torch.bfloat16 else CASCADE_F32,
                               _ptr(lse), _stream(stream)))

@@ -34,6 +34,12 @@ namespace casc {
 
 constexpr int kRowWaves = 8;
 
+// Mask kind of a key range, as a type for the key loop.
+template <int K>
+struct KeyKind {
+  static constexpr int value = K;
+};
+
 template <int MODE, int DEPTH, int RBW>
 __global__ void __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2)))
 rows_kernel(const AttnArgs a) {
@@ -112,24 +118,32 @@ rows_kernel(const AttnArgs a) {
   // from the 32-slot boundary at or below ds0; the keys in front of the
   // branch are staged as zeros and masked.  Other requests take their draft
   // tiles through per-key offset tables (the draft phase below).
+  // The fused verify launch streams such a branch the same way after the
+  // prefix (split 0).
   bool slot_mode = false;
   int ds0 = 0;
   int p0 = 0, p1 = 0;
-  if constexpr (kDraft) {
-    const int64_t cap = (int64_t)a.draft_page_table_stride << a.kv.log2_page;
-    if (nb == 1 && cap > 0) {
+  const int64_t dcap = (int64_t)a.draft_page_table_stride << a.kv.log2_page;
+  if (kDraft || (kVerify && split == 0)) {
+    if (nb == 1 && dcap > 0) {
       ds0 = a.draft_start ? as_const(a.draft_start)[jb] : 0;
-      slot_mode = ds0 >= 0 && ds0 < cap;
+      slot_mode = ds0 >= 0 && ds0 < dcap;
     }
+  }
+  // Key range of a slot-mode branch: slots [ds0 & ~31, ds0 + dhi) of its row.
+  auto slot_range = [&](int& q0, int& q1) {
+    int64_t se = (int64_t)ds0 + dhi;
+    if (se > dcap) {
+      if (tid == 0) atomicOr(&g_device_error, kErrPage);
+      se = dcap;
+    }
+    q0 = ds0 & ~31;
+    q1 = (int)se;
+  };
+  if constexpr (kDraft) {
     if (slot_mode) {
       pt_row = as_const(a.draft_page_table + (int64_t)jb * a.draft_page_table_stride);
-      int64_t se = (int64_t)ds0 + dhi;
-      if (se > cap) {
-        if (tid == 0) atomicOr(&g_device_error, kErrPage);
-        se = cap;
-      }
-      p0 = ds0 & ~31;
-      p1 = (int)se;
+      slot_range(p0, p1);
     }
   } else {
   int L = L_in;
@@ -156,12 +170,13 @@ rows_kernel(const AttnArgs a) {
   }
   p0 = __builtin_amdgcn_readfirstlane(p0);
   p1 = __builtin_amdgcn_readfirstlane(p1);
-  const int nt = (p1 - p0 + 31) >> 5;  // tiles of the key loop
+  int nt = (p1 - p0 + 31) >> 5;  // tiles of the key loop
   // Key loop tiles as the mask sees them: prefix keys [p0, p1), or the draft
-  // tokens of a slot-mode branch (slot - ds0, negative in front of it).
-  const int kshift = kDraft ? ds0 : 0;
-  const int kind = kDraft ? 1 : 0;
-  const int kend = kDraft ? dhi : p1;
+  // tokens of a slot-mode branch (slot - ds0, negative in front of it; the
+  // slots in front of the branch are staged as zeros).
+  int kshift = kDraft ? ds0 : 0;
+  int kend = kDraft ? dhi : p1;
+  int front = kDraft ? ds0 : p0;
 
   const KvView kv = a.kv;
   const float c2 = a.scale_log2;
@@ -245,7 +260,7 @@ rows_kernel(const AttnArgs a) {
   }
 
   // ---- tree tables (fused verify split 0, pass B not in slot mode) ---------
-  const bool drafts = (kVerify && split == 0) || (kDraft && !slot_mode);
+  const bool drafts = (kVerify && split == 0 && !slot_mode) || (kDraft && !slot_mode);
   const bool lds_bnd = nb <= NBCAP;
   int dlo = 0;
   Raw dk, dv;  // the first draft tile, requested after the tables
@@ -427,41 +442,69 @@ rows_kernel(const AttnArgs a) {
 
   // Request token of the wave's first row (its rows' tokens are not smaller).
   const int wave_tok = (row0 + w * ROWS_W) / a.group;
-  // Slot-mode pass B: every row's branch starts at request token 0.
-  if (kDraft && slot_mode && tree) {
+  // Slot-mode branches: every row's branch starts at request token 0.
+  if ((kDraft || kVerify) && slot_mode && tree) {
 #pragma unroll
     for (int rb = 0; rb < RBW; ++rb)
       if (rvalid[rb]) ranc[rb] = a.draft_mask[tok0 + rtok[rb]];
   }
-  // Tile 0 into stage 0 (keys in front of a slot-mode branch as zeros); its
-  // slot then requests tile DEPTH.
-  stage(kq[0], vq[0], !kDraft || p0 + skey >= ds0, stg[0]);
-  load_tile(DEPTH, pgn, kq[0], vq[0]);
-  pgn = page_of(DEPTH + 1);
-  __syncthreads();
+  // The key loop over the current key range, its first DEPTH tiles requested:
+  // tile 0 into stage 0 (slots in front of `front` as zeros); its slot then
+  // requests tile DEPTH.
+  // The range's mask kind (0: prefix keys, 1: draft keys) is a compile-time
+  // tag, so each instantiation keeps one masking rule per tile.
   // Step t: stage tile t+1 (slot (t+1) % DEPTH) into stage (t+1) & 1, request
   // tile t+1+DEPTH into that slot, compute tile t out of stage t & 1, barrier.
-  // Tiles past the split are empty ranges: no memory access, zeros staged.
+  // Tiles past the range are empty: no memory access, zeros staged.
   // Whole rings of DEPTH steps, with no exit inside a ring: every back edge
   // then carries the same ring state as the entry, and each stage waits for
   // its own slot only.  Steps past the last tile stage zeros and compute
   // nothing.
-  for (int t0 = 0; t0 < nt; t0 += DEPTH) {
+  auto key_loop = [&](auto kind_tag) {
+    constexpr int KIND = decltype(kind_tag)::value;
+    stage(kq[0], vq[0], p0 + skey >= front, stg[0]);
+    load_tile(DEPTH, pgn, kq[0], vq[0]);
+    pgn = page_of(DEPTH + 1);
+    __syncthreads();
+    for (int t0 = 0; t0 < nt; t0 += DEPTH) {
 #pragma unroll
-    for (int k = 0; k < DEPTH; ++k) {
-      const int t = t0 + k;
-      const int sn = (k + 1) % DEPTH;
-      stage(kq[sn], vq[sn], true, stg[(k + 1) & 1]);
-      load_tile(t + 1 + DEPTH, pgn, kq[sn], vq[sn]);
-      pgn = page_of(t + 2 + DEPTH);
-      if (wave_rows && t < nt) {
-        // A slot-mode chain tile that ends at or before the wave's first row
-        // token is visible to all of the wave's rows: no mask.
-        const int tb = p0 + t * 32 - kshift;
-        const bool open = kDraft && slot_mode && !tree && tb >= 0 && tb + 32 <= wave_tok + 1;
-        compute(stg[k & 1], tb, open ? tb + 32 : kend, open ? 0 : kind);
+      for (int k = 0; k < DEPTH; ++k) {
+        const int t = t0 + k;
+        const int sn = (k + 1) % DEPTH;
+        stage(kq[sn], vq[sn], true, stg[(k + 1) & 1]);
+        load_tile(t + 1 + DEPTH, pgn, kq[sn], vq[sn]);
+        pgn = page_of(t + 2 + DEPTH);
+        if (wave_rows && t < nt) {
+          // A slot-mode chain tile that ends at or before the wave's first
+          // row token is visible to all of the wave's rows: no mask.
+          const int tb = p0 + t * 32 - kshift;
+          const bool open = KIND == 1 && slot_mode && !tree && tb >= 0 && tb + 32 <= wave_tok + 1;
+          compute(stg[k & 1], tb, open ? tb + 32 : kend, open ? 0 : KIND);
+        }
+        __syncthreads();
       }
-      __syncthreads();
+    }
+  };
+  key_loop(KeyKind<kDraft ? 1 : 0>{});
+
+  // ---- fused verify, slot mode: the branch's draft keys as a second range ---
+  if constexpr (kVerify) {
+    if (split == 0 && slot_mode) {
+      pt_row = as_const(a.draft_page_table + (int64_t)jb * a.draft_page_table_stride);
+      slot_range(p0, p1);
+      p0 = __builtin_amdgcn_readfirstlane(p0);
+      p1 = __builtin_amdgcn_readfirstlane(p1);
+      nt = (p1 - p0 + 31) >> 5;
+      kshift = ds0;
+      kend = dhi;
+      front = ds0;
+      pgn = page_of(0);
+#pragma unroll
+      for (int j = 0; j < DEPTH; ++j) {
+        load_tile(j, pgn, kq[j], vq[j]);
+        pgn = page_of(j + 1);
+      }
+      key_loop(KeyKind<1>{});
     }
   }
 

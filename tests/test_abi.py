@@ -182,3 +182,27 @@ def test_fp8_kv_checks():
     kv.head_dim = 96   # a later check still runs: the scales were not the problem
     assert call_verify(q, kv, t) == B.CASCADE_ERR_UNSUPPORTED
     assert b"head_dim" in B.lib().cascade_last_error()
+
+
+def test_binding_rejects_wrong_output_buffers():
+    """A caller's output buffer of the wrong shape, element type or layout is
+    refused before any library call (the C ABI cannot check its extent)."""
+    import torch
+    from cascade_attention_tree_amd import binding as B
+    from cascade_attention_tree_amd import workload as W
+    wl = W.tiny(values="bf16")
+    x = B.to_device(wl, "cpu")
+    R, Hq, d = x.q.shape
+    bad = [torch.empty((R, Hq, d - 1)), torch.empty((R, Hq, d), dtype=torch.float16),
+           torch.empty((R, d, Hq)).transpose(1, 2)]
+    for o in bad:
+        with pytest.raises(ValueError):
+            B.cascade_verify_attn(x, o=o)
+        with pytest.raises(ValueError):
+            B.cascade_prefix_attn(x, o_a=o)
+        with pytest.raises(ValueError):
+            B.cascade_draft_attn(x, o_b=o)
+        with pytest.raises(ValueError):
+            B.naive_expand(x, o=o)
+    with pytest.raises(ValueError):
+        B.cascade_verify_attn(x, lse=torch.empty((R, Hq + 1)))

@@ -277,9 +277,11 @@ def test_prefix_hit_full_sampled(B, h):
     oa, la = B.cascade_prefix_attn(x)
     ob, lb = B.cascade_draft_attn(x)
     o, l = B.merge_state(oa, la, ob, lb)
+    of, lf = B.cascade_verify_attn(x)  # the same split and merge in one launch
     torch.cuda.synchronize()
     r, ro, rl = O.cascade_rows(wl, rows)
     cmp(o, l, ro, rl, rows=r)
+    cmp(of, lf, ro, rl, rows=r)
 
 
 @pytest.mark.parametrize("tree", [False, True])
