@@ -79,9 +79,10 @@ rows_kernel(const AttnArgs a) {
   const int split = item / per_split;
   item -= split * per_split;
   // Pass B is causal: a chunk's keys end at its last token, so later chunks
-  // are longer.  They are handed out longest first, so that the short ones
-  // fill in behind them instead of the long ones forming the launch's tail.
-  const int chunk = kDraft ? a.n_chunks - 1 - item % a.n_chunks : item % a.n_chunks;
+  // are longer (in pass B and in the fused verify).  They are handed out
+  // longest first, so that the short ones fill in behind them instead of the
+  // long ones forming the launch's tail.
+  const int chunk = (kDraft || kVerify) ? a.n_chunks - 1 - item % a.n_chunks : item % a.n_chunks;
   item /= a.n_chunks;
   const int g = item % a.num_kv_heads;
   const int req = item / a.num_kv_heads;
