@@ -92,6 +92,13 @@ def small_cases():
                                                 16, 2, 128, 64, seed=35),
         "rows_suffix_p64": lambda: W.build_workload("rows_suffix_p64", [600], [[200]], 16, 2, 128, 64,
                                                     seed=36, suffix_in_prefix_pages=True),
+        # One branch per request behind a long, key-split prefix: split 0 of
+        # the fused verify launch streams the branch after its prefix keys
+        # while the other splits hold prefix keys only; a chain and a tree.
+        "rows_split_slot": lambda: W.build_workload("rows_split_slot", [9000], [[130]], 16, 2, 128, 16,
+                                                    seed=37),
+        "rows_split_slot_tree": lambda: W.attach_random_trees(
+            W.build_workload("rows_split_slot_tree", [5000, 2100], [[64], [40]], 32, 2, 128, 16, seed=38), 39),
     }
 
 
