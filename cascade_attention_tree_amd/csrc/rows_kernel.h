@@ -1,13 +1,14 @@
-// Row-split attention kernel for the prefix-only launches (pass A and the
+// Row-split attention kernel for row-heavy launches (pass A, pass B and the
 // fused verify pass), head_dim 128, bf16 pools.
 //
 // One workgroup of 8 waves (two per SIMD) handles one work item
-//   (request, kv head g, chunk of at most 128 query rows, key split).
+//   (request, kv head g, chunk of at most kRowsPerItem query rows, key split).
 // The chunk's rows -- the request's query tokens times the query heads that
-// share kv head g -- are dealt out to the 8 waves, at most 16 per wave (one
-// MFMA row block), so every wave keeps its own rows' complete online softmax
-// state and no state is merged across waves.  All 8 waves go through the
-// same 32-key tiles in lock step:
+// share kv head g -- are dealt out to the 8 waves, at most 16 * RBW per wave
+// (RBW MFMA row blocks sharing every K and V fragment the wave reads), so
+// every wave keeps its own rows' complete online softmax state and no state
+// is merged across waves.  All 8 waves go through the same 32-key tiles in
+// lock step:
 //   * each thread loads one 16-byte chunk of K and one of V per tile (the
 //     workgroup's 512 threads cover the 32 keys x 16 chunks of a tile; the 64
 //     lanes of a wave read four whole 256-byte key rows of one page), DEPTH
@@ -21,11 +22,14 @@
 //     updates its rows' base-2 online softmax, and reads V back transposed
 //     (ds_read_b64_tr_b16) for O^T += V^T P^T; P^T stays in the lanes that
 //     computed S^T.
-// In the fused verify launch the request's draft tiles (pass B, under the
+// In the fused verify launch the request's draft keys (pass B, under the
 // in-branch ancestor mask) follow the prefix tiles as further steps of the
 // same online softmax, so passes A and B meet in one state: the merge of the
 // two passes is the online softmax itself (cascade page, splittability: the
-// same LSE identity).
+// same LSE identity).  A request with one branch whose slots lie in its
+// draft-page row streams them through the same ring loop, in pass B and in
+// the fused launch; other requests reach their draft keys through per-key
+// offset tables.
 #pragma once
 
 #include "attn_kernel.h"
