@@ -869,12 +869,9 @@ attn_kernel(const AttnArgs a) {
       for (int db = 0; db < DB; ++db)
 #pragma unroll
         for (int rb = 0; rb < RB; ++rb) o[rb][db] = mfma16(pv_v[db], pv_p[rb], o[rb][db]);
-      // Interleave: one matrix instruction, then a few VALU instructions.
-#pragma unroll
-      for (int i = 0; i < RB * DB; ++i) {
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-        __builtin_amdgcn_sched_group_barrier(0x002, 3, 0);
-      }
+      // The compiler interleaves these matrix instructions with the VALU
+      // work around them: fixed patterns of one MFMA per 2, 3 or 5 VALU
+      // instructions measured 1-2 % slower on the verify kernel.
 #pragma unroll
       for (int rb = 0; rb < RB; ++rb) {
         pv_p[rb] = pf[rb];
