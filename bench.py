@@ -126,28 +126,113 @@ def time_warm(fn, steps, torch):
     return a.elapsed_time(b) / steps
 
 
-def cpu_baseline(wl, kv_bytes, budget_s):
-    """The fp64 oracle (pass A, pass B, merge for every row) on the host, on one
-    thread, repeated over the full batch until `budget_s` of work is done."""
-    from oracle import cascade_oracle as O
+def cpu_info():
+    """Host CPU model (from /proc/cpuinfo) and the number of CPUs this
+    process may run on."""
+    model = "unknown"
     try:
-        from threadpoolctl import threadpool_limits
-        limiter = threadpool_limits(limits=1)
-    except Exception:  # pragma: no cover - threadpoolctl is installed here
-        limiter = None
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    try:
+        n = len(os.sched_getaffinity(0))
+    except AttributeError:  # pragma: no cover
+        n = os.cpu_count() or 1
+    return model, n
+
+
+def _time_oracle(fn, budget_s):
     reps, t0 = 0, time.perf_counter()
     while True:
-        O.cascade(wl)
+        fn()
         reps += 1
         if time.perf_counter() - t0 >= budget_s:
             break
-    dt = (time.perf_counter() - t0) / reps
-    if limiter is not None:
-        limiter.unregister() if hasattr(limiter, "unregister") else None
-    return {"value": kv_bytes / dt / 1e9, "unit": "GB/s", "cores": 1, "kind": "oracle",
-            "sample": f"full headline batch ({wl.total_rows} rows x {wl.num_qo_heads} heads), "
-                      f"{reps} repetitions, {dt:.2f} s each, numpy/BLAS limited to 1 thread",
-            "query_tok_per_s": wl.total_rows / dt}
+    return (time.perf_counter() - t0) / reps, reps
+
+
+def cpu_baseline(wl, kv_bytes, budget_s):
+    """The fp64 oracle (pass A, pass B, merge for every row of the headline
+    batch) on the host, as it stands: once with numpy's BLAS on every CPU the
+    process may use, once limited to one thread, each repeated until
+    `budget_s` seconds of work are done."""
+    from oracle import cascade_oracle as O
+    from threadpoolctl import threadpool_info, threadpool_limits
+    model, ncpu = cpu_info()
+    blas_threads = max([p.get("num_threads", 1) for p in threadpool_info()] + [1])
+    dt_all, reps_all = _time_oracle(lambda: O.cascade(wl), budget_s)
+    with threadpool_limits(limits=1):
+        dt_one, reps_one = _time_oracle(lambda: O.cascade(wl), budget_s)
+    sample = (f"full headline batch ({wl.total_rows} rows x {wl.num_qo_heads} heads, all KV), "
+              f"{reps_all} repetitions of {dt_all:.2f} s with numpy BLAS on {blas_threads} threads")
+    return {"value": kv_bytes / dt_all / 1e9, "unit": "GB/s", "cores": blas_threads, "kind": "oracle",
+            "sample": sample, "query_tok_per_s": wl.total_rows / dt_all, "seconds_per_step": dt_all,
+            "cpu_model": model, "nproc": ncpu,
+            "single_core": {"value": kv_bytes / dt_one / 1e9, "unit": "GB/s", "cores": 1,
+                            "query_tok_per_s": wl.total_rows / dt_one, "seconds_per_step": dt_one,
+                            "sample": f"same batch, {reps_one} repetitions, BLAS limited to 1 thread"}}
+
+
+def gqa_timing(B, W, torch, flush, steps, warmup):
+    """The GQA verify configuration (B=8, Hq=32, Hkv=8, d=128, L=1000, topk=4,
+    S=3, page 16): fused verify, cold protocol, against its HBM roofline
+    (KV + Q + output bytes at 8 TB/s)."""
+    wl = W.gqa()
+    kv_bytes, kv_naive, q_bytes, o_bytes = workload_bytes(wl)
+    x = B.to_device(wl, "cuda", layout="HND")
+    ws = B.workspace_for(x)
+    o = torch.empty(wl.q.shape, dtype=torch.bfloat16, device="cuda")
+    lse = torch.empty(wl.q.shape[:2], dtype=torch.float32, device="cuda")
+
+    def verify():
+        B.cascade_verify_attn(x, o=o, lse=lse, workspace=ws)
+
+    def naive():
+        B.naive_expand(x, o=o, lse=lse)
+
+    ms, _ = time_steps(verify, steps, warmup, flush, torch)
+    k_ms = time_kernel(verify, steps, flush, B)
+    ms_n, _ = time_steps(naive, steps, warmup, flush, torch)
+    t, kt = float(np.median(ms)), float(np.median(k_ms))
+    compulsory = kv_bytes + q_bytes + o_bytes
+    t_roof = compulsory / (HBM_PEAK_GBS * 1e9)
+    out = {"workload": "GQA verify: B=8, Hq=32, Hkv=8, d=128, L=1000, topk=4, S=3, page 16, HND",
+           "median_ms": t, "kernel_median_ms": kt, "kernel_mean_ms": float(np.mean(k_ms)),
+           "kv_GBps": kv_bytes / (t * 1e-3) / 1e9, "query_tok_per_s": wl.total_rows / (t * 1e-3),
+           "roofline_ms": t_roof * 1e3, "roofline_frac_kernel": t_roof / (kt * 1e-3),
+           "split_prefix": ws is not None, "naive_median_ms": float(np.median(ms_n)),
+           "speedup_vs_naive": float(np.median(ms_n)) / t}
+    del x, ws, o, lse
+    torch.cuda.empty_cache()
+    return out
+
+
+def layout_timing(B, W, torch, flush, wl, layout, steps, warmup):
+    """The headline verify with the pool in another page layout (same logical
+    content): event-timed step and the kernel's own time."""
+    kv_bytes, _, q_bytes, o_bytes = workload_bytes(wl)
+    x = B.to_device(wl, "cuda", layout=layout)
+    ws = B.workspace_for(x)
+    o = torch.empty(wl.q.shape, dtype=torch.bfloat16, device="cuda")
+    lse = torch.empty(wl.q.shape[:2], dtype=torch.float32, device="cuda")
+
+    def verify():
+        B.cascade_verify_attn(x, o=o, lse=lse, workspace=ws)
+
+    ms, _ = time_steps(verify, steps, warmup, flush, torch)
+    k_ms = time_kernel(verify, steps, flush, B)
+    t, kt = float(np.mean(ms)), float(np.mean(k_ms))
+    compulsory = kv_bytes + q_bytes + o_bytes
+    out = {"page_layout": layout, "ms_per_step": t, "median_ms": float(np.median(ms)),
+           "kv_GBps": kv_bytes / (t * 1e-3) / 1e9, "query_tok_per_s": wl.total_rows / (t * 1e-3),
+           "kernel_ms": kt, "roofline_frac": compulsory / (kt * 1e-3) / 1e9 / HBM_PEAK_GBS}
+    del x, ws, o, lse
+    torch.cuda.empty_cache()
+    return out
 
 
 def ragged_timing(B, W, torch, flush, steps=10, warmup=3):
@@ -360,7 +445,7 @@ def main():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--only-verify", action="store_true", help="time only the fused verify call")
     ap.add_argument("--layout", choices=("HND", "NHD"), default="HND",
                     help="page layout of the KV pool on the device (same logical content)")
@@ -518,6 +603,12 @@ def main():
         sr = streaming_read_GBps(B, torch)
         line["streaming_read_GBps"] = sr
         line["pct_streaming_read"] = 100.0 * kv_gbs / sr
+    if not args.only_verify:
+        other = "NHD" if args.layout == "HND" else "HND"
+        print(f"bench: timing the headline verify with {other} pages", file=sys.stderr, flush=True)
+        line["other_layout"] = layout_timing(B, W, torch, flush, wl, other, args.steps, args.warmup)
+        print("bench: timing the GQA verify configuration", file=sys.stderr, flush=True)
+        line["gqa"] = gqa_timing(B, W, torch, flush, args.steps, args.warmup)
     if not args.no_ragged and not args.only_verify:
         print("bench: timing the ragged configuration", file=sys.stderr, flush=True)
         line["ragged"] = ragged_timing(B, W, torch, flush)

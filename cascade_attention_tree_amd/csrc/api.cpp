@@ -66,7 +66,8 @@ void plan_rows(Plan& p, int64_t rows_per_segment) {
 void plan_splits(Plan& p, int max_len) {
   const int len = max_len > 0 ? max_len : 1;
   int64_t n = 1;
-  if (len > 2 * kMinSplitKeys && p.items < kTargetItems) {
+  // An empty launch (no requests) has no items to fill the device with.
+  if (len > 2 * kMinSplitKeys && p.items > 0 && p.items < kTargetItems) {
     n = cdiv(kTargetItems, p.items);
     const int64_t cap = cdiv(len, kMinSplitKeys);
     if (n > cap) n = cap;
@@ -139,7 +140,11 @@ cascade_status check_query(const cascade_query* q, const cascade_paged_kv* kv) {
   if (q->row_stride % 8 || q->head_stride % 8)
     return fail(CASCADE_ERR_UNSUPPORTED, "q strides must be multiples of 8 elements");
   if (q->q && !aligned16(q->q)) return fail(CASCADE_ERR_UNSUPPORTED, "q must be 16-byte aligned");
-  if (!std::isfinite(q->sm_scale)) return fail(CASCADE_ERR_SHAPE, "sm_scale must be finite");
+  // The kernels take the running row max over raw scores and scale it
+  // afterwards, which is the max of the scaled scores only for a positive
+  // scale; a zero scale would also turn masked (-inf) scores into NaN.
+  if (!std::isfinite(q->sm_scale) || !(q->sm_scale > 0.f))
+    return fail(CASCADE_ERR_SHAPE, "sm_scale must be finite and > 0");
   return CASCADE_OK;
 }
 
@@ -487,6 +492,7 @@ cascade_status cascade_debug_gather(const cascade_paged_kv* kv, const cascade_tr
   casc::DebugArgs a{};
   a.kv = kv_view(kv);
   a.head_dim = kv->head_dim;
+  a.num_kv_heads = kv->num_kv_heads;
   a.batch_size = t->batch_size;
   a.page_table = t->page_table;
   a.page_table_stride = t->page_table_stride;

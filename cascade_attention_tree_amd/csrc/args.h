@@ -121,6 +121,7 @@ struct CommitArgs {
 struct DebugArgs {
   KvView kv;
   int32_t head_dim;
+  int32_t num_kv_heads;
   int32_t batch_size;
   const int32_t* page_table;
   int32_t page_table_stride;

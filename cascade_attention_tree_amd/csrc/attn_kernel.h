@@ -277,7 +277,6 @@ attn_kernel(const AttnArgs a) {
 
   const KvView kv = a.kv;
   const float c2 = a.scale_log2;
-  const int pmask = (1 << kv.log2_page) - 1;
   const int64_t head_off = (int64_t)g * kv.head_stride;
   // Segment tokens of this chunk's rows, and the draft keys [dlo, dhi) they
   // can see (dlo, the start of the first row's branch, is set below).
@@ -331,21 +330,15 @@ attn_kernel(const AttnArgs a) {
   constexpr int NV = 16 / TPI;
   int lane_off[NV];
 #pragma unroll
-  for (int i = 0; i < NV; ++i)
-    lane_off[i] = (int)(((int64_t)(i * TPI + lane / CPR) * kv.token_stride + head_off + (lane % CPR) * 8) * EB);
-  const unsigned char* const k_bytes = reinterpret_cast<const unsigned char*>(kv.k);
-  const unsigned char* const v_bytes = reinterpret_cast<const unsigned char*>(kv.v);
+  for (int i = 0; i < NV; ++i) lane_off[i] = prefix_lane_offset<EB>(kv, i * TPI + lane / CPR, head_off, lane % CPR);
   auto load_rows = [&](const int (&pg)[2], int base, int end, Raw (&kr)[NI], Raw (&vr)[NI]) {
     __amdgpu_buffer_rsrc_t rk[2], rv[2];
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
       const int first = base + kb * 16;
       const int nvalid = min(max(end - first, 0), 16);
-      const bool ok = pg[kb] >= 0 && nvalid > 0;
-      const int64_t hbase = (int64_t)(ok ? pg[kb] : 0) * kv.page_stride + (int64_t)(first & pmask) * kv.token_stride;
-      const int bytes = ok ? (int)(((int64_t)(nvalid - 1) * kv.token_stride + head_off + D) * EB) : 0;
-      rk[kb] = page_rsrc(k_bytes + hbase * EB, bytes);
-      rv[kb] = page_rsrc(v_bytes + hbase * EB, bytes);
+      rk[kb] = prefix_half_rsrc<EB>(kv.k, kv, pg[kb], first, nvalid, head_off, D);
+      rv[kb] = prefix_half_rsrc<EB>(kv.v, kv, pg[kb], first, nvalid, head_off, D);
     }
 #pragma unroll
     for (int n = 0; n < NI; ++n) {
@@ -358,8 +351,7 @@ attn_kernel(const AttnArgs a) {
     if (id >= kv.num_pages) {
       if (lane == 0) atomicOr(&g_device_error, kErrPage);
     }
-    if ((uint32_t)id >= (uint32_t)kv.num_pages) id = -1;
-    return __builtin_amdgcn_readfirstlane(id);  // uniform by construction
+    return __builtin_amdgcn_readfirstlane(checked_page(id, kv.num_pages));  // uniform by construction
   };
   auto prefix_pages = [&](int base, int end, int (&pg)[2]) {
 #pragma unroll
@@ -486,13 +478,7 @@ attn_kernel(const AttnArgs a) {
         const int x = dlo + t;
         const int jl = branch_at(x);
         const int slot = branch_dstart(jl) + (x - branch_start(jl));
-        int64_t off = -1;
-        if (slot >= 0 && (slot >> kv.log2_page) < dstride) {
-          const int page = a.draft_page_table[(int64_t)(jb + jl) * dstride + (slot >> kv.log2_page)];
-          if ((uint32_t)page < (uint32_t)kv.num_pages)
-            off = (int64_t)page * kv.page_stride + (int64_t)(slot & pmask) * kv.token_stride;
-        }
-        t_doff[t] = off;
+        t_doff[t] = draft_slot_offset(kv, a.draft_page_table + (int64_t)(jb + jl) * dstride, dstride, slot);
       }
     }
     if constexpr (kWaveTables) wave_lds_sync();  // t_rbs and t_doff before the draft wave reads them
@@ -553,6 +539,7 @@ attn_kernel(const AttnArgs a) {
   // Lanes without a key load nothing (all such lanes of all workgroups would
   // otherwise hit one row) and hold zeros; their K is masked later and their
   // V is zero (bit kb of `ok` also zeroes it when staged).
+  const int64_t last_row = pool_last_row(kv, a.num_kv_heads);
   auto load_draft_at = [&](const int64_t (&off)[2], Raw (&kr)[NI], Raw (&vr)[NI], int& ok) {
     ok = 0;
 #pragma unroll
@@ -560,11 +547,11 @@ attn_kernel(const AttnArgs a) {
       const bool valid = off[kb] >= 0;
       ok |= valid ? (1 << kb) : 0;
       if (valid) {
-        const int64_t o2 = off[kb] + g4 * 8;
+        const int64_t o2 = clamp_row(off[kb], last_row) + g4 * 8;
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks) {
-          kr[kb * KS + ks] = *reinterpret_cast<const Raw*>(k_bytes + (o2 + ks * 32) * EB);
-          vr[kb * KS + ks] = *reinterpret_cast<const Raw*>(v_bytes + (o2 + ks * 32) * EB);
+          kr[kb * KS + ks] = load_key_chunk<Raw, EB>(kv.k, o2 + ks * 32);
+          vr[kb * KS + ks] = load_key_chunk<Raw, EB>(kv.v, o2 + ks * 32);
         }
       } else {
 #pragma unroll

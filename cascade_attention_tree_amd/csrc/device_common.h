@@ -91,6 +91,19 @@ __device__ __forceinline__ bool draft_visible_tree(uint64_t anc, int bs, int kt)
   return (u >= 0) & (u < 64) & (((anc >> (u & 63)) & 1ull) != 0ull);
 }
 
+// Element offset (kv head excluded) of logical slot `slot` of draft
+// block-table row `row` (`stride` entries), or -1 when the slot lies outside
+// the row or its page id outside the pool.  The draft-key tables of the
+// attention kernels, the draft gather hook and the serving-step writes all
+// resolve draft slots through this function.
+__device__ __forceinline__ int64_t draft_slot_offset(const KvView& kv, const int32_t* row, int32_t stride,
+                                                     int32_t slot) {
+  if (slot < 0 || (slot >> kv.log2_page) >= stride) return -1;
+  const int32_t page = row[slot >> kv.log2_page];
+  if ((uint32_t)page >= (uint32_t)kv.num_pages) return -1;
+  return (int64_t)page * kv.page_stride + (int64_t)(slot & ((1 << kv.log2_page) - 1)) * kv.token_stride;
+}
+
 // Physical offset of draft token `kt` (numbered from the first row of branch
 // jb) of kv head g.  Branch j's token u is at logical slot draft_start[j] + u
 // of draft block-table row j (dstride entries).  -1 when the slot lies past
@@ -103,8 +116,20 @@ __device__ __forceinline__ int64_t draft_offset(const KvView& kv, const int32_t*
   const int j = branch_of_row(qo, jb, je, row);
   const int u = row - qo[j];
   const int slot = (dstart ? dstart[j] : 0) + u;
-  if (slot < 0 || (slot >> kv.log2_page) >= dstride) return -1;
-  return paged_offset(kv, dpt + (int64_t)j * dstride, slot, g);
+  const int64_t off = draft_slot_offset(kv, dpt + (int64_t)j * dstride, dstride, slot);
+  return off < 0 ? -1 : off + (int64_t)g * kv.head_stride;
+}
+
+// Largest element offset at which a whole key row of one kv head starts
+// inside the pool.  A draft-key load clamps its offset to [0, this], so even
+// an offset read from a table entry that was never written stays inside the
+// pool (it reads a wrong row, never an unmapped address).
+__device__ __forceinline__ int64_t pool_last_row(const KvView& kv, int num_kv_heads) {
+  return (int64_t)(kv.num_pages - 1) * kv.page_stride + (int64_t)((1 << kv.log2_page) - 1) * kv.token_stride +
+         (int64_t)(num_kv_heads - 1) * kv.head_stride;
+}
+__device__ __forceinline__ int64_t clamp_row(int64_t off, int64_t last) {
+  return off < 0 ? 0 : (off > last ? last : off);
 }
 
 // Buffer descriptor over a byte range (gfx9-family raw buffer: stride 0,
@@ -122,6 +147,36 @@ __device__ __forceinline__ u32x2 buf_load8(__amdgpu_buffer_rsrc_t r, int byte_of
   return __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(r, byte_off, 0, 0));
 }
 
+// Prefix tiles start at multiples of 32 slots and pages hold >= 16 tokens,
+// so each 16-key half of a tile lies in one page.  The half's buffer
+// descriptor starts at its first key's row (slot `first` of page `page`, kv
+// head at element offset `head_off`) and ends after the row of its last valid
+// key (`nvalid` keys), so lanes addressing keys past the end -- and every key
+// of a half whose page id is -1 (none, or outside the pool) -- read zeros.
+// EB is the pool's element size in bytes, D the head dim.  The attention
+// kernels and the prefix gather hook build their prefix loads from these two
+// functions.
+template <int EB>
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t prefix_half_rsrc(const void* pool, const KvView& kv, int page,
+                                                                   int first, int nvalid, int64_t head_off,
+                                                                   int D) {
+  const bool ok = page >= 0 && nvalid > 0;
+  const int64_t base = (int64_t)(ok ? page : 0) * kv.page_stride +
+                       (int64_t)(first & ((1 << kv.log2_page) - 1)) * kv.token_stride;
+  const int bytes = ok ? (int)(((int64_t)(nvalid - 1) * kv.token_stride + head_off + D) * EB) : 0;
+  return page_rsrc(static_cast<const unsigned char*>(pool) + base * EB, bytes);
+}
+// Byte offset, inside its half's descriptor, of 8-channel chunk `chunk` of
+// the key `key` places after the half's first key.
+template <int EB>
+__device__ __forceinline__ int prefix_lane_offset(const KvView& kv, int key, int64_t head_off, int chunk) {
+  return (int)(((int64_t)key * kv.token_stride + head_off + chunk * 8) * EB);
+}
+// A block-table entry as a page id: -1 for ids outside [0, num_pages).
+__device__ __forceinline__ int checked_page(int id, int num_pages) {
+  return (uint32_t)id < (uint32_t)num_pages ? id : -1;
+}
+
 // Eight consecutive K or V channels as they sit in the pool: eight bf16
 // values (16 bytes), or eight FP8 E4M3 codes (8 bytes; KV-cache page,
 // section 4.5 -- FP8 KV with a per-tensor scale).
@@ -133,6 +188,14 @@ __device__ __forceinline__ u32x4 buf_load_chunk(__amdgpu_buffer_rsrc_t r, int by
 }
 __device__ __forceinline__ u32x2 buf_load_chunk(__amdgpu_buffer_rsrc_t r, int byte_off, u32x2*) {
   return buf_load8(r, byte_off);
+}
+
+// One chunk of eight channels at element offset `elem_off` of a pool (the
+// draft-key loads, whose keys resolve their rows one by one; the offset is
+// clamped into the pool by the caller).
+template <typename Raw, int EB>
+__device__ __forceinline__ Raw load_key_chunk(const void* pool, int64_t elem_off) {
+  return *reinterpret_cast<const Raw*>(static_cast<const unsigned char*>(pool) + elem_off * EB);
 }
 
 // The eight channels as bf16.  E4M3 (1 sign, 4 exponent bits with bias 7,

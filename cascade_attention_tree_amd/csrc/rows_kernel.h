@@ -185,7 +185,6 @@ rows_kernel(const AttnArgs a) {
 
   const KvView kv = a.kv;
   const float c2 = a.scale_log2;
-  const int pmask = (1 << kv.log2_page) - 1;
   const int64_t head_off = (int64_t)g * kv.head_stride;
 
   // ---- this lane's rows: wave w holds chunk rows [ROWS_W w, ROWS_W (w+1)) --
@@ -219,9 +218,7 @@ rows_kernel(const AttnArgs a) {
   // end after the row of its last valid key, so keys past `p1` (and bad pages)
   // read zeros.
   const int half = w >> 2;
-  const int lane_off = (int)((((int64_t)((w & 3) * 4 + g4) * kv.token_stride) + head_off + l16 * 8) * EB);
-  const unsigned char* const k_bytes = reinterpret_cast<const unsigned char*>(kv.k);
-  const unsigned char* const v_bytes = reinterpret_cast<const unsigned char*>(kv.v);
+  const int lane_off = prefix_lane_offset<EB>(kv, (w & 3) * 4 + g4, head_off, l16);
   // Page ids outside the pool are noted here and flagged once at the end: a
   // store in the key loop would count on the same counter as the K/V loads
   // and blur the loop's wait counts.
@@ -231,16 +228,13 @@ rows_kernel(const AttnArgs a) {
     int id = first < p1 ? pt_row[first >> kv.log2_page] : -1;
     id = __builtin_amdgcn_readfirstlane(id);
     bad_page |= id >= kv.num_pages;
-    return (uint32_t)id < (uint32_t)kv.num_pages ? id : -1;
+    return checked_page(id, kv.num_pages);
   };
   auto load_tile = [&](int tile, int pg, Raw& kr, Raw& vr) {
     const int first = p0 + tile * 32 + half * 16;
     const int nvalid = min(max(p1 - first, 0), 16);
-    const bool ok = pg >= 0 && nvalid > 0;
-    const int64_t hbase = (int64_t)(ok ? pg : 0) * kv.page_stride + (int64_t)(first & pmask) * kv.token_stride;
-    const int bytes = ok ? (int)(((int64_t)(nvalid - 1) * kv.token_stride + head_off + D) * EB) : 0;
-    kr = buf_load_chunk(page_rsrc(k_bytes + hbase * EB, bytes), lane_off, (Raw*)nullptr);
-    vr = buf_load_chunk(page_rsrc(v_bytes + hbase * EB, bytes), lane_off, (Raw*)nullptr);
+    kr = buf_load_chunk(prefix_half_rsrc<EB>(kv.k, kv, pg, first, nvalid, head_off, D), lane_off, (Raw*)nullptr);
+    vr = buf_load_chunk(prefix_half_rsrc<EB>(kv.v, kv, pg, first, nvalid, head_off, D), lane_off, (Raw*)nullptr);
   };
   // Thread tid's chunk of a tile into a stage (zeros where `keep` is false).
   const int skey = tid >> 4, sch = tid & 15;
@@ -285,6 +279,7 @@ rows_kernel(const AttnArgs a) {
   auto branch_dstart = [&](int jl) {
     return lds_bnd ? t_dst[jl] : (a.draft_start ? a.draft_start[jb + jl] : 0);
   };
+  const int64_t last_row = pool_last_row(kv, a.num_kv_heads);
   // Key base + tid / 16 of a draft tile (request tokens), chunk tid % 16;
   // zeros for keys past dhi and for bad slots or pages (flagged).
   auto load_draft = [&](int base, Raw& kr, Raw& vr, bool& keep) {
@@ -301,9 +296,9 @@ rows_kernel(const AttnArgs a) {
       if (off == -1) atomicOr(&g_device_error, kErrPage);
     }
     keep = off >= 0;
-    const int64_t e = (keep ? off : 0) + sch * 8;
-    kr = keep ? *reinterpret_cast<const Raw*>(k_bytes + e * EB) : Raw{};
-    vr = keep ? *reinterpret_cast<const Raw*>(v_bytes + e * EB) : Raw{};
+    const int64_t e = clamp_row(off, last_row) + sch * 8;
+    kr = keep ? load_key_chunk<Raw, EB>(kv.k, e) : Raw{};
+    vr = keep ? load_key_chunk<Raw, EB>(kv.v, e) : Raw{};
   };
   if constexpr (kTables) {
     if (drafts) {
@@ -320,13 +315,7 @@ rows_kernel(const AttnArgs a) {
         const int x = dlo + t;
         const int jl = branch_at(x);
         const int slot = branch_dstart(jl) + (x - branch_start(jl));
-        int64_t off = -1;
-        if (slot >= 0 && (slot >> kv.log2_page) < dstride) {
-          const int page = a.draft_page_table[(int64_t)(jb + jl) * dstride + (slot >> kv.log2_page)];
-          if ((uint32_t)page < (uint32_t)kv.num_pages)
-            off = (int64_t)page * kv.page_stride + (int64_t)(slot & pmask) * kv.token_stride;
-        }
-        t_doff[t] = off;
+        t_doff[t] = draft_slot_offset(kv, a.draft_page_table + (int64_t)(jb + jl) * dstride, dstride, slot);
       }
       __syncthreads();
       load_draft(dlo, dk, dv, dkeep);

@@ -40,38 +40,64 @@ __global__ void __launch_bounds__(256) merge_state_kernel(const MergeArgs a) {
   if (c == 0 && a.lse) a.lse[r] = lse;
 }
 
-// Copies `count` tokens of one kv head through the same address helpers the
-// attention kernels use: which == 0, the prefix of request `index`
-// (paged_offset on its block-table row); which == 1, the drafts of branch
-// `index` (draft_offset).  FP8 codes are widened to bf16 by the conversion
-// the attention kernels stage with.  One thread per 8 channels of one token.
-__global__ void __launch_bounds__(256) debug_gather_kernel(const DebugArgs a) {
-  const int c8 = a.head_dim >> 3;
-  const int idx = blockIdx.x * blockDim.x + threadIdx.x;
-  if (idx >= a.count * c8) return;
-  const int t = idx / c8;
-  const int c = (idx - t * c8) * 8;
-  int64_t off;
+// Copies `count` tokens of one kv head with the gather functions of the
+// attention kernels.  which == 0, the prefix of request `index`: the token's
+// 16-key half gets its page id from the block-table row (checked_page) and
+// its buffer descriptor from prefix_half_rsrc, and the chunk is read at
+// prefix_lane_offset -- the prefix tile loads of both attention kernels.
+// which == 1, the drafts of branch `index`: the slot resolves through
+// draft_slot_offset, the offset is clamped into the pool and the chunk read
+// by load_key_chunk -- the draft-key tables and loads of both kernels.  FP8
+// codes are widened to bf16 by the conversion the kernels stage with.  One
+// thread per 8 channels of one token; tokens whose page id (or slot) is bad
+// read zeros and raise the sticky flag.
+template <int EB>
+__device__ __forceinline__ void debug_gather_token(const DebugArgs& a, int t, int c8) {
+  typedef typename KvChunk<EB == 1>::T Raw;
+  const KvView& kv = a.kv;
+  const int64_t head_off = (int64_t)a.kv_head * kv.head_stride;
+  Raw k = {}, v = {};
+  bool bad = false;
   if (a.which == 0) {
-    off = (t >> a.kv.log2_page) < a.page_table_stride
-              ? paged_offset(a.kv, a.page_table + (int64_t)a.index * a.page_table_stride, t, a.kv_head)
-              : -1;
+    const int32_t* pt_row = a.page_table + (int64_t)a.index * a.page_table_stride;
+    const int cap = a.page_table_stride << kv.log2_page;
+    const int end = a.count < cap ? a.count : cap;
+    const int first = t & ~15;
+    const int id = first < end ? pt_row[first >> kv.log2_page] : -1;
+    const int pg = checked_page(id, kv.num_pages);
+    const int nvalid = min(max(end - first, 0), 16);
+    const int off = prefix_lane_offset<EB>(kv, t - first, head_off, c8);
+    k = buf_load_chunk(prefix_half_rsrc<EB>(kv.k, kv, pg, first, nvalid, head_off, a.head_dim), off, (Raw*)nullptr);
+    v = buf_load_chunk(prefix_half_rsrc<EB>(kv.v, kv, pg, first, nvalid, head_off, a.head_dim), off, (Raw*)nullptr);
+    bad = pg < 0 || t >= end;
   } else {
-    off = draft_offset(a.kv, a.branch_qo_indptr, a.draft_page_table, a.draft_page_table_stride,
-                       a.draft_start, a.index, a.index + 1, t, a.kv_head);
+    const int j = a.index;
+    const int slot = (a.draft_start ? a.draft_start[j] : 0) + t;
+    const int64_t off = draft_slot_offset(kv, a.draft_page_table + (int64_t)j * a.draft_page_table_stride,
+                                          a.draft_page_table_stride, slot);
+    bad = off < 0;
+    if (!bad) {
+      const int64_t e = clamp_row(off + head_off, pool_last_row(kv, a.num_kv_heads)) + c8 * 8;
+      k = load_key_chunk<Raw, EB>(kv.k, e);
+      v = load_key_chunk<Raw, EB>(kv.v, e);
+    }
   }
-  u32x4 k = {0u, 0u, 0u, 0u}, v = {0u, 0u, 0u, 0u};
-  if (off >= 0 && a.kv.elem_bytes == 1) {
-    k = widen_bf16(*reinterpret_cast<const u32x2*>(reinterpret_cast<const unsigned char*>(a.kv.k) + off + c));
-    v = widen_bf16(*reinterpret_cast<const u32x2*>(reinterpret_cast<const unsigned char*>(a.kv.v) + off + c));
-  } else if (off >= 0) {
-    k = *reinterpret_cast<const u32x4*>(a.kv.k + off + c);
-    v = *reinterpret_cast<const u32x4*>(a.kv.v + off + c);
+  if (bad) atomicOr(&g_device_error, kErrPage);
+  *reinterpret_cast<u32x4*>(a.k_out + (int64_t)t * a.head_dim + c8 * 8) = widen_bf16(k);
+  *reinterpret_cast<u32x4*>(a.v_out + (int64_t)t * a.head_dim + c8 * 8) = widen_bf16(v);
+}
+
+__global__ void __launch_bounds__(256) debug_gather_kernel(const DebugArgs a) {
+  const int c8n = a.head_dim >> 3;
+  const int idx = blockIdx.x * blockDim.x + threadIdx.x;
+  if (idx >= a.count * c8n) return;
+  const int t = idx / c8n;
+  const int c8 = idx - t * c8n;
+  if (a.kv.elem_bytes == 1) {
+    debug_gather_token<1>(a, t, c8);
   } else {
-    atomicOr(&g_device_error, kErrPage);
+    debug_gather_token<2>(a, t, c8);
   }
-  *reinterpret_cast<u32x4*>(a.k_out + (int64_t)t * a.head_dim + c) = k;
-  *reinterpret_cast<u32x4*>(a.v_out + (int64_t)t * a.head_dim + c) = v;
 }
 
 // Branch `index`'s visibility over [its request's prefix ; its drafts]:
@@ -145,36 +171,83 @@ __global__ void __launch_bounds__(256) append_kv_kernel(const AppendArgs a) {
 }
 
 // Commit: the k-th accepted row of request i has its draft K/V copied to
-// logical slot L_i + k of block-table row i.  One group of 16 lanes per
-// (request, k, kv head); groups past the request's accepted count return.
+// logical slot L_i + k of block-table row i.  One workgroup per (request, kv
+// head) walks the request's accepted rows in path order, 16 rows per round,
+// one group of 16 lanes per row: every row of a round is read into registers
+// before any row of that round is written, and rounds follow each other.  So
+// a destination may be the draft slot of the same or an earlier row of the
+// path -- the usual layout when drafts continue the prefix pages and the
+// accepted path skips nodes: destination L_i + k, source L_i + path[k] with
+// path[k] >= k -- and every row still copies the value it had before the
+// commit.
+constexpr int kCommitRowsPerRound = 16;
+
+__device__ __forceinline__ int copy_chunks(int head_dim, int elem_bytes) {
+  return head_dim * elem_bytes / (elem_bytes == 2 ? 16 : 8);
+}
+
 __global__ void __launch_bounds__(256) commit_kernel(const CommitArgs a) {
-  const int64_t item = ((int64_t)blockIdx.x * blockDim.x + threadIdx.x) >> 4;
+  const int i = blockIdx.x / a.num_kv_heads;
+  const int g = blockIdx.x - i * a.num_kv_heads;
+  const int grp = threadIdx.x >> 4;
   const int lane = threadIdx.x & 15;
-  const int64_t per_req = (int64_t)a.max_accepted * a.num_kv_heads;
-  if (item >= (int64_t)a.batch_size * per_req) return;
-  const int i = (int)(item / per_req);
-  const int rem = (int)(item - (int64_t)i * per_req);
-  const int k = rem / a.num_kv_heads;
-  const int g = rem - k * a.num_kv_heads;
   const int a0 = a.accepted_indptr[i];
-  if (k >= a.accepted_indptr[i + 1] - a0) return;
-  const int r = a.accepted_rows[a0 + k];
-  bool ok = r >= 0 && r < a.total_rows;
-  int64_t src = -1, dst = -1;
-  if (ok) {
-    src = draft_offset(a.kv, a.branch_qo_indptr, a.draft_page_table, a.draft_page_table_stride,
-                       a.draft_start, 0, a.num_branches, r, g);
-    const int slot = a.cache_seqlens[i] + k;
-    if (slot >= 0 && (slot >> a.kv.log2_page) < a.page_table_stride)
-      dst = paged_offset(a.kv, a.page_table + (int64_t)i * a.page_table_stride, slot, g);
-    ok = src >= 0 && dst >= 0;
+  const int count = a.accepted_indptr[i + 1] - a0;
+  const int L = a.cache_seqlens[i];
+  const bool fp8 = a.kv.elem_bytes == 1;
+  const int nchunk = copy_chunks(a.head_dim, a.kv.elem_bytes);  // 16 for every supported case
+  unsigned char* kp = reinterpret_cast<unsigned char*>(const_cast<uint16_t*>(a.kv.k));
+  unsigned char* vp = reinterpret_cast<unsigned char*>(const_cast<uint16_t*>(a.kv.v));
+  const int cbytes = fp8 ? 8 : 16;
+  for (int base = 0; base < count; base += kCommitRowsPerRound) {
+    const int k = base + grp;
+    int64_t src = -1, dst = -1;
+    int err = 0;
+    if (k < count) {
+      const int r = a.accepted_rows[a0 + k];
+      if (r >= 0 && r < a.total_rows) {
+        src = draft_offset(a.kv, a.branch_qo_indptr, a.draft_page_table, a.draft_page_table_stride,
+                           a.draft_start, 0, a.num_branches, r, g);
+        const int slot = L + k;
+        if (slot >= 0 && (slot >> a.kv.log2_page) < a.page_table_stride)
+          dst = paged_offset(a.kv, a.page_table + (int64_t)i * a.page_table_stride, slot, g);
+        if (src < 0 || dst < 0) err = kErrPage;
+      } else {
+        err = kErrRow;
+      }
+      if (err && lane == 0) atomicOr(&g_device_error, err);
+    }
+    const bool ok = k < count && err == 0;
+    // Read phase: this group's row (chunk `lane` of K and of V).
+    u32x4 kr = {0u, 0u, 0u, 0u}, vr = {0u, 0u, 0u, 0u};
+    if (ok && lane < nchunk) {
+      const int64_t off = src * a.kv.elem_bytes + lane * cbytes;
+      if (fp8) {
+        const u32x2 k8 = *reinterpret_cast<const u32x2*>(kp + off);
+        const u32x2 v8 = *reinterpret_cast<const u32x2*>(vp + off);
+        kr = u32x4{k8[0], k8[1], 0u, 0u};
+        vr = u32x4{v8[0], v8[1], 0u, 0u};
+      } else {
+        kr = *reinterpret_cast<const u32x4*>(kp + off);
+        vr = *reinterpret_cast<const u32x4*>(vp + off);
+      }
+    }
+    // The loaded values are in registers before any lane passes the barrier.
+    asm volatile("" : "+v"(kr), "+v"(vr));
+    __syncthreads();
+    if (ok && lane < nchunk) {
+      const int64_t off = dst * a.kv.elem_bytes + lane * cbytes;
+      if (fp8) {
+        *reinterpret_cast<u32x2*>(kp + off) = u32x2{kr[0], kr[1]};
+        *reinterpret_cast<u32x2*>(vp + off) = u32x2{vr[0], vr[1]};
+      } else {
+        *reinterpret_cast<u32x4*>(kp + off) = kr;
+        *reinterpret_cast<u32x4*>(vp + off) = vr;
+      }
+    }
+    // Every write of this round is issued before the next round reads.
+    __syncthreads();
   }
-  if (!ok) {
-    if (lane == 0) atomicOr(&g_device_error, r >= 0 && r < a.total_rows ? kErrPage : kErrRow);
-    return;
-  }
-  copy_row(const_cast<uint16_t*>(a.kv.k), a.kv.k, dst, src, a.head_dim, a.kv.elem_bytes, lane);
-  copy_row(const_cast<uint16_t*>(a.kv.v), a.kv.v, dst, src, a.head_dim, a.kv.elem_bytes, lane);
 }
 
 // Lengths after the commit (a launch of its own, after every copy has read
@@ -194,8 +267,8 @@ hipError_t launch_append_kv(const AppendArgs& a, hipStream_t s) {
 
 hipError_t launch_commit(const CommitArgs& a, hipStream_t s) {
   if (a.batch_size == 0) return hipSuccess;
-  const int64_t lanes = (int64_t)a.batch_size * a.max_accepted * a.num_kv_heads * 16;
-  if (lanes > 0) hipLaunchKernelGGL(commit_kernel, dim3((unsigned)((lanes + 255) / 256)), dim3(256), 0, s, a);
+  const int64_t groups = (int64_t)a.batch_size * a.num_kv_heads;
+  if (a.max_accepted > 0) hipLaunchKernelGGL(commit_kernel, dim3((unsigned)groups), dim3(256), 0, s, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(commit_lengths_kernel, dim3((unsigned)((a.batch_size + 255) / 256)), dim3(256), 0, s, a);

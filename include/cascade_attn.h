@@ -100,7 +100,8 @@ typedef struct {
 /* Queries, bf16 [total_rows, Hq, head_dim]; element (row, h, c) at
  * q + row*row_stride + h*head_stride + c.  Strides are multiples of 8
  * elements, q is 16-byte aligned.  Rows are ordered request-major, then
- * branch, then draft position.  sm_scale is usually 1/sqrt(head_dim). */
+ * branch, then draft position.  sm_scale is usually 1/sqrt(head_dim); it must be
+ * finite and > 0 (CASCADE_ERR_SHAPE otherwise). */
 typedef struct {
   const void *q;
   int64_t row_stride;
@@ -242,10 +243,14 @@ CASCADE_API cascade_status cascade_device_error(int32_t *flag_out, int32_t clear
  * i (those slots must already be mapped: the caller owns page allocation), then
  * cache_seqlens_out[i] = L_i + their count (cache_seqlens_out may be
  * t->cache_seqlens itself: the lengths are updated in place by a second
- * launch).  max_accepted >= every request's count.  A destination slot may be
- * the row's own draft slot (drafts continuing the prefix pages) but must not be
- * the draft slot of another accepted row.  Rejected drafts cost nothing: their
- * slots are rewritten by the next append.  Both calls are graph-capturable. */
+ * launch).  max_accepted >= every request's count.  The rows of a request are
+ * copied in path order and every copy reads the value its source held before
+ * the call, so destination L_i + k may be the draft slot of the k-th or of an
+ * earlier accepted row (drafts continuing the prefix pages with
+ * draft_start = L_i, and an accepted path that skips nodes, e.g. nodes
+ * [0, 2, 5]); it must not be the draft slot of a later accepted row.
+ * Rejected drafts cost nothing: their slots are rewritten by the next append.
+ * Both calls are graph-capturable. */
 CASCADE_API cascade_status cascade_append_draft_kv(const cascade_paged_kv *kv, const cascade_tree *t,
                                        int32_t total_rows, const void *k_new, const void *v_new,
                                        int64_t new_row_stride, int64_t new_head_stride, void *stream);

@@ -85,9 +85,28 @@ def test_rejects_before_launch():
     q, kv, t = make()
     q.sm_scale = float("nan")
     assert call_verify(q, kv, t) == B.CASCADE_ERR_SHAPE
+    # The running max is taken over raw scores and then scaled: only a
+    # positive scale keeps it the max of the scaled scores.
+    for bad in (-0.125, 0.0):
+        q, kv, t = make()
+        q.sm_scale = bad
+        assert call_verify(q, kv, t) == B.CASCADE_ERR_SHAPE
+        assert b"sm_scale" in lib.cascade_last_error()
     q, kv, t = make()
     assert lib.naive_expand(ctypes.byref(q), ctypes.byref(kv), ctypes.byref(t), FAKE, 7, None,
                             None) == B.CASCADE_ERR_UNSUPPORTED
+
+
+def test_empty_batch_with_long_prefix_bound():
+    # No requests but a long max_prefix_len: the split planner must not divide
+    # by the (zero) item count, and the calls succeed without launching.
+    lib = B.lib()
+    q, kv, t = make(B_=0, L=1000, rows=0, branches=0)
+    t.page_table_stride = 63
+    assert lib.cascade_workspace_size(ctypes.byref(q), ctypes.byref(kv), ctypes.byref(t)) == 0
+    assert call_verify(q, kv, t, o=None) == B.CASCADE_OK
+    assert lib.cascade_prefix_attn(ctypes.byref(q), ctypes.byref(kv), ctypes.byref(t), None, None,
+                                   None, 0, None) == B.CASCADE_OK
 
 
 def test_workspace_rules():

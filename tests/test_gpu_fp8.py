@@ -66,6 +66,12 @@ def cases():
                                               seed=45),
         "draft_tree": lambda: W.attach_random_trees(
             W.build_workload("draft_tree", [75, 0, 300], [[12], [7], [20]], 8, 2, 128, 16, seed=46), 47),
+        # A 600-token suffix continuing its prefix pages (one branch): the row
+        # chunks near its end see more than 512 draft keys, past the kernel's
+        # LDS table of draft-key offsets, so those keys resolve through the
+        # block table one by one.
+        "suffix600": lambda: W.build_workload("suffix600", [100, 37], [[600], [530]], 8, 2, 128, 16, seed=49,
+                                              suffix_in_prefix_pages=True),
     }
 
 
@@ -93,6 +99,24 @@ def test_fp8_verify_and_three_call_path(B, case, layout):
     cmp(o3, l3, ro, rl)
     ra, rla = O.prefix_pass(ref)
     cmp(oa, la, ra, rla)
+    assert B.cascade_device_error(clear=True) == 0
+
+
+@pytest.mark.parametrize("layout", ["NHD", "HND"])
+def test_fp8_headline_all_rows(B, layout):
+    """The headline shapes (B=32, Hq=32, Hkv=8, d=128, L=2000, topk=4 chains of
+    S=5, page 16) over FP8 E4M3 KV: the fused verify launch the benchmark
+    times, all 640 x 32 rows, and naive expansion, against the oracle over the
+    dequantised pools."""
+    wl = W.with_fp8_kv(W.headline())
+    note(f"fp8 headline all rows {layout}")
+    x = B.to_device(wl, layout=layout)
+    o, l = B.cascade_verify_attn(x, out_dtype=torch.bfloat16)
+    on, ln = B.naive_expand(x)
+    torch.cuda.synchronize()
+    ro, rl = O.cascade(O.dequantize_kv(wl))
+    cmp(o, l, ro, rl)
+    cmp(on, ln, ro, rl)
     assert B.cascade_device_error(clear=True) == 0
 
 

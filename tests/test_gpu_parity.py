@@ -99,6 +99,16 @@ def small_cases():
                                                     seed=37),
         "rows_split_slot_tree": lambda: W.attach_random_trees(
             W.build_workload("rows_split_slot_tree", [5000, 2100], [[64], [40]], 32, 2, 128, 16, seed=38), 39),
+        # A 600-token suffix (one branch continuing its prefix pages) at d = 64,
+        # which the key-split kernel runs: row chunks near the end of the
+        # suffix see more than 512 draft keys, past the LDS table of draft-key
+        # offsets, so those keys resolve through the block table one by one.
+        "suffix600_d64": lambda: W.build_workload("suffix600_d64", [100, 37], [[600], [530]], 8, 2, 64, 16,
+                                                  seed=40, suffix_in_prefix_pages=True),
+        # The same past-the-table draft keys in draft pages of their own, a
+        # short branch in front of a 560-token one.
+        "long_branch_d64": lambda: W.build_workload("long_branch_d64", [64], [[40, 560]], 4, 2, 64, 16,
+                                                    seed=42),
     }
 
 
@@ -181,15 +191,21 @@ def test_merge_state_kernel(B):
 
 @pytest.mark.parametrize("layout", ["NHD", "HND"])
 def test_verify_headline_all_rows(B, layout):
+    """The headline launch the benchmark times (bf16 output), naive expansion,
+    and the three-call form (pass A, pass B, merge_state), all rows."""
     wl = W.headline()
     note(f"verify headline rows={wl.total_rows} {layout}")
     x = B.to_device(wl, layout=layout)
-    o, l = B.cascade_verify_attn(x)
+    o, l = B.cascade_verify_attn(x, out_dtype=torch.bfloat16)
     on, ln = B.naive_expand(x)
+    oa, la = B.cascade_prefix_attn(x, workspace=B.workspace_for(x))
+    ob, lb = B.cascade_draft_attn(x)
+    o3, l3 = B.merge_state(oa, la, ob, lb, out_dtype=torch.bfloat16)
     torch.cuda.synchronize()
     ro, rl = O.cascade(wl)
     cmp(o, l, ro, rl)
     cmp(on, ln, ro, rl)
+    cmp(o3, l3, ro, rl)
 
 
 def test_verify_gqa_config_split_path(B):
@@ -291,31 +307,74 @@ def test_prefix_hit_full_sampled(B, h):
     cmp(of, lf, ro, rl, rows=r)
 
 
+def _gather_ref_bits(wl, pool_name, table_row, first_slot, count, g):
+    """CPU gather of `count` logical slots from `first_slot` of one block-table
+    row (kv head g), as bf16 bits: bf16 pools directly, FP8 pools as the value
+    of each E4M3 code (exact in bf16; scales not applied)."""
+    t = first_slot + np.arange(count)
+    P = wl.page_size
+    if getattr(wl, "k_codes", None) is not None:
+        codes = (wl.k_codes if pool_name == "k" else wl.v_codes)[table_row[t // P], t % P, g]
+        return W.bf16_bits(O.e4m3_value(codes).astype(np.float32))
+    pool = wl.k_pool if pool_name == "k" else wl.v_pool
+    return W.bf16_bits(pool[table_row[t // P], t % P, g])
+
+
+def _bits(t):
+    return t.view(torch.int16).cpu().numpy().view(np.uint16)
+
+
+@pytest.mark.parametrize("kv", ["bf16", "fp8"])
+@pytest.mark.parametrize("page", [16, 64])
+@pytest.mark.parametrize("layout", ["NHD", "HND"])
+def test_gather_hook_bit_exact(B, layout, page, kv):
+    """The gather hook runs the attention kernels' own gather functions (page
+    id of each 16-key half, its buffer descriptor, the lane offset; the
+    draft-slot resolution and the clamped draft-key load) and must reproduce
+    the CPU gather through the block tables bit for bit, for prefixes (tails
+    that end inside a half and inside a page, an empty one) and for draft
+    branches, one of which continues its request's prefix pages."""
+    wls = [W.build_workload("gather", [75, 0, 300, 31], [[2, 4, 1], [3], [1, 5], [9]], 8, 2, 128, page,
+                            seed=51),
+           # one branch per request continuing its prefix pages from slot L_i
+           # (31: inside a 16-key half; 100: inside a page)
+           W.build_workload("gather_suffix", [31, 100, 0], [[9], [40], [3]], 8, 2, 128, page, seed=54,
+                            suffix_in_prefix_pages=True)]
+    for wl in wls:
+        if kv == "fp8":
+            wl = W.with_fp8_kv(wl)
+        _check_gather(B, wl, layout, f"{wl.name} {layout} page {page}")
+
+
+def _check_gather(B, wl, layout, label):
+    x = B.to_device(wl, layout=layout)
+    note(f"debug gather {label}")
+    for i in range(wl.batch_size):
+        L = int(wl.cache_seqlens[i])
+        for g in range(wl.num_kv_heads):
+            k, v = B.cascade_debug_gather(x, 0, i, g, L)
+            assert np.array_equal(_bits(k), _gather_ref_bits(wl, "k", wl.page_table[i], 0, L, g))
+            assert np.array_equal(_bits(v), _gather_ref_bits(wl, "v", wl.page_table[i], 0, L, g))
+    for j in range(wl.num_branches):
+        S = int(wl.branch_qo_indptr[j + 1] - wl.branch_qo_indptr[j])
+        for g in range(wl.num_kv_heads):
+            k, v = B.cascade_debug_gather(x, 1, j, g, S)
+            ds = int(wl.draft_start[j])
+            assert np.array_equal(_bits(k), _gather_ref_bits(wl, "k", wl.draft_page_table[j], ds, S, g))
+            assert np.array_equal(_bits(v), _gather_ref_bits(wl, "v", wl.draft_page_table[j], ds, S, g))
+    assert B.cascade_device_error(clear=True) == 0
+
+
 @pytest.mark.parametrize("tree", [False, True])
-def test_gather_and_mask_bit_exact(B, tree):
+def test_mask_hook_bit_exact(B, tree):
     wl = W.build_workload("gm", [75, 0, 300], [[2, 4, 1], [3], [1, 5]], 8, 2, 128, 16, seed=51)
     if tree:
         wl = W.build_workload("gm_tree", [75, 0, 300], [[13], [3], [40]], 8, 2, 128, 16, seed=52)
         W.attach_random_trees(wl, 53)
     x = B.to_device(wl)
-    kbits = W.bf16_bits(wl.k_pool)
-    vbits = W.bf16_bits(wl.v_pool)
-    note("debug gather / mask")
-    for i in range(wl.batch_size):
-        L = int(wl.cache_seqlens[i])
-        for g in range(wl.num_kv_heads):
-            k, v = B.cascade_debug_gather(x, 0, i, g, L)
-            t = np.arange(L)
-            ref_k = kbits[wl.page_table[i, t // 16], t % 16, g]
-            ref_v = vbits[wl.page_table[i, t // 16], t % 16, g]
-            assert np.array_equal(k.view(torch.int16).cpu().numpy().view(np.uint16), ref_k)
-            assert np.array_equal(v.view(torch.int16).cpu().numpy().view(np.uint16), ref_v)
+    note("debug mask")
     for j in range(wl.num_branches):
         S = int(wl.branch_qo_indptr[j + 1] - wl.branch_qo_indptr[j])
-        k, _ = B.cascade_debug_gather(x, 1, j, 1, S)
-        u = np.arange(S)
-        ref = kbits[wl.draft_page_table[j, u // 16], u % 16, 1]
-        assert np.array_equal(k.view(torch.int16).cpu().numpy().view(np.uint16), ref)
         i = int(np.searchsorted(wl.req_branch_indptr, j, side="right") - 1)
         L = int(wl.cache_seqlens[i])
         m = B.cascade_debug_mask(x, j, S, L + S + 3).cpu().numpy().astype(bool)

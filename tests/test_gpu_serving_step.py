@@ -118,6 +118,44 @@ def test_append_and_commit_bit_exact(B, layout):
     assert np.max(np.abs(l[fin] - rl[fin])) <= 1e-3 and np.array_equal(np.isneginf(l), np.isneginf(rl))
 
 
+@pytest.mark.parametrize("layout", ["NHD", "HND"])
+def test_commit_tree_path_skipping_nodes_in_prefix_pages(B, layout):
+    """Drafts continue the prefix pages (draft_start = L_i) and each request
+    accepts a root-to-leaf path of its draft tree that skips nodes, so the k-th
+    destination L_i + k is the draft slot of an earlier accepted node: every
+    copy must still move the value its source held before the commit."""
+    wl = W.build_workload("treecommit", [37, 64, 5, 90], [[12], [20], [9], [16]], 8, 2, 128, 16,
+                          seed=64, suffix_in_prefix_pages=True)
+    wl = W.attach_random_trees(wl, seed=65, max_children=2)
+    qo = wl.branch_qo_indptr
+    acc, ind = [], [0]
+    for i in range(wl.batch_size):
+        r0, S = int(qo[i]), int(qo[i + 1] - qo[i])
+        leaf = S - 1                        # deepest-numbered node; walk up to the root
+        path = []
+        u = leaf
+        while u >= 0:
+            path.append(u)
+            u = int(wl.draft_parent[r0 + u])
+        path = path[::-1]
+        acc += [r0 + u for u in path]
+        ind.append(len(acc))
+    skipping = sum(1 for i in range(wl.batch_size)
+                   for k, r in enumerate(acc[ind[i]:ind[i + 1]]) if r - int(qo[i]) != k)
+    assert skipping > 0                     # some destination is an earlier node's draft slot
+    x = B.to_device(wl, layout=layout)
+    kc, vc, lens = O.commit_accepted(wl, np.array(ind), np.array(acc))
+    note(f"commit tree path {layout}")
+    B.cascade_commit_accepted(x, torch.tensor(ind, dtype=torch.int32, device="cuda"),
+                              torch.tensor(acc, dtype=torch.int32, device="cuda"),
+                              max(np.diff(ind)))
+    torch.cuda.synchronize()
+    assert np.array_equal(x.cache_seqlens.cpu().numpy(), lens)
+    assert np.array_equal(pool_bits_nhd(x.k_pool, layout), W.bf16_bits(kc))
+    assert np.array_equal(pool_bits_nhd(x.v_pool, layout), W.bf16_bits(vc))
+    assert B.cascade_device_error(clear=True) == 0
+
+
 def test_append_empty_commit_changes_nothing(B):
     wl = W.build_workload("step0", [33, 17], [[2, 2], [3]], 4, 2, 64, 16, seed=63)
     x = B.to_device(wl)
