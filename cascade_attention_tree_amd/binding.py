@@ -34,7 +34,7 @@ EXPORTED = (
     "cascade_verify_attn", "naive_expand", "cascade_status_string", "cascade_last_error",
     "cascade_debug_gather", "cascade_debug_mask", "cascade_device_error",
     "cascade_kernel_timing", "cascade_last_verify_ms", "cascade_append_draft_kv",
-    "cascade_commit_accepted", "cascade_stream_read",
+    "cascade_commit_accepted", "cascade_stream_read", "cascade_verify_attn_noalloc",
 )
 
 
@@ -97,6 +97,8 @@ def lib() -> ctypes.CDLL:
         L.cascade_verify_attn.argtypes = [P(Query), P(PagedKV), P(Tree), vp, ctypes.c_int, vp, vp,
                                           ctypes.c_size_t, vp]
         L.cascade_verify_attn.restype = st
+        L.cascade_verify_attn_noalloc.argtypes = [P(Query), P(PagedKV), P(Tree), vp, ctypes.c_int, vp, vp]
+        L.cascade_verify_attn_noalloc.restype = st
         L.naive_expand.argtypes = [P(Query), P(PagedKV), P(Tree), vp, ctypes.c_int, vp, vp]
         L.naive_expand.restype = st
         L.cascade_status_string.argtypes = [ctypes.c_int]
@@ -325,6 +327,21 @@ def cascade_verify_attn(x: DeviceInputs, out_dtype=torch.float32, o=None, lse=No
                                      o.data_ptr(),
                                      CASCADE_BF16 if o.dtype == torch.bfloat16 else CASCADE_F32,
                                      _ptr(lse), _ptr(workspace), nbytes, _stream(stream)))
+    return o, lse
+
+
+def cascade_verify_attn_noalloc(x: DeviceInputs, out_dtype=torch.float32, o=None, lse=None, stream=None,
+                                want_lse=True):
+    """cascade_verify_attn with the library's built-in workspace (no device
+    allocation by the library)."""
+    so, sl = _out_shape(x)
+    o = _out(o, so, (out_dtype, torch.bfloat16 if out_dtype == torch.float32 else torch.float32), x.q)
+    if lse is not None or want_lse:
+        lse = _out(lse, sl, (torch.float32,), x.q)
+    _check(lib().cascade_verify_attn_noalloc(ctypes.byref(x.query), ctypes.byref(x.kv), ctypes.byref(x.tree),
+                                             o.data_ptr(),
+                                             CASCADE_BF16 if o.dtype == torch.bfloat16 else CASCADE_F32,
+                                             _ptr(lse), _stream(stream)))
     return o, lse
 
 

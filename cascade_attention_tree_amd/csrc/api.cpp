@@ -400,7 +400,7 @@ cascade_status merge_state(const float* o_a, const float* lse_a, const float* o_
   return CASCADE_OK;
 }
 
-cascade_status cascade_verify_attn(const cascade_query* q, const cascade_paged_kv* kv,
+static cascade_status verify_impl(const cascade_query* q, const cascade_paged_kv* kv,
                                    const cascade_tree* t, void* o, cascade_dtype o_dtype, float* lse,
                                    void* ws, size_t ws_bytes, void* stream) {
   cascade_status st = check_all(q, kv, t);
@@ -438,6 +438,31 @@ cascade_status cascade_verify_attn(const cascade_query* q, const cascade_paged_k
   }
   if (g_timing.enabled) g_timing.recorded = true;
   return CASCADE_OK;
+}
+
+cascade_status cascade_verify_attn(const cascade_query* q, const cascade_paged_kv* kv,
+                                   const cascade_tree* t, void* o, cascade_dtype o_dtype, float* lse,
+                                   void* ws, size_t ws_bytes, void* stream) {
+  return verify_impl(q, kv, t, o, o_dtype, lse, ws, ws_bytes, stream);
+}
+
+cascade_status cascade_verify_attn_noalloc(const cascade_query* q, const cascade_paged_kv* kv,
+                                           const cascade_tree* t, void* o, cascade_dtype o_dtype,
+                                           float* lse, void* stream) {
+  cascade_status st = check_all(q, kv, t);
+  if (st != CASCADE_OK) return st;
+  const size_t need = ws_layout(q, kv, plan_request(q, kv, t)).bytes;
+  if (need > casc::kScratchBytes)
+    return fail(CASCADE_ERR_WORKSPACE,
+                "these shapes need %zu bytes of workspace; the built-in workspace holds %zu "
+                "(use cascade_verify_attn with a caller workspace)",
+                need, casc::kScratchBytes);
+  void* ws = nullptr;
+  if (need > 0) {
+    const hipError_t e = casc::scratch_for_current_device(&ws);
+    if (e != hipSuccess) return hip_fail(e, "built-in workspace address");
+  }
+  return verify_impl(q, kv, t, o, o_dtype, lse, ws, need > 0 ? casc::kScratchBytes : 0, stream);
 }
 
 cascade_status naive_expand(const cascade_query* q, const cascade_paged_kv* kv, const cascade_tree* t,

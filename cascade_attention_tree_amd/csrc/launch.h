@@ -33,6 +33,12 @@ hipError_t launch_commit(const CommitArgs& a, hipStream_t s);
 hipError_t launch_debug_gather(const DebugArgs& a, hipStream_t s);
 hipError_t launch_debug_mask(const DebugArgs& a, hipStream_t s);
 
+// The allocation-free verify entry point's workspace: a file-scope device
+// array of kScratchBytes per GPU.  scratch_for_current_device returns the
+// current device's copy (looked up once per device).
+constexpr size_t kScratchBytes = size_t(32) << 20;
+hipError_t scratch_for_current_device(void** ptr);
+
 // Sticky device error words of each translation unit (read, optionally clear).
 hipError_t read_error_d64(int* v, int clear);
 hipError_t read_error_d128(int* v, int clear);

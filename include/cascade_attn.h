@@ -195,6 +195,23 @@ CASCADE_API cascade_status cascade_verify_attn(const cascade_query *q, const cas
                                    float *lse, void *workspace, size_t workspace_bytes,
                                    void *stream);
 
+/* cascade_verify_attn for callers that cannot allocate device memory (code
+ * under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc): the same kernels and results, with the split-prefix workspace
+ * taken from a file-scope device array of 32 MiB that the library holds on
+ * each GPU it runs on until the process ends (its address is looked up once
+ * per device, on the device current at the first call).  The call allocates
+ * and frees nothing.  Shapes that need more workspace than the array holds
+ * (cascade_workspace_size > 32 MiB) return CASCADE_ERR_WORKSPACE and launch
+ * nothing.  Every call on one GPU shares that GPU's array: calls that overlap
+ * in time on one GPU (other streams, other threads) race on it, so the
+ * caller orders them.  The array's contents carry no meaning between calls
+ * (every byte a call reads it first writes).  The stream must belong to the
+ * current device. */
+CASCADE_API cascade_status cascade_verify_attn_noalloc(const cascade_query *q, const cascade_paged_kv *kv,
+                                           const cascade_tree *tree, void *o, cascade_dtype o_dtype,
+                                           float *lse, void *stream);
+
 /* Baseline (cascade page, naive expansion): the batch expanded into one
  * virtual request per branch; each reads its request's whole prefix and its
  * own drafts and runs one softmax.  Same outputs as cascade_verify_attn. */
