@@ -461,6 +461,10 @@ def main():
                     help="skip the FP8 KV variant of the headline")
     ap.add_argument("--fp8-only", action="store_true",
                     help="for profiling: only the FP8 headline verify (cold steps)")
+    ap.add_argument("--gqa-only", action="store_true",
+                    help="for profiling: only the GQA verify configuration (cold steps)")
+    ap.add_argument("--ragged-only", action="store_true",
+                    help="for profiling: only the ragged configuration (cold steps)")
     ap.add_argument("--traffic-probe", action="store_true",
                     help="for hardware-counter runs: one plain 256 MiB device copy (known bytes), "
                          "then a few flushed verify steps and naive-expand steps; prints nothing else")
@@ -474,6 +478,20 @@ def main():
     from cascade_attention_tree_amd import binding as B
     from cascade_attention_tree_amd import workload as W
 
+    flush_buf = torch.ones(1 << 28, dtype=torch.float32, device="cuda")
+    flush_out = torch.empty((), dtype=torch.float32, device="cuda")
+
+    def flush():
+        torch.sum(flush_buf, dim=0, out=flush_out)   # reads 1 GiB, writes 4 bytes
+
+    if args.gqa_only or args.ragged_only:
+        print("bench: profiling leg only", file=sys.stderr, flush=True)
+        out = (gqa_timing(B, W, torch, flush, args.steps, args.warmup) if args.gqa_only
+               else ragged_timing(B, W, torch, flush, steps=args.steps, warmup=args.warmup))
+        print(json.dumps({"profiling_leg": "gqa" if args.gqa_only else "ragged", **out,
+                          "kernel_hash": kernel_source_hash()}), flush=True)
+        return
+
     print("bench: generating headline workload", file=sys.stderr, flush=True)
     wl = W.headline()
     kv_casc, kv_naive, q_bytes, o_bytes = workload_bytes(wl)
@@ -481,11 +499,6 @@ def main():
     o = torch.empty(wl.q.shape, dtype=torch.bfloat16, device="cuda")
     lse = torch.empty(wl.q.shape[:2], dtype=torch.float32, device="cuda")
     ws = B.workspace_for(x)
-    flush_buf = torch.ones(1 << 28, dtype=torch.float32, device="cuda")
-    flush_out = torch.empty((), dtype=torch.float32, device="cuda")
-
-    def flush():
-        torch.sum(flush_buf, dim=0, out=flush_out)   # reads 1 GiB, writes 4 bytes
 
     def verify():
         B.cascade_verify_attn(x, o=o, lse=lse, workspace=ws)

@@ -41,20 +41,27 @@ int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
-// Work items wanted per launch before the prefix is split (one per CU of an
-// MI355X), and the bounds on keys per split.
+// Work items wanted per launch before the prefix is split: one per CU of an
+// MI355X for the key-split kernel, two per CU for the pair kernel (which
+// fits two workgroups on a CU); and the bounds on keys per split.
 constexpr int kTargetItems = 256;
+constexpr int kPairTargetItems = 512;
 constexpr int kMinSplitKeys = 256;
 constexpr int kMaxSplitKeys = 4096;
 constexpr int kMaxRowBlocks = 5;
 
 struct Plan {
   int group = 1;
-  int rb = 1;        // 16-row blocks per chunk
-  int n_chunks = 1;  // row chunks per (segment, kv head)
+  int rb = 1;        // 16-row blocks per chunk (key-split kernel, split merges)
+  int n_chunks = 1;  // row chunks per (segment, kv head) of the key-split kernel
   int n_splits = 1;  // key splits of the prefix
   int split_len = 32;
-  int64_t items = 0;  // segments * kv heads * chunks
+  int64_t items = 0;  // segments * kv heads * chunks (key-split kernel)
+  // Pass A and the fused verify pass on the pair kernel: chunks of at most
+  // pair_rows rows, pair_chunks per (request, kv head).
+  bool pair = false;
+  int pair_chunks = 1;
+  int pair_rows = 0;
 };
 
 void plan_rows(Plan& p, int64_t rows_per_segment) {
@@ -63,12 +70,14 @@ void plan_rows(Plan& p, int64_t rows_per_segment) {
   p.n_chunks = (int)(rows_per_segment > 0 ? cdiv(rows_per_segment, 16 * p.rb) : 1);
 }
 
-void plan_splits(Plan& p, int max_len) {
+// Key splits for `items` work items: enough to reach `target` items when the
+// prefix is long enough, at most kMaxSplitKeys keys per split.
+void plan_splits(Plan& p, int max_len, int64_t items, int64_t target) {
   const int len = max_len > 0 ? max_len : 1;
   int64_t n = 1;
   // An empty launch (no requests) has no items to fill the device with.
-  if (len > 2 * kMinSplitKeys && p.items > 0 && p.items < kTargetItems) {
-    n = cdiv(kTargetItems, p.items);
+  if (len > 2 * kMinSplitKeys && items > 0 && items < target) {
+    n = cdiv(target, items);
     const int64_t cap = cdiv(len, kMinSplitKeys);
     if (n > cap) n = cap;
   }
@@ -222,14 +231,48 @@ casc::AttnArgs make_args(const cascade_query* q, const cascade_paged_kv* kv, con
   return a;
 }
 
-// Plan of the per-request launches (pass A, pass B, verify).
+// Query rows per (request, kv head) from which pass A, the fused verify pass
+// and pass B run the row-split kernel (head dim 128, bf16 pools): at least
+// four full work items of kRowsPerItem rows, where its two waves per SIMD keep
+// the matrix pipes busy (a prefix-hit suffix prefill).
+constexpr int64_t kRowKernelMinRows = 1024;
+
+// Plan of the per-request launches (pass A, pass B, verify).  At head_dim 128,
+// pass A and the fused verify pass of requests below kRowKernelMinRows rows
+// per kv head run on the pair kernel (chunks of up to kPairRows rows, two
+// workgroups per CU, the chunks of a (request, kv head) sharing its prefix
+// stream through one L2) -- except bf16 pools whose (request, kv head) pairs
+// already fill the device with one chunk of at most 16 * kMaxRowBlocks rows
+// each: there the key-split kernel, one workgroup per CU holding all rows,
+// measured faster (60.6 against 64.5 us at 32 requests x 8 kv heads x 80
+// rows), while the pair kernel is faster over FP8 pools, on the ragged
+// batch and at equal speed on the GQA configuration.  A request with 32 rows
+// or more is cut in two chunks when there are too few (request, kv head)
+// pairs to fill the device.
 Plan plan_request(const cascade_query* q, const cascade_paged_kv* kv, const cascade_tree* t) {
   Plan p;
   p.group = q->num_qo_heads / kv->num_kv_heads;
-  plan_rows(p, (int64_t)t->max_request_rows * p.group);
+  const int64_t rows = (int64_t)t->max_request_rows * p.group;
+  plan_rows(p, rows);
   p.items = (int64_t)t->batch_size * kv->num_kv_heads * p.n_chunks;
-  plan_splits(p, t->max_prefix_len);
+  const int64_t pairs = (int64_t)t->batch_size * kv->num_kv_heads;
+  const bool one_chunk_fills = !kv_fp8(kv) && rows <= 16 * kMaxRowBlocks && pairs >= kTargetItems;
+  p.pair = kv->head_dim == 128 && rows > 0 && rows < kRowKernelMinRows && !one_chunk_fills;
+  if (p.pair) {
+    p.pair_chunks = (int)cdiv(rows, casc::kPairRows);
+    if (p.pair_chunks == 1 && rows >= 32 && pairs < kPairTargetItems) p.pair_chunks = 2;
+    p.pair_rows = (int)cdiv(rows, p.pair_chunks);
+    plan_splits(p, t->max_prefix_len, pairs * p.pair_chunks, kPairTargetItems);
+  } else {
+    plan_splits(p, t->max_prefix_len, p.items, kTargetItems);
+  }
   return p;
+}
+
+// Workgroups of one key split of the pair kernel: (request, kv head) pairs
+// rounded up to a multiple of the 8 XCDs, times the row chunks.
+int64_t pair_grid_per_split(const cascade_tree* t, const cascade_paged_kv* kv, const Plan& p) {
+  return cdiv((int64_t)t->batch_size * kv->num_kv_heads, 8) * 8 * p.pair_chunks;
 }
 
 struct WsLayout {
@@ -247,11 +290,35 @@ WsLayout ws_layout(const cascade_query* q, const cascade_paged_kv* kv, const Pla
   return w;
 }
 
+// Arguments of the split merge that follows a split prefix or verify pass.
+casc::SplitMergeArgs split_merge_args(const cascade_query* q, const cascade_paged_kv* kv, const cascade_tree* t,
+                                      const Plan& p, const casc::AttnArgs& a, bool verify) {
+  casc::SplitMergeArgs m{};
+  m.ws_o = a.ws_o;
+  m.ws_lse = a.ws_lse;
+  m.n_splits = p.n_splits;
+  m.split_len = p.split_len;
+  m.total_rows = q->total_rows;
+  m.num_qo_heads = q->num_qo_heads;
+  m.head_dim = kv->head_dim;
+  m.batch_size = t->batch_size;
+  const int64_t cap = (int64_t)t->page_table_stride * kv->page_size;
+  const int64_t planned = (int64_t)p.n_splits * p.split_len;
+  m.len_cap = (int32_t)(cap < planned ? cap : planned);
+  m.verify = verify ? 1 : 0;
+  m.cache_seqlens = t->cache_seqlens;
+  m.req_branch_indptr = t->req_branch_indptr;
+  m.branch_qo_indptr = t->branch_qo_indptr;
+  m.o = a.o;
+  m.o_bf16 = a.o_bf16;
+  m.lse = a.lse;
+  return m;
+}
+
 hipError_t launch(int mode, int head_dim, int rb, const casc::AttnArgs& a, int64_t grid, hipStream_t s,
                   hipEvent_t e0 = nullptr, hipEvent_t e1 = nullptr) {
   if (grid <= 0) return hipSuccess;
-  // The split merges read only the fp32 workspace: one kernel for both pool types.
-  const bool fp8 = a.kv.elem_bytes == 1 && mode != casc::kModePrefixFinish && mode != casc::kModeVerifyFinish;
+  const bool fp8 = a.kv.elem_bytes == 1;
   if (head_dim == 64)
     return fp8 ? casc::launch_attn_d64_fp8(mode, rb, a, (int)grid, s, e0, e1)
                : casc::launch_attn_d64(mode, rb, a, (int)grid, s, e0, e1);
@@ -259,13 +326,6 @@ hipError_t launch(int mode, int head_dim, int rb, const casc::AttnArgs& a, int64
              : casc::launch_attn_d128(mode, rb, a, (int)grid, s, e0, e1);
 }
 
-// Query rows per (request, kv head) from which pass A, the fused verify pass
-// and pass B run the row-split kernel: at least four full work items of
-// kRowsPerItem rows, where its two waves per SIMD keep the matrix pipes
-// busy (a prefix-hit suffix prefill).  Below it the key-split kernel, one
-// wave per SIMD over the whole row tile, is as fast or faster (measured on
-// the verify workloads).
-constexpr int64_t kRowKernelMinRows = 1024;
 
 // Pass A, the fused verify pass or pass B (`mode`), unsplit or one launch of
 // the splits: the row-split kernel (head dim 128, bf16 pools, row-heavy
@@ -274,6 +334,14 @@ constexpr int64_t kRowKernelMinRows = 1024;
 hipError_t launch_row_modes(int mode, const cascade_paged_kv* kv,
                                const cascade_tree* t, const Plan& p, casc::AttnArgs a, int splits,
                                hipStream_t s, hipEvent_t e0 = nullptr, hipEvent_t e1 = nullptr) {
+  if (p.pair && (mode == casc::kModePrefix || mode == casc::kModeVerify)) {
+    a.n_chunks = p.pair_chunks;
+    a.chunk_rows = p.pair_rows;
+    const int64_t grid = pair_grid_per_split(t, kv, p) * splits;
+    if (grid <= 0) return hipSuccess;
+    return kv_fp8(kv) ? casc::launch_pair_d128_fp8(mode, a, (int)grid, s, e0, e1)
+                      : casc::launch_pair_d128(mode, a, (int)grid, s, e0, e1);
+  }
   const int64_t rows = (int64_t)t->max_request_rows * p.group;
   if (kv->head_dim != 128 || kv_fp8(kv) || rows < kRowKernelMinRows)
     return launch(mode, kv->head_dim, p.rb, a, p.items * splits, s, e0, e1);
@@ -292,6 +360,11 @@ struct KernelTiming {
 };
 thread_local KernelTiming g_timing;
 
+cascade_status check_grid(int64_t grid);
+cascade_status check_plan_grid(const cascade_tree* t, const cascade_paged_kv* kv, const Plan& p) {
+  const int64_t pair = p.pair ? pair_grid_per_split(t, kv, p) * p.n_splits : 0;
+  return check_grid(pair > p.items * p.n_splits ? pair : p.items * p.n_splits);
+}
 cascade_status check_grid(int64_t grid) {
   if (grid > INT32_MAX) return fail(CASCADE_ERR_SHAPE, "launch too large (%lld work items)", (long long)grid);
   return CASCADE_OK;
@@ -332,7 +405,7 @@ cascade_status cascade_prefix_attn(const cascade_query* q, const cascade_paged_k
   if (wl.bytes > 0 && (!ws || ws_bytes < wl.bytes))
     return fail(CASCADE_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", wl.bytes, ws ? ws_bytes : 0);
   if (ws && !aligned16(ws)) return fail(CASCADE_ERR_UNSUPPORTED, "workspace must be 16-byte aligned");
-  if ((st = check_grid(p.items * p.n_splits)) != CASCADE_OK) return st;
+  if ((st = check_plan_grid(t, kv, p)) != CASCADE_OK) return st;
   if (q->total_rows == 0 || t->batch_size == 0) return CASCADE_OK;
   hipStream_t s = static_cast<hipStream_t>(stream);
   casc::AttnArgs a = make_args(q, kv, t, p);
@@ -346,8 +419,7 @@ cascade_status cascade_prefix_attn(const cascade_query* q, const cascade_paged_k
     a.grid_splits = p.n_splits;
     e = launch_row_modes(casc::kModePrefix, kv, t, p, a, p.n_splits, s);
     if (e != hipSuccess) return hip_fail(e, "prefix pass launch");
-    a.grid_splits = 1;
-    e = launch(casc::kModePrefixFinish, kv->head_dim, p.rb, a, p.items, s);
+    e = casc::launch_split_merge(split_merge_args(q, kv, t, p, a, false), s, nullptr);
     if (e != hipSuccess) return hip_fail(e, "prefix split merge launch");
   } else {
     e = launch_row_modes(casc::kModePrefix, kv, t, p, a, 1, s);
@@ -413,7 +485,7 @@ static cascade_status verify_impl(const cascade_query* q, const cascade_paged_kv
   if (wl.bytes > 0 && (!ws || ws_bytes < wl.bytes))
     return fail(CASCADE_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", wl.bytes, ws ? ws_bytes : 0);
   if (ws && !aligned16(ws)) return fail(CASCADE_ERR_UNSUPPORTED, "workspace must be 16-byte aligned");
-  if ((st = check_grid(p.items * p.n_splits)) != CASCADE_OK) return st;
+  if ((st = check_plan_grid(t, kv, p)) != CASCADE_OK) return st;
   if (q->total_rows == 0 || t->batch_size == 0) return CASCADE_OK;
   hipStream_t s = static_cast<hipStream_t>(stream);
   casc::AttnArgs a = make_args(q, kv, t, p);
@@ -429,8 +501,7 @@ static cascade_status verify_impl(const cascade_query* q, const cascade_paged_kv
     a.grid_splits = p.n_splits;
     e = launch_row_modes(casc::kModeVerify, kv, t, p, a, p.n_splits, s, e0, nullptr);
     if (e != hipSuccess) return hip_fail(e, "verify prefix launch");
-    a.grid_splits = 1;
-    e = launch(casc::kModeVerifyFinish, kv->head_dim, p.rb, a, p.items, s, nullptr, e1);
+    e = casc::launch_split_merge(split_merge_args(q, kv, t, p, a, true), s, e1);
     if (e != hipSuccess) return hip_fail(e, "verify merge launch");
   } else {
     e = launch_row_modes(casc::kModeVerify, kv, t, p, a, 1, s, e0, e1);
@@ -574,7 +645,8 @@ cascade_status cascade_device_error(int32_t* flag_out, int32_t clear) {
   int flags = 0;
   hipError_t (*const readers[])(int*, int) = {casc::read_error_d64, casc::read_error_d128,
                                               casc::read_error_d64_fp8, casc::read_error_d128_fp8,
-                                              casc::read_error_small};
+                                              casc::read_error_small, casc::read_error_pair_d128,
+                                              casc::read_error_pair_d128_fp8};
   for (auto* rd : readers) {
     int v = 0;
     if ((e = rd(&v, clear)) != hipSuccess) return hip_fail(e, "read error word");

@@ -22,6 +22,9 @@ struct KvView {
                        // count elements, so they are byte offsets for FP8)
 };
 
+// Query rows per chunk of the pair kernel (three 16-row MFMA blocks).
+constexpr int kPairRows = 48;
+
 // Query rows per work item of the row-split kernel (head_dim 128): 8 waves
 // of at most 32 rows (two 16-row MFMA blocks each).
 constexpr int kRowsPerItem = 256;
@@ -31,8 +34,6 @@ enum AttnMode : int {
   kModeDraft = 1,         // pass B -> (o_B, LSE_B)
   kModeVerify = 2,        // pass A; unsplit: + pass B + merge -> (o, LSE); split -> partials
   kModeNaive = 3,         // naive expansion, one softmax per branch -> (o, LSE)
-  kModePrefixFinish = 4,  // merge split partials -> (o_A, LSE_A)
-  kModeVerifyFinish = 5,  // merge split partials, pass B, merge -> (o, LSE)
 };
 
 struct AttnArgs {
@@ -57,6 +58,7 @@ struct AttnArgs {
   const int32_t* draft_start;
   const uint64_t* draft_mask;  // per row: ancestor set over its branch's nodes (NULL: chains)
   int32_t n_chunks;     // row chunks per segment and kv head
+  int32_t chunk_rows;   // pair kernel: query rows per chunk (<= 16 * its row blocks)
   int32_t grid_splits;  // key splits in this launch's grid
   int32_t n_splits;     // key splits of the prefix (partials in the workspace)
   int32_t split_len;    // keys per split (multiple of 32)
@@ -65,6 +67,27 @@ struct AttnArgs {
   float* lse;
   float* ws_o;    // [n_splits, total_rows, Hq, D] normalised partial outputs
   float* ws_lse;  // [n_splits, total_rows, Hq] partial LSE, base 2
+};
+
+// Merge of the key-split partial states of pass A or the fused verify pass
+// (one thread per 4 channels of one (row, head)).
+struct SplitMergeArgs {
+  const float* ws_o;    // [n_splits, total_rows, Hq, D] normalised partial outputs
+  const float* ws_lse;  // [n_splits, total_rows, Hq] partial LSE, base 2
+  int32_t n_splits;
+  int32_t split_len;
+  int32_t total_rows;
+  int32_t num_qo_heads;
+  int32_t head_dim;
+  int32_t batch_size;
+  int32_t len_cap;      // keys a request can have: block-table capacity, and the planned splits
+  int32_t verify;       // split 0 always holds a partial (the drafts of the fused pass)
+  const int32_t* cache_seqlens;
+  const int32_t* req_branch_indptr;
+  const int32_t* branch_qo_indptr;
+  void* o;
+  int32_t o_bf16;
+  float* lse;           // natural log (nullable)
 };
 
 // Elementwise merge of two attention states (the standalone merge_state).

@@ -28,8 +28,8 @@
 //
 // The four waves then merge their states with the LSE identity; each wave
 // ends up owning a quarter of the head dimension.  Depending on the mode the
-// merged state is written as a pass state, as a split partial, or merged once
-// more with pass B (computed in the epilogue) into the final output.
+// merged state is written as a pass state, as a split partial (merged later
+// by the split-merge kernel), or as the final output.
 #pragma once
 
 #include "device_common.h"
@@ -149,8 +149,7 @@ attn_kernel(const AttnArgs a) {
   constexpr int STAGE_BYTES = 4 * STAGE * 2;
   constexpr int XBYTES = 12 * XSLOT * 4;
   constexpr int UNION_BYTES = STAGE_BYTES > XBYTES ? STAGE_BYTES : XBYTES;
-  constexpr bool kMainLoop = MODE <= kModeNaive;
-  constexpr bool kFinish = MODE == kModePrefixFinish || MODE == kModeVerifyFinish;
+  static_assert(MODE >= kModePrefix && MODE <= kModeNaive, "pass A, pass B, verify or naive expansion");
   constexpr bool kDraftKeys = MODE == kModeDraft || MODE == kModeNaive || MODE == kModeVerify;
   // In the fused verify launch the request's draft tiles are taken by one
   // wave, after its share of the prefix tiles, into its own online softmax
@@ -158,10 +157,9 @@ attn_kernel(const AttnArgs a) {
   // LSE identity as the prefix partial states.  Wave 3 has the fewest prefix
   // tiles (tiles go round-robin from wave 0).
   constexpr int kDraftWave = 3;
-  constexpr bool kNeedQ = !kFinish;
   // Large row tiles keep Q in LDS (read per tile as B-fragments) so that the
   // architectural VGPRs stay free for K/V in flight and the softmax.
-  constexpr bool kQInLds = kNeedQ && RB * KS >= 16;
+  constexpr bool kQInLds = RB * KS >= 16;
   constexpr int QSTR = D + 8;  // padded LDS row stride of Q: rows land 4 banks apart
   constexpr int QBYTES = kQInLds ? ROWS * QSTR * 2 : 0;
   constexpr int MLBYTES = 4 * ROWS * 2 * 4;
@@ -422,16 +420,14 @@ attn_kernel(const AttnArgs a) {
   // The first prefix tile goes out after Q, which the first scores need.
   Raw kr[NI], vr[NI];
   int pg[2] = {-1, -1};
-  if constexpr (kMainLoop) {
-    if (w < npt) {
-      if constexpr (MODE == kModePrefix || MODE == kModeVerify) {
+  if (w < npt) {
+    if constexpr (MODE == kModePrefix || MODE == kModeVerify) {
 #pragma unroll
-        for (int kb = 0; kb < 2; ++kb) pg[kb] = page_id(p0 + w * 32 + kb * 16 < p1 ? pt_first[kb] : -1);
-      } else {
-        prefix_pages(p0 + w * 32, p1, pg);
-      }
-      load_rows(pg, p0 + w * 32, p1, kr, vr);
+      for (int kb = 0; kb < 2; ++kb) pg[kb] = page_id(p0 + w * 32 + kb * 16 < p1 ? pt_first[kb] : -1);
+    } else {
+      prefix_pages(p0 + w * 32, p1, pg);
     }
+    load_rows(pg, p0 + w * 32, p1, kr, vr);
   }
 
   // ---- tree tables ---------------------------------------------------------
@@ -495,7 +491,7 @@ attn_kernel(const AttnArgs a) {
 
   // Q B-fragments: lane holds row rb*16 + l16, channels ks*32 + g4*8 .. +8.
   bf16x8 qf[kQInLds ? 1 : RB][KS];
-  if constexpr (!kQInLds && kNeedQ) {
+  if constexpr (!kQInLds) {
 #pragma unroll
     for (int rb = 0; rb < RB; ++rb) {
       const int rho = row0 + rb * 16 + l16;
@@ -740,267 +736,232 @@ attn_kernel(const AttnArgs a) {
   f32x4 acc[RB][DBW];
   float lse2[RB];
 
-  if constexpr (kMainLoop) {
-    int d0 = 0, d1 = 0;
-    if constexpr (MODE == kModeDraft || MODE == kModeNaive) {
-      d0 = dlo;
-      d1 = dhi;
-    }
-    const int ndt = (d1 - d0 + 31) >> 5;
-    const int nt = npt + ndt;
-    if constexpr (MODE == kModeDraft || MODE == kModeNaive) load_row_masks();
+  int d0 = 0, d1 = 0;
+  if constexpr (MODE == kModeDraft || MODE == kModeNaive) {
+    d0 = dlo;
+    d1 = dhi;
+  }
+  const int ndt = (d1 - d0 + 31) >> 5;
+  const int nt = npt + ndt;
+  if constexpr (MODE == kModeDraft || MODE == kModeNaive) load_row_masks();
 
-    float m[RB], l[RB];
-    f32x4 o[RB][DB];
+  float m[RB], l[RB];
+  f32x4 o[RB][DB];
+#pragma unroll
+  for (int rb = 0; rb < RB; ++rb) {
+    m[rb] = kNegInf;
+    l[rb] = 0.f;
+#pragma unroll
+    for (int db = 0; db < DB; ++db) o[rb][db] = f32x4{0.f, 0.f, 0.f, 0.f};
+  }
+  uint16_t* st = reinterpret_cast<uint16_t*>(smem) + w * STAGE;
+
+  // Tile tau covers prefix keys p0 + 32*tau .. for tau < npt, then draft
+  // tokens d0 + 32*(tau - npt) .. .  pg always holds the pages of the next
+  // prefix tile to be loaded.
+  auto pages_of = [&](int tau, int (&pg)[2]) {
+    if (tau < npt) {
+      prefix_pages(p0 + tau * 32, p1, pg);
+    } else {
+      pg[0] = -1;
+      pg[1] = -1;
+    }
+  };
+  int ok = 3;
+  auto issue = [&](int tau) {
+    if (tau < npt) {
+      load_rows(pg, p0 + tau * 32, p1, kr, vr);
+      ok = 3;
+    } else {
+      load_draft(d0 + (tau - npt) * 32, d1, kr, vr, ok);
+    }
+  };
+  // Prefix-only launches (pass A, verify) prefetch without branches: past the
+  // wave's last tile the "next" tile is the current one again (L2-resident,
+  // never used), so the load sequence and its wait counts are the same every
+  // iteration.
+  constexpr bool kPrefixOnly = MODE == kModePrefix || MODE == kModeVerify;
+  if (w < nt) {
+    if (w >= npt) issue(w);  // a draft tile (prefix tiles were requested above)
+    pages_of(w + 4 < nt ? w + 4 : w, pg);
+  }
+  // The draft wave of a verify launch: its first draft tile is requested in
+  // place of the prefetch past its last prefix tile.
+  const bool verify_drafts = MODE == kModeVerify && split == 0 && dlo < dhi && w == kDraftWave;
+  if (verify_drafts && w >= nt) load_draft(dlo, dhi, kr, vr, ok);
+  // Each tile's P·V is issued one iteration late, in one block with the
+  // next tile's softmax exponentials, so that the matrix pipe works through
+  // it while the VALU computes the weights (one wave per SIMD has no other
+  // wave to overlap with).  The deferred tile keeps its P^T fragments, its
+  // V^T fragments (read out of the stage before the stage is overwritten)
+  // and the rescale the following softmax asks for; the rescale is applied
+  // before that tile's P·V, since its P is relative to the raised max.
+  // Before the first tile the deferred operands are zeros: an exact no-op.
+  bf16x8 pv_p[RB], pv_v[DB];
+  float pv_alpha[RB];
+  bool pv_rescale = false;
+#pragma unroll
+  for (int rb = 0; rb < RB; ++rb) pv_p[rb] = bf16x8{};
+  auto rescale_o = [&](const float (&alpha)[RB]) {
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb)
+#pragma unroll
+      for (int db = 0; db < DB; ++db) o[rb][db] *= alpha[rb];
+  };
+  for (int tau = w; tau < nt; tau += 4) {
+    const int nxt = tau + 4;
+    const bool is_prefix = tau < npt;
+    const int base = is_prefix ? p0 + tau * 32 : d0 + (tau - npt) * 32;
+    const int end = is_prefix ? p1 : d1;
+    // V of the deferred tile leaves the stage (zeros before the first tile).
+    const bool first = tau == w;
+#pragma unroll
+    for (int db = 0; db < DB; ++db) {
+      const bf16x8 vf = vt_frag(st, db);
+      pv_v[db] = first ? bf16x8{} : vf;
+    }
+    // Stage this tile, then reuse its registers for the next tile's loads,
+    // which then have a whole iteration to land.
+    stage(kr, vr, is_prefix, ok, st);
+    if constexpr (kPrefixOnly) {
+      if (verify_drafts && nxt >= nt) {
+        load_draft(dlo, dhi, kr, vr, ok);
+      } else {
+        const int ld = nxt < nt ? nxt : tau;
+        load_rows(pg, p0 + ld * 32, p1, kr, vr);
+        pages_of(nxt + 4 < nt ? nxt + 4 : ld, pg);
+      }
+    } else {
+      if (nxt < nt) issue(nxt);
+      if (nxt + 4 < nt) pages_of(nxt + 4, pg);
+    }
+    if (pv_rescale) rescale_o(pv_alpha);
+    f32x4 s[RB][2];
+    scores(st, s);
+    if (!is_prefix) {
+      mask_draft(base, end, s);
+    } else if (base + 32 > end) {
+      mask_prefix(base, end, s);
+    }
+    float alpha[RB];
+    const bool resc = __any(softmax_max(s, m, alpha));
+    bf16x8 pf[RB];
+    softmax_exp(s, m, l, alpha, pf);
+#pragma unroll
+    for (int db = 0; db < DB; ++db)
+#pragma unroll
+      for (int rb = 0; rb < RB; ++rb) o[rb][db] = mfma16(pv_v[db], pv_p[rb], o[rb][db]);
+    // The compiler interleaves these matrix instructions with the VALU
+    // work around them: fixed patterns of one MFMA per 2, 3 or 5 VALU
+    // instructions measured 1-2 % slower on the verify kernel.
 #pragma unroll
     for (int rb = 0; rb < RB; ++rb) {
-      m[rb] = kNegInf;
-      l[rb] = 0.f;
-#pragma unroll
-      for (int db = 0; db < DB; ++db) o[rb][db] = f32x4{0.f, 0.f, 0.f, 0.f};
+      pv_p[rb] = pf[rb];
+      pv_alpha[rb] = alpha[rb];
     }
-    uint16_t* st = reinterpret_cast<uint16_t*>(smem) + w * STAGE;
-
-    // Tile tau covers prefix keys p0 + 32*tau .. for tau < npt, then draft
-    // tokens d0 + 32*(tau - npt) .. .  pg always holds the pages of the next
-    // prefix tile to be loaded.
-    auto pages_of = [&](int tau, int (&pg)[2]) {
-      if (tau < npt) {
-        prefix_pages(p0 + tau * 32, p1, pg);
-      } else {
-        pg[0] = -1;
-        pg[1] = -1;
-      }
-    };
-    int ok = 3;
-    auto issue = [&](int tau) {
-      if (tau < npt) {
-        load_rows(pg, p0 + tau * 32, p1, kr, vr);
-        ok = 3;
-      } else {
-        load_draft(d0 + (tau - npt) * 32, d1, kr, vr, ok);
-      }
-    };
-    // Prefix-only launches (pass A, verify) prefetch without branches: past the
-    // wave's last tile the "next" tile is the current one again (L2-resident,
-    // never used), so the load sequence and its wait counts are the same every
-    // iteration.
-    constexpr bool kPrefixOnly = MODE == kModePrefix || MODE == kModeVerify;
-    if (w < nt) {
-      if (w >= npt) issue(w);  // a draft tile (prefix tiles were requested above)
-      pages_of(w + 4 < nt ? w + 4 : w, pg);
+    pv_rescale = resc;
+  }
+  // The last tile's P·V (its V is still in the stage).
+  if (w < nt) {
+    mfma_drain();
+    if (pv_rescale) rescale_o(pv_alpha);
+#pragma unroll
+    for (int db = 0; db < DB; ++db) {
+      const bf16x8 vf = vt_frag(st, db);
+#pragma unroll
+      for (int rb = 0; rb < RB; ++rb) o[rb][db] = mfma16(vf, pv_p[rb], o[rb][db]);
     }
-    // The draft wave of a verify launch: its first draft tile is requested in
-    // place of the prefetch past its last prefix tile.
-    const bool verify_drafts = MODE == kModeVerify && split == 0 && dlo < dhi && w == kDraftWave;
-    if (verify_drafts && w >= nt) load_draft(dlo, dhi, kr, vr, ok);
-    // Each tile's P·V is issued one iteration late, in one block with the
-    // next tile's softmax exponentials, so that the matrix pipe works through
-    // it while the VALU computes the weights (one wave per SIMD has no other
-    // wave to overlap with).  The deferred tile keeps its P^T fragments, its
-    // V^T fragments (read out of the stage before the stage is overwritten)
-    // and the rescale the following softmax asks for; the rescale is applied
-    // before that tile's P·V, since its P is relative to the raised max.
-    // Before the first tile the deferred operands are zeros: an exact no-op.
-    bf16x8 pv_p[RB], pv_v[DB];
-    float pv_alpha[RB];
-    bool pv_rescale = false;
-#pragma unroll
-    for (int rb = 0; rb < RB; ++rb) pv_p[rb] = bf16x8{};
-    auto rescale_o = [&](const float (&alpha)[RB]) {
-#pragma unroll
-      for (int rb = 0; rb < RB; ++rb)
-#pragma unroll
-        for (int db = 0; db < DB; ++db) o[rb][db] *= alpha[rb];
-    };
-    for (int tau = w; tau < nt; tau += 4) {
-      const int nxt = tau + 4;
-      const bool is_prefix = tau < npt;
-      const int base = is_prefix ? p0 + tau * 32 : d0 + (tau - npt) * 32;
-      const int end = is_prefix ? p1 : d1;
-      // V of the deferred tile leaves the stage (zeros before the first tile).
-      const bool first = tau == w;
-#pragma unroll
-      for (int db = 0; db < DB; ++db) {
-        const bf16x8 vf = vt_frag(st, db);
-        pv_v[db] = first ? bf16x8{} : vf;
-      }
-      // Stage this tile, then reuse its registers for the next tile's loads,
-      // which then have a whole iteration to land.
-      stage(kr, vr, is_prefix, ok, st);
-      if constexpr (kPrefixOnly) {
-        if (verify_drafts && nxt >= nt) {
-          load_draft(dlo, dhi, kr, vr, ok);
-        } else {
-          const int ld = nxt < nt ? nxt : tau;
-          load_rows(pg, p0 + ld * 32, p1, kr, vr);
-          pages_of(nxt + 4 < nt ? nxt + 4 : ld, pg);
-        }
-      } else {
-        if (nxt < nt) issue(nxt);
-        if (nxt + 4 < nt) pages_of(nxt + 4, pg);
-      }
-      if (pv_rescale) rescale_o(pv_alpha);
+    mfma_drain();
+  }
+  if (verify_drafts) {
+    // Pass B of the chunk's rows into this wave's state: its visible draft
+    // tiles (usually one), under the in-branch ancestor mask.
+    load_row_masks();
+    for (int base = dlo; base < dhi; base += 32) {
+      if (base != dlo) load_draft(base, dhi, kr, vr, ok);
+      stage(kr, vr, false, ok, st);
       f32x4 s[RB][2];
       scores(st, s);
-      if (!is_prefix) {
-        mask_draft(base, end, s);
-      } else if (base + 32 > end) {
-        mask_prefix(base, end, s);
-      }
+      mask_draft(base, dhi, s);
       float alpha[RB];
-      const bool resc = __any(softmax_max(s, m, alpha));
       bf16x8 pf[RB];
-      softmax_exp(s, m, l, alpha, pf);
+      if (__any(softmax(s, m, l, alpha, pf))) {
 #pragma unroll
-      for (int db = 0; db < DB; ++db)
+        for (int rb = 0; rb < RB; ++rb)
 #pragma unroll
-        for (int rb = 0; rb < RB; ++rb) o[rb][db] = mfma16(pv_v[db], pv_p[rb], o[rb][db]);
-      // The compiler interleaves these matrix instructions with the VALU
-      // work around them: fixed patterns of one MFMA per 2, 3 or 5 VALU
-      // instructions measured 1-2 % slower on the verify kernel.
-#pragma unroll
-      for (int rb = 0; rb < RB; ++rb) {
-        pv_p[rb] = pf[rb];
-        pv_alpha[rb] = alpha[rb];
+          for (int db = 0; db < DB; ++db) o[rb][db] *= alpha[rb];
       }
-      pv_rescale = resc;
-    }
-    // The last tile's P·V (its V is still in the stage).
-    if (w < nt) {
-      mfma_drain();
-      if (pv_rescale) rescale_o(pv_alpha);
 #pragma unroll
       for (int db = 0; db < DB; ++db) {
         const bf16x8 vf = vt_frag(st, db);
 #pragma unroll
-        for (int rb = 0; rb < RB; ++rb) o[rb][db] = mfma16(vf, pv_p[rb], o[rb][db]);
-      }
-      mfma_drain();
-    }
-    if (verify_drafts) {
-      // Pass B of the chunk's rows into this wave's state: its visible draft
-      // tiles (usually one), under the in-branch ancestor mask.
-      load_row_masks();
-      for (int base = dlo; base < dhi; base += 32) {
-        if (base != dlo) load_draft(base, dhi, kr, vr, ok);
-        stage(kr, vr, false, ok, st);
-        f32x4 s[RB][2];
-        scores(st, s);
-        mask_draft(base, dhi, s);
-        float alpha[RB];
-        bf16x8 pf[RB];
-        if (__any(softmax(s, m, l, alpha, pf))) {
-#pragma unroll
-          for (int rb = 0; rb < RB; ++rb)
-#pragma unroll
-            for (int db = 0; db < DB; ++db) o[rb][db] *= alpha[rb];
-        }
-#pragma unroll
-        for (int db = 0; db < DB; ++db) {
-          const bf16x8 vf = vt_frag(st, db);
-#pragma unroll
-          for (int rb = 0; rb < RB; ++rb) o[rb][db] = mfma16(vf, pf[rb], o[rb][db]);
-        }
-      }
-    }
-
-    mfma_drain();
-
-    // ---- merge the four waves' states (LSE identity) ----------------------
-#pragma unroll
-    for (int rb = 0; rb < RB; ++rb) l[rb] = rowgroup_sum(l[rb]);
-    if (g4 == 0) {
-#pragma unroll
-      for (int rb = 0; rb < RB; ++rb) {
-        ml[(w * ROWS + rb * 16 + l16) * 2 + 0] = m[rb];
-        ml[(w * ROWS + rb * 16 + l16) * 2 + 1] = l[rb];
-      }
-    }
-    __syncthreads();
-#pragma unroll
-    for (int rb = 0; rb < RB; ++rb) {
-      const int r = rb * 16 + l16;
-      float M = kNegInf;
-#pragma unroll
-      for (int w2 = 0; w2 < 4; ++w2) M = fmaxf(M, ml[(w2 * ROWS + r) * 2]);
-      const float ms = M == kNegInf ? 0.f : M;
-      float tot = 0.f;
-#pragma unroll
-      for (int w2 = 0; w2 < 4; ++w2)
-        tot += ml[(w2 * ROWS + r) * 2 + 1] * fast_exp2(ml[(w2 * ROWS + r) * 2] - ms);
-      // FP8 pools: the V scale multiplies every normalised output once, here.
-      const float f = tot > 0.f ? fast_exp2(m[rb] - ms) / tot * (KV8 ? a.v_scale : 1.f) : 0.f;
-      lse2[rb] = tot > 0.f ? M + fast_log2(tot) : kNegInf;
-#pragma unroll
-      for (int db = 0; db < DB; ++db) o[rb][db] *= f;
-    }
-    // Owner ow of channel blocks [ow*DBW, ow*DBW + DBW) receives the other
-    // waves' scaled blocks through LDS and sums all four in wave order.
-    float* xbuf = reinterpret_cast<float*>(smem);
-    auto slot = [](int owner, int src) { return owner * 3 + (src < owner ? src : src - 1); };
-#pragma unroll
-    for (int ow = 0; ow < 4; ++ow) {
-      if (ow == w) continue;
-      float* dst = xbuf + slot(ow, w) * XSLOT;
-#pragma unroll
-      for (int rb = 0; rb < RB; ++rb)
-#pragma unroll
-        for (int dbl = 0; dbl < DBW; ++dbl)
-          *reinterpret_cast<f32x4*>(dst + ((rb * DBW + dbl) * 64 + lane) * 4) = o[rb][ow * DBW + dbl];
-    }
-    __syncthreads();
-#pragma unroll
-    for (int rb = 0; rb < RB; ++rb) {
-#pragma unroll
-      for (int dbl = 0; dbl < DBW; ++dbl) {
-        f32x4 own = o[rb][dbl];
-#pragma unroll
-        for (int ow = 1; ow < 4; ++ow)
-          if (ow == w) own = o[rb][ow * DBW + dbl];
-        f32x4 sum = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int w2 = 0; w2 < 4; ++w2) {
-          const f32x4 x = w2 == w ? own
-                                  : *reinterpret_cast<const f32x4*>(
-                                        xbuf + slot(w, w2) * XSLOT + ((rb * DBW + dbl) * 64 + lane) * 4);
-          sum += x;
-        }
-        acc[rb][dbl] = sum;
+        for (int rb = 0; rb < RB; ++rb) o[rb][db] = mfma16(vf, pf[rb], o[rb][db]);
       }
     }
   }
 
-  if constexpr (kFinish) {
-    // Merge the prefix split partials of these rows (fixed split order).
-    int nsp = (L + a.split_len - 1) / a.split_len;
-    if constexpr (MODE == kModeVerifyFinish) nsp = nsp > 0 ? nsp : 1;  // split 0 holds the drafts
-    const int64_t plane = (int64_t)a.total_rows * a.num_qo_heads;
+  mfma_drain();
+
+  // ---- merge the four waves' states (LSE identity) ----------------------
+#pragma unroll
+  for (int rb = 0; rb < RB; ++rb) l[rb] = rowgroup_sum(l[rb]);
+  if (g4 == 0) {
 #pragma unroll
     for (int rb = 0; rb < RB; ++rb) {
+      ml[(w * ROWS + rb * 16 + l16) * 2 + 0] = m[rb];
+      ml[(w * ROWS + rb * 16 + l16) * 2 + 1] = l[rb];
+    }
+  }
+  __syncthreads();
 #pragma unroll
-      for (int dbl = 0; dbl < DBW; ++dbl) acc[rb][dbl] = f32x4{0.f, 0.f, 0.f, 0.f};
-      lse2[rb] = kNegInf;
-      if (!row_valid(rb)) continue;
-      const int64_t orow = row_out(rb);
-      float M = kNegInf;
-      for (int sp = 0; sp < nsp; ++sp) M = fmaxf(M, a.ws_lse[sp * plane + orow]);
-      const float ms = M == kNegInf ? 0.f : M;
-      float tot = 0.f;
-      for (int sp = 0; sp < nsp; ++sp) {
-        const float wgt = fast_exp2(a.ws_lse[sp * plane + orow] - ms);
-        tot += wgt;
+  for (int rb = 0; rb < RB; ++rb) {
+    const int r = rb * 16 + l16;
+    float M = kNegInf;
 #pragma unroll
-        for (int dbl = 0; dbl < DBW; ++dbl) {
-          const f32x4 x = *reinterpret_cast<const f32x4*>(
-              a.ws_o + (sp * plane + orow) * D + (w * DBW + dbl) * 16 + g4 * 4);
-          if (wgt != 0.f) acc[rb][dbl] += wgt * x;
-        }
+    for (int w2 = 0; w2 < 4; ++w2) M = fmaxf(M, ml[(w2 * ROWS + r) * 2]);
+    const float ms = M == kNegInf ? 0.f : M;
+    float tot = 0.f;
+#pragma unroll
+    for (int w2 = 0; w2 < 4; ++w2)
+      tot += ml[(w2 * ROWS + r) * 2 + 1] * fast_exp2(ml[(w2 * ROWS + r) * 2] - ms);
+    // FP8 pools: the V scale multiplies every normalised output once, here.
+    const float f = tot > 0.f ? fast_exp2(m[rb] - ms) / tot * (KV8 ? a.v_scale : 1.f) : 0.f;
+    lse2[rb] = tot > 0.f ? M + fast_log2(tot) : kNegInf;
+#pragma unroll
+    for (int db = 0; db < DB; ++db) o[rb][db] *= f;
+  }
+  // Owner ow of channel blocks [ow*DBW, ow*DBW + DBW) receives the other
+  // waves' scaled blocks through LDS and sums all four in wave order.
+  float* xbuf = reinterpret_cast<float*>(smem);
+  auto slot = [](int owner, int src) { return owner * 3 + (src < owner ? src : src - 1); };
+#pragma unroll
+  for (int ow = 0; ow < 4; ++ow) {
+    if (ow == w) continue;
+    float* dst = xbuf + slot(ow, w) * XSLOT;
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb)
+#pragma unroll
+      for (int dbl = 0; dbl < DBW; ++dbl)
+        *reinterpret_cast<f32x4*>(dst + ((rb * DBW + dbl) * 64 + lane) * 4) = o[rb][ow * DBW + dbl];
+  }
+  __syncthreads();
+#pragma unroll
+  for (int rb = 0; rb < RB; ++rb) {
+#pragma unroll
+    for (int dbl = 0; dbl < DBW; ++dbl) {
+      f32x4 own = o[rb][dbl];
+#pragma unroll
+      for (int ow = 1; ow < 4; ++ow)
+        if (ow == w) own = o[rb][ow * DBW + dbl];
+      f32x4 sum = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int w2 = 0; w2 < 4; ++w2) {
+        const f32x4 x = w2 == w ? own
+                                : *reinterpret_cast<const f32x4*>(
+                                      xbuf + slot(w, w2) * XSLOT + ((rb * DBW + dbl) * 64 + lane) * 4);
+        sum += x;
       }
-      const float inv = tot > 0.f ? 1.f / tot : 0.f;
-#pragma unroll
-      for (int dbl = 0; dbl < DBW; ++dbl) acc[rb][dbl] *= inv;
-      lse2[rb] = tot > 0.f ? M + fast_log2(tot) : kNegInf;
+      acc[rb][dbl] = sum;
     }
   }
 

@@ -21,8 +21,6 @@ static void go(K kernel, dim3 g, dim3 b, hipStream_t s, hipEvent_t e0, hipEvent_
   }
 }
 
-// FP8 pools only need the modes that read keys; the split merges read the
-// fp32 workspace and are launched from the bf16 unit.
 template <int D, int RB, bool KV8>
 static hipError_t launch_rb(int mode, const AttnArgs& a, int grid, hipStream_t s, hipEvent_t e0,
                             hipEvent_t e1) {
@@ -32,14 +30,6 @@ static hipError_t launch_rb(int mode, const AttnArgs& a, int grid, hipStream_t s
     case kModeDraft: go(attn_kernel<D, RB, kModeDraft, KV8>, g, b, s, e0, e1, a); break;
     case kModeVerify: go(attn_kernel<D, RB, kModeVerify, KV8>, g, b, s, e0, e1, a); break;
     case kModeNaive: go(attn_kernel<D, RB, kModeNaive, KV8>, g, b, s, e0, e1, a); break;
-    case kModePrefixFinish:
-      if constexpr (KV8) return hipErrorInvalidValue;
-      else go(attn_kernel<D, RB, kModePrefixFinish>, g, b, s, e0, e1, a);
-      break;
-    case kModeVerifyFinish:
-      if constexpr (KV8) return hipErrorInvalidValue;
-      else go(attn_kernel<D, RB, kModeVerifyFinish>, g, b, s, e0, e1, a);
-      break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
@@ -62,6 +52,12 @@ static inline hipError_t launch_rows(int mode, const AttnArgs& a, int grid, hipS
   }
   return hipGetLastError();
 }
+
+// Pair kernel (head_dim 128): pass A or the fused verify pass over chunks of
+// a.chunk_rows query rows; defined where pair_kernel.h is included.
+template <bool KV8>
+static hipError_t launch_pair(int mode, const AttnArgs& a, int grid, hipStream_t s, hipEvent_t e0,
+                              hipEvent_t e1);
 
 template <int D, bool KV8>
 static hipError_t launch_any_rb(int mode, int rb, const AttnArgs& a, int grid, hipStream_t s,

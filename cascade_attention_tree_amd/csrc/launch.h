@@ -26,7 +26,17 @@ hipError_t launch_attn_d128_fp8(int mode, int rb, const AttnArgs& a, int grid, h
 hipError_t launch_rows_d128(int mode, const AttnArgs& a, int grid, hipStream_t s, hipEvent_t ev_start,
                             hipEvent_t ev_stop);
 
+// Pair kernel, head_dim 128 (bf16 / FP8 pools), modes kModePrefix and
+// kModeVerify: a.n_chunks chunks of a.chunk_rows rows per (request, kv head),
+// grid = a.grid_splits * (items rounded up to a multiple of 8) * a.n_chunks.
+hipError_t launch_pair_d128(int mode, const AttnArgs& a, int grid, hipStream_t s, hipEvent_t ev_start,
+                            hipEvent_t ev_stop);
+hipError_t launch_pair_d128_fp8(int mode, const AttnArgs& a, int grid, hipStream_t s, hipEvent_t ev_start,
+                                hipEvent_t ev_stop);
+
 hipError_t launch_merge(const MergeArgs& a, hipStream_t s);
+// Merge of key-split partial states; e1 (may be null): event recorded when it ends.
+hipError_t launch_split_merge(const SplitMergeArgs& a, hipStream_t s, hipEvent_t e1);
 hipError_t launch_append_kv(const AppendArgs& a, hipStream_t s);
 hipError_t launch_stream_read(const void* buf, size_t bytes, unsigned int* sink, hipStream_t s);
 hipError_t launch_commit(const CommitArgs& a, hipStream_t s);
@@ -45,5 +55,7 @@ hipError_t read_error_d128(int* v, int clear);
 hipError_t read_error_d64_fp8(int* v, int clear);
 hipError_t read_error_d128_fp8(int* v, int clear);
 hipError_t read_error_small(int* v, int clear);
+hipError_t read_error_pair_d128(int* v, int clear);
+hipError_t read_error_pair_d128_fp8(int* v, int clear);
 
 }  // namespace casc

@@ -1,6 +1,8 @@
 // The standalone merge of two attention states, and the debug hooks that
 // expose the paged gather and the draft mask exactly as the attention kernels
 // compute them (same helpers from device_common.h).
+#include <hip/hip_ext.h>
+
 #include "device_common.h"
 #include "launch.h"
 
@@ -38,6 +40,66 @@ __global__ void __launch_bounds__(256) merge_state_kernel(const MergeArgs a) {
     *reinterpret_cast<f32x4*>(reinterpret_cast<float*>(a.o) + r * a.head_dim + c) = out;
   }
   if (c == 0 && a.lse) a.lse[r] = lse;
+}
+
+// Key-split merge: the partial states a split prefix pass left in the
+// workspace are merged per (row, head) with the LSE identity (cascade page,
+// splittability of standard attention), splits in order.  A request with L
+// keys has partials for splits 0 .. ceil(L / split_len) - 1 (the fused
+// verify pass also for split 0 when L = 0: it holds the drafts); no partial
+// means o = 0, LSE = -inf.  One thread per 4 channels of one (row, head):
+// every partial of that slice is loaded before any is combined.
+__global__ void __launch_bounds__(256) split_merge_kernel(const SplitMergeArgs a) {
+  const int d4 = a.head_dim >> 2;
+  const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  const int64_t plane = (int64_t)a.total_rows * a.num_qo_heads;
+  if (idx >= plane * d4) return;
+  const int64_t rh = idx / d4;              // row * Hq + head
+  const int c = (int)(idx - rh * d4) * 4;
+  const int row = (int)(rh / a.num_qo_heads);
+  // The request whose rows contain `row`: the last one starting at or before it.
+  int lo = 0, hi = a.batch_size - 1;
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if (a.branch_qo_indptr[a.req_branch_indptr[mid]] <= row) lo = mid; else hi = mid - 1;
+  }
+  int L = a.cache_seqlens[lo];
+  L = L < 0 ? 0 : (L > a.len_cap ? a.len_cap : L);
+  int nsp = (L + a.split_len - 1) / a.split_len;
+  if (a.verify && nsp < 1) nsp = 1;
+  if (nsp > a.n_splits) nsp = a.n_splits;
+  float M = kNegInf;
+  for (int sp = 0; sp < nsp; ++sp) M = fmaxf(M, a.ws_lse[sp * plane + rh]);
+  const float ms = M == kNegInf ? 0.f : M;
+  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+  float tot = 0.f;
+  for (int sp = 0; sp < nsp; ++sp) {
+    const float wgt = fast_exp2(a.ws_lse[sp * plane + rh] - ms);
+    const f32x4 x = *reinterpret_cast<const f32x4*>(a.ws_o + (sp * plane + rh) * a.head_dim + c);
+    tot += wgt;
+    if (wgt != 0.f) acc += wgt * x;
+  }
+  const float inv = tot > 0.f ? 1.f / tot : 0.f;
+  acc *= inv;
+  if (a.o_bf16) {
+    *reinterpret_cast<u32x2*>(reinterpret_cast<uint16_t*>(a.o) + rh * a.head_dim + c) =
+        u32x2{pack_bf16x2(acc[0], acc[1]), pack_bf16x2(acc[2], acc[3])};
+  } else {
+    *reinterpret_cast<f32x4*>(reinterpret_cast<float*>(a.o) + rh * a.head_dim + c) = acc;
+  }
+  if (c == 0 && a.lse) a.lse[rh] = tot > 0.f ? (M + fast_log2(tot)) * kLn2 : kNegInf;
+}
+
+hipError_t launch_split_merge(const SplitMergeArgs& a, hipStream_t s, hipEvent_t e1) {
+  const int64_t n = (int64_t)a.total_rows * a.num_qo_heads * (a.head_dim / 4);
+  if (n == 0) return hipSuccess;
+  const dim3 g((unsigned)((n + 255) / 256)), b(256);
+  if (e1) {
+    hipExtLaunchKernelGGL(split_merge_kernel, g, b, 0, s, nullptr, e1, 0, a);
+  } else {
+    hipLaunchKernelGGL(split_merge_kernel, g, b, 0, s, a);
+  }
+  return hipGetLastError();
 }
 
 // Copies `count` tokens of one kv head with the gather functions of the
