@@ -218,6 +218,122 @@ def test_graph_captured_multi_layer_step(B):
     assert np.max(np.abs(o - ro)) <= 1e-2
 
 
+def _move_page_on_device(x, i, p, old, new_page):
+    """Moves logical page p of request i from physical page `old` to
+    `new_page` in place: the page's K/V are copied, then the block-table entry
+    is rewritten (the device buffers keep their addresses)."""
+    for pool in (x.k_pool, x.v_pool):
+        pool[new_page].copy_(pool[old])
+    x.page_table[i, p] = new_page
+
+
+def test_graph_replay_after_in_place_table_updates(B):
+    """One serving step -- draft-KV append, fused verify, commit of the accepted
+    rows with in-place lengths -- captured once in a HIP graph and replayed
+    while, between replays, block-table entries are rewritten in place (pages
+    moved to fresh physical pages), the committed lengths grow on the device,
+    and new draft values and acceptance lists are written into the captured
+    buffers (the KV-cache tutorial's CUDA-Graph note: update the block-table
+    contents, replay without re-capture).  Every replay must equal the same
+    step run eagerly on a second copy of the state, bit for bit (outputs,
+    pools, lengths), and the final step must match the oracle."""
+    n_steps = 4
+    base = W.build_workload("replay", [300, 120, 64], [[3, 3, 2], [4], [2, 5]], 8, 2, 128, 16, seed=66)
+    w = with_room(base, 3 * n_steps + 4)
+    # fresh pages at the end of the pool, targets of the in-place remaps
+    extra = 2 * n_steps
+    fresh = np.full((extra,) + w.k_pool.shape[1:], np.nan, np.float32)
+    first_fresh = w.k_pool.shape[0]
+    w.k_pool = np.concatenate([w.k_pool, fresh])
+    w.v_pool = np.concatenate([w.v_pool, fresh.copy()])
+    bound = int(w.cache_seqlens.max()) + 3 * n_steps
+    xs = {}
+    for name in ("graph", "eager"):
+        x = B.to_device(w, layout="HND")
+        x.tree.max_prefix_len = bound       # the lengths grow by up to 3 per step
+        xs[name] = x
+    ws = {k: B.workspace_for(x) for k, x in xs.items()}
+    shape = (w.total_rows, w.num_kv_heads, w.head_dim)
+    R, Hq, d = w.total_rows, w.num_qo_heads, w.head_dim
+    bufs = {}
+    for name in xs:
+        bufs[name] = dict(k=torch.zeros(shape, dtype=torch.bfloat16, device="cuda"),
+                          v=torch.zeros(shape, dtype=torch.bfloat16, device="cuda"),
+                          ind=torch.zeros(w.batch_size + 1, dtype=torch.int32, device="cuda"),
+                          rows=torch.zeros(3 * w.batch_size, dtype=torch.int32, device="cuda"),
+                          o=torch.empty((R, Hq, d), dtype=torch.bfloat16, device="cuda"),
+                          lse=torch.empty((R, Hq), dtype=torch.float32, device="cuda"))
+
+    def step(name):
+        x, b = xs[name], bufs[name]
+        B.cascade_append_draft_kv(x, b["k"], b["v"])
+        B.cascade_verify_attn(x, o=b["o"], lse=b["lse"], workspace=ws[name])
+        B.cascade_commit_accepted(x, b["ind"], b["rows"], 3)
+
+    # capture the step once (its inputs are the buffers above); capturing
+    # runs nothing, so both copies still hold the same state
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    note("graph replay: capture")
+    with torch.cuda.graph(g):
+        step("graph")
+    torch.cuda.synchronize()
+    qo, rbi = w.branch_qo_indptr, w.req_branch_indptr
+    rng = np.random.default_rng(67)
+    for it in range(n_steps):
+        # in place, on both copies: draft values, acceptance, a page move
+        gen = torch.Generator().manual_seed(300 + it)
+        kn = torch.randn(shape, generator=gen).to(torch.bfloat16)
+        vn = torch.randn(shape, generator=gen).to(torch.bfloat16)
+        acc, ind = [], [0]
+        for i in range(w.batch_size):
+            j = int(rbi[i] + rng.integers(int(rbi[i + 1] - rbi[i])))
+            n = int(rng.integers(0, min(3, int(qo[j + 1] - qo[j])) + 1))
+            acc += list(range(int(qo[j]), int(qo[j]) + n))
+            ind.append(len(acc))
+        i_move = it % w.batch_size
+        p_move = int(rng.integers(max(1, -(-int(w.cache_seqlens[i_move]) // w.page_size))))
+        for name in xs:
+            b = bufs[name]
+            b["k"].copy_(kn)
+            b["v"].copy_(vn)
+            b["ind"].copy_(torch.tensor(ind, dtype=torch.int32))
+            b["rows"].zero_()
+            if acc:
+                b["rows"][:len(acc)].copy_(torch.tensor(acc, dtype=torch.int32))
+        old, new_page = int(w.page_table[i_move, p_move]), first_fresh + it
+        for x in xs.values():
+            _move_page_on_device(x, i_move, p_move, old, new_page)
+        w.k_pool[new_page] = w.k_pool[old]
+        w.v_pool[new_page] = w.v_pool[old]
+        w.page_table[i_move, p_move] = new_page
+        torch.cuda.synchronize()
+        note(f"graph replay {it}: move request {i_move} page {p_move}, accept {len(acc)} rows")
+        g.replay()
+        torch.cuda.synchronize()
+        step("eager")
+        torch.cuda.synchronize()
+        xg, xe, bg, be = xs["graph"], xs["eager"], bufs["graph"], bufs["eager"]
+        assert torch.equal(bg["o"], be["o"]) and torch.equal(bg["lse"], be["lse"])
+        assert torch.equal(xg.cache_seqlens, xe.cache_seqlens)
+        assert torch.equal(xg.k_pool.view(torch.int16), xe.k_pool.view(torch.int16))
+        assert torch.equal(xg.v_pool.view(torch.int16), xe.v_pool.view(torch.int16))
+        # the oracle follows the same step on the host copy
+        ko, vo = O.append_draft_kv(w, kn.float().numpy(), vn.float().numpy())
+        w.k_pool, w.v_pool = ko, vo
+        ro, rl = O.cascade(w)
+        o = be["o"].float().cpu().numpy().astype(np.float64)
+        l = be["lse"].cpu().numpy().astype(np.float64)
+        assert np.max(np.abs(o - ro)) <= 1e-2
+        fin = np.isfinite(rl)
+        assert np.max(np.abs(l[fin] - rl[fin])) <= 1e-3
+        kc, vc, lens = O.commit_accepted(w, np.array(ind), np.array(acc, dtype=np.int64))
+        w.k_pool, w.v_pool, w.cache_seqlens = kc, vc, lens
+        assert np.array_equal(xe.cache_seqlens.cpu().numpy(), lens)
+        assert np.array_equal(pool_bits_nhd(xe.k_pool, "HND"), W.bf16_bits(kc))
+    assert B.cascade_device_error(clear=True) == 0
+
+
 def test_stream_read_reference(B):
     buf = torch.arange(1 << 20, dtype=torch.int32, device="cuda")
     sink = torch.zeros(4, dtype=torch.int32, device="cuda")
