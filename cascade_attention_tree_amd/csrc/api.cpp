@@ -315,9 +315,15 @@ casc::SplitMergeArgs split_merge_args(const cascade_query* q, const cascade_page
   return m;
 }
 
-hipError_t launch(int mode, int head_dim, int rb, const casc::AttnArgs& a, int64_t grid, hipStream_t s,
+// Workgroups of the key-split kernel: `seg_items` (segment, kv head) pairs
+// rounded up to a multiple of the 8 XCDs, times the row chunks and splits.
+int64_t xcd_grid(int64_t seg_items, int n_chunks, int splits) { return cdiv(seg_items, 8) * 8 * n_chunks * splits; }
+
+hipError_t launch(int mode, int head_dim, int rb, casc::AttnArgs a, int64_t seg_items, int splits, hipStream_t s,
                   hipEvent_t e0 = nullptr, hipEvent_t e1 = nullptr) {
-  if (grid <= 0) return hipSuccess;
+  a.n_seg_items = (int32_t)seg_items;
+  const int64_t grid = xcd_grid(seg_items, a.n_chunks, splits);
+  if (seg_items <= 0 || grid <= 0) return hipSuccess;
   const bool fp8 = a.kv.elem_bytes == 1;
   if (head_dim == 64)
     return fp8 ? casc::launch_attn_d64_fp8(mode, rb, a, (int)grid, s, e0, e1)
@@ -344,7 +350,7 @@ hipError_t launch_row_modes(int mode, const cascade_paged_kv* kv,
   }
   const int64_t rows = (int64_t)t->max_request_rows * p.group;
   if (kv->head_dim != 128 || kv_fp8(kv) || rows < kRowKernelMinRows)
-    return launch(mode, kv->head_dim, p.rb, a, p.items * splits, s, e0, e1);
+    return launch(mode, kv->head_dim, p.rb, a, (int64_t)t->batch_size * kv->num_kv_heads, splits, s, e0, e1);
   a.n_chunks = (int)(rows > 0 ? cdiv(rows, casc::kRowsPerItem) : 1);
   const int64_t grid = (int64_t)t->batch_size * kv->num_kv_heads * a.n_chunks * splits;
   if (grid <= 0) return hipSuccess;
@@ -363,7 +369,8 @@ thread_local KernelTiming g_timing;
 cascade_status check_grid(int64_t grid);
 cascade_status check_plan_grid(const cascade_tree* t, const cascade_paged_kv* kv, const Plan& p) {
   const int64_t pair = p.pair ? pair_grid_per_split(t, kv, p) * p.n_splits : 0;
-  return check_grid(pair > p.items * p.n_splits ? pair : p.items * p.n_splits);
+  const int64_t ks = xcd_grid((int64_t)t->batch_size * kv->num_kv_heads, p.n_chunks, p.n_splits);
+  return check_grid(pair > ks ? pair : ks);
 }
 cascade_status check_grid(int64_t grid) {
   if (grid > INT32_MAX) return fail(CASCADE_ERR_SHAPE, "launch too large (%lld work items)", (long long)grid);
@@ -436,7 +443,7 @@ cascade_status cascade_draft_attn(const cascade_query* q, const cascade_paged_kv
   if (o_b && !aligned16(o_b)) return fail(CASCADE_ERR_UNSUPPORTED, "o_b must be 16-byte aligned");
   Plan p = plan_request(q, kv, t);
   p.n_splits = 1;
-  if ((st = check_grid(p.items)) != CASCADE_OK) return st;
+  if ((st = check_grid(xcd_grid((int64_t)t->batch_size * kv->num_kv_heads, p.n_chunks, 1))) != CASCADE_OK) return st;
   if (q->total_rows == 0 || t->batch_size == 0) return CASCADE_OK;
   casc::AttnArgs a = make_args(q, kv, t, p);
   a.o = o_b;
@@ -549,13 +556,14 @@ cascade_status naive_expand(const cascade_query* q, const cascade_paged_kv* kv, 
   p.items = (int64_t)t->num_branches * kv->num_kv_heads * p.n_chunks;
   p.n_splits = 1;
   p.split_len = 32;
-  if ((st = check_grid(p.items)) != CASCADE_OK) return st;
+  if ((st = check_grid(xcd_grid((int64_t)t->num_branches * kv->num_kv_heads, p.n_chunks, 1))) != CASCADE_OK) return st;
   if (q->total_rows == 0 || t->num_branches == 0) return CASCADE_OK;
   casc::AttnArgs a = make_args(q, kv, t, p);
   a.o = o;
   a.o_bf16 = o_dtype == CASCADE_BF16;
   a.lse = lse;
-  const hipError_t e = launch(casc::kModeNaive, kv->head_dim, p.rb, a, p.items, static_cast<hipStream_t>(stream));
+  const hipError_t e = launch(casc::kModeNaive, kv->head_dim, p.rb, a, (int64_t)t->num_branches * kv->num_kv_heads,
+                              1, static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return hip_fail(e, "naive expand launch");
   return CASCADE_OK;
 }

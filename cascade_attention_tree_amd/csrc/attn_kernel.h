@@ -183,16 +183,19 @@ attn_kernel(const AttnArgs a) {
   const int g4 = lane >> 4;
 
   // ---- work item -------------------------------------------------------
-  // Key splits vary slowest and row chunks fastest, so that consecutive
-  // workgroups -- which go to different XCDs round-robin -- take different
-  // chunks, heads and requests of one split: every XCD gets a like share of
-  // the (uneven) work when requests differ in length and row count.
-  int item = blockIdx.x;
+  // Key splits vary slowest, so that every XCD gets a like share of each
+  // split's (uneven) work when requests differ in length and row count.
+  // Within a split, workgroup u goes to XCD u % 8 (round-robin dispatch) and
+  // u / 8 walks the row chunks of one (segment, kv head) pair, then the next
+  // pair of that XCD: the chunks of a pair run side by side on one L2, which
+  // serves every chunk after the first its prefix tiles.
   const int per_split = (int)gridDim.x / a.grid_splits;
-  const int split = item / per_split;
-  item -= split * per_split;
-  const int chunk = item % a.n_chunks;
-  item /= a.n_chunks;
+  const int split = (int)blockIdx.x / per_split;
+  const int u = (int)blockIdx.x - split * per_split;
+  const int v8 = u >> 3;
+  const int chunk = v8 % a.n_chunks;
+  const int item = (v8 / a.n_chunks) * 8 + (u & 7);
+  if (item >= a.n_seg_items) return;
   const int g = item % a.num_kv_heads;
   const int seg = item / a.num_kv_heads;
 

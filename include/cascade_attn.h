@@ -187,9 +187,11 @@ CASCADE_API cascade_status merge_state(const float *o_a, const float *lse_a, con
                            void *stream);
 
 /* The whole cascade in as few launches as the shapes allow: pass A, pass B and
- * the merge fused in one kernel when the prefix runs unsplit; otherwise the
- * split prefix pass, then one kernel that merges the splits, runs pass B and
- * merges.  o [total_rows, Hq, head_dim] in o_dtype, lse float32 (nullable). */
+ * the merge fused in one kernel when the prefix runs unsplit; otherwise a
+ * first kernel runs pass A over the prefix splits (pass B joins the state of
+ * split 0) and writes one partial state per split to the workspace, and a
+ * second kernel merges the partial states with the same LSE identity.
+ * o [total_rows, Hq, head_dim] in o_dtype, lse float32 (nullable). */
 CASCADE_API cascade_status cascade_verify_attn(const cascade_query *q, const cascade_paged_kv *kv,
                                    const cascade_tree *tree, void *o, cascade_dtype o_dtype,
                                    float *lse, void *workspace, size_t workspace_bytes,
@@ -240,7 +242,9 @@ CASCADE_API cascade_status cascade_debug_mask(const cascade_tree *tree, int32_t 
  * kernel met a page id or row outside its bounds.  Synchronises the device. */
 CASCADE_API cascade_status cascade_device_error(int32_t *flag_out, int32_t clear);
 
-/* The serving step around verification (tutorial page, sections 5.2 and 8):
+/* The serving step around verification (tutorial page, section 5.2: pages
+ * through the block table; section 7, 7.1 and 7.6: the verify and rollback
+ * loop, where rejected drafts are dropped by not advancing the length):
  *
  * cascade_append_draft_kv writes the K and V of every query row's draft token
  * into its page before the verify pass reads them: row r, position u of branch

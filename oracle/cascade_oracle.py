@@ -114,7 +114,8 @@ def scatter_slots(pool, table_row, first_slot, values, page_size):
 
 
 # ---------------------------------------------------------------------------
-# The serving step around verification (tutorial page, sections 5.2 and 8):
+# The serving step around verification (tutorial page, section 5.2, pages
+# through the block table; section 7, 7.1 and 7.6, the verify and rollback loop):
 # the drafts' K/V are written into their pages before the verify pass, and
 # after it the accepted path's K/V join the request's prefix.
 # ---------------------------------------------------------------------------
