@@ -465,6 +465,8 @@ def main():
                     help="for profiling: only the GQA verify configuration (cold steps)")
     ap.add_argument("--ragged-only", action="store_true",
                     help="for profiling: only the ragged configuration (cold steps)")
+    ap.add_argument("--prefix-hit-only", action="store_true",
+                    help="for profiling: only the prefix-hit suffix prefill (cold steps)")
     ap.add_argument("--traffic-probe", action="store_true",
                     help="for hardware-counter runs: one plain 256 MiB device copy (known bytes), "
                          "then a few flushed verify steps and naive-expand steps; prints nothing else")
@@ -484,12 +486,15 @@ def main():
     def flush():
         torch.sum(flush_buf, dim=0, out=flush_out)   # reads 1 GiB, writes 4 bytes
 
-    if args.gqa_only or args.ragged_only:
+    if args.gqa_only or args.ragged_only or args.prefix_hit_only:
         print("bench: profiling leg only", file=sys.stderr, flush=True)
-        out = (gqa_timing(B, W, torch, flush, args.steps, args.warmup) if args.gqa_only
-               else ragged_timing(B, W, torch, flush, steps=args.steps, warmup=args.warmup))
-        print(json.dumps({"profiling_leg": "gqa" if args.gqa_only else "ragged", **out,
-                          "kernel_hash": kernel_source_hash()}), flush=True)
+        if args.gqa_only:
+            leg, out = "gqa", gqa_timing(B, W, torch, flush, args.steps, args.warmup)
+        elif args.ragged_only:
+            leg, out = "ragged", ragged_timing(B, W, torch, flush, steps=args.steps, warmup=args.warmup)
+        else:
+            leg, out = "prefix_hit", prefix_hit_timings(B, W, torch, flush, steps=args.steps, warmup=args.warmup)
+        print(json.dumps({"profiling_leg": leg, **out, "kernel_hash": kernel_source_hash()}), flush=True)
         return
 
     print("bench: generating headline workload", file=sys.stderr, flush=True)

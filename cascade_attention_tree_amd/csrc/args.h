@@ -25,9 +25,10 @@ struct KvView {
 // Query rows per chunk of the pair kernel (three 16-row MFMA blocks).
 constexpr int kPairRows = 48;
 
-// Query rows per work item of the row-split kernel (head_dim 128): 8 waves
-// of at most 32 rows (two 16-row MFMA blocks each).
-constexpr int kRowsPerItem = 256;
+// Row-split kernel (head_dim 128): waves per workgroup, and query rows per
+// work item -- kRowWaves waves of at most 32 rows (two 16-row MFMA blocks).
+constexpr int kRowWaves = 4;
+constexpr int kRowsPerItem = kRowWaves * 32;
 
 enum AttnMode : int {
   kModePrefix = 0,        // pass A: unsplit -> (o_A, LSE_A); split -> partial states

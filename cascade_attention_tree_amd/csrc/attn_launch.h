@@ -43,7 +43,7 @@ constexpr int kRowBlocks = 2;
 
 static inline hipError_t launch_rows(int mode, const AttnArgs& a, int grid, hipStream_t s, hipEvent_t e0,
                                      hipEvent_t e1) {
-  const dim3 g(grid), b(512);
+  const dim3 g(grid), b(64 * kRowWaves);
   switch (mode) {
     case kModePrefix: go(rows_kernel<kModePrefix, kRowDepth, kRowBlocks>, g, b, s, e0, e1, a); break;
     case kModeVerify: go(rows_kernel<kModeVerify, kRowDepth, kRowBlocks>, g, b, s, e0, e1, a); break;

@@ -1,19 +1,21 @@
 // Row-split attention kernel for row-heavy launches (pass A, pass B and the
 // fused verify pass), head_dim 128, bf16 pools.
 //
-// One workgroup of 8 waves (two per SIMD) handles one work item
+// One workgroup of kRowWaves = 4 waves (one per SIMD; two workgroups share a
+// CU, so every SIMD runs two waves of independent workgroups) handles one
+// work item
 //   (request, kv head g, chunk of at most kRowsPerItem query rows, key split).
 // The chunk's rows -- the request's query tokens times the query heads that
-// share kv head g -- are dealt out to the 8 waves, at most 16 * RBW per wave
+// share kv head g -- are dealt out to the waves, at most 16 * RBW per wave
 // (RBW MFMA row blocks sharing every K and V fragment the wave reads), so
 // every wave keeps its own rows' complete online softmax state and no state
-// is merged across waves.  All 8 waves go through the same 32-key tiles in
-// lock step:
-//   * each thread loads one 16-byte chunk of K and one of V per tile (the
-//     workgroup's 512 threads cover the 32 keys x 16 chunks of a tile; the 64
-//     lanes of a wave read four whole 256-byte key rows of one page), DEPTH
-//     tiles ahead, into a ring of DEPTH register slots -- a handful of
-//     registers per tile, so many tiles are in flight;
+// is merged across waves.  The waves of a workgroup go through the same
+// 32-key tiles in lock step:
+//   * each thread loads 512 / (64 kRowWaves) 16-byte chunks of K and as many
+//     of V per tile (the workgroup's threads cover the 32 keys x 16 chunks of
+//     a tile; the 64 lanes of a wave read four whole 256-byte key rows of one
+//     page per chunk), DEPTH tiles ahead, into a ring of DEPTH register slots
+//     -- a handful of registers per tile, so many tiles are in flight;
 //   * per step the workgroup writes the next tile into one of two LDS
 //     stages, computes the current tile out of the other, and meets at one
 //     barrier;
@@ -36,8 +38,6 @@
 
 namespace casc {
 
-constexpr int kRowWaves = 8;
-
 // Mask kind of a key range, as a type for the key loop.
 template <int K>
 struct KeyKind {
@@ -45,7 +45,7 @@ struct KeyKind {
 };
 
 template <int MODE, int DEPTH, int RBW>
-__global__ void __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2)))
+__global__ void __launch_bounds__(64 * kRowWaves) __attribute__((amdgpu_waves_per_eu(2, 2)))
 rows_kernel(const AttnArgs a) {
   static_assert(MODE == kModePrefix || MODE == kModeVerify || MODE == kModeDraft, "pass A, verify, pass B");
   static_assert(DEPTH % 2 == 0, "the two LDS stages alternate within the unrolled ring");
@@ -59,6 +59,17 @@ rows_kernel(const AttnArgs a) {
   constexpr int STAGE = 2 * 32 * RS;  // bf16 elements of one stage: K tile, then V tile
   constexpr int EB = 2;  // bf16 pools
   typedef u32x4 Raw;
+  // The workgroup's NT threads cover a tile's 32 keys x 16 chunks of K (and
+  // of V); thread tid holds chunks tid + q*NT, q < CPT.
+  constexpr int NT = 64 * kRowWaves;
+  constexpr int CPT = 512 / NT;
+  static_assert(CPT * NT == 512, "whole tiles per workgroup");
+  struct Tile {
+    Raw k[CPT], v[CPT];
+  };
+  struct Pages {
+    int p[CPT];
+  };
   constexpr bool kVerify = MODE == kModeVerify;
   constexpr bool kDraft = MODE == kModeDraft;
   constexpr bool kTables = kVerify || kDraft;
@@ -212,49 +223,65 @@ rows_kernel(const AttnArgs a) {
   }
 
   // ---- prefix tile loads -------------------------------------------------
-  // Thread tid loads chunk tid % 16 of key tid / 16 of a tile: the wave's four
-  // keys (w % 4)*4 .. +4 lie in the tile's 16-key half w / 4, whose page id is
-  // wave-uniform.  The half's buffer descriptors start at its first key and
-  // end after the row of its last valid key, so keys past `p1` (and bad pages)
-  // read zeros.
-  const int half = w >> 2;
-  const int lane_off = prefix_lane_offset<EB>(kv, (w & 3) * 4 + g4, head_off, l16);
+  // Chunk e = tid + q*NT of a tile is chunk e % 16 of key e / 16: the wave's
+  // four keys of chunk q lie in the tile's 16-key half e / 256, whose page id
+  // is wave-uniform, at the same place in the half for every q.  The half's
+  // buffer descriptors start at its first key and end after the row of its
+  // last valid key, so keys past `p1` (and bad pages) read zeros.
+  auto half_of = [&](int q) { return (w * 64 + q * NT) >> 8; };
+  const int lane_off = prefix_lane_offset<EB>(kv, (w * 4 + g4) & 15, head_off, l16);
   // Page ids outside the pool are noted here and flagged once at the end: a
   // store in the key loop would count on the same counter as the K/V loads
   // and blur the loop's wait counts.
   bool bad_page = false;
-  auto page_of = [&](int tile) -> int {  // page id of this wave's half of a tile, -1 if none
-    const int first = p0 + tile * 32 + half * 16;
-    int id = first < p1 ? pt_row[first >> kv.log2_page] : -1;
-    id = __builtin_amdgcn_readfirstlane(id);
-    bad_page |= id >= kv.num_pages;
-    return checked_page(id, kv.num_pages);
-  };
-  auto load_tile = [&](int tile, int pg, Raw& kr, Raw& vr) {
-    const int first = p0 + tile * 32 + half * 16;
-    const int nvalid = min(max(p1 - first, 0), 16);
-    kr = buf_load_chunk(prefix_half_rsrc<EB>(kv.k, kv, pg, first, nvalid, head_off, D), lane_off, (Raw*)nullptr);
-    vr = buf_load_chunk(prefix_half_rsrc<EB>(kv.v, kv, pg, first, nvalid, head_off, D), lane_off, (Raw*)nullptr);
-  };
-  // Thread tid's chunk of a tile into a stage (zeros where `keep` is false).
-  const int skey = tid >> 4, sch = tid & 15;
-  auto stage = [&](const Raw& kr, const Raw& vr, bool keep, uint16_t* st) {
-    u32x4 k = widen_bf16(kr), v = widen_bf16(vr);
-    if (!keep) {
-      k = u32x4{0u, 0u, 0u, 0u};
-      v = u32x4{0u, 0u, 0u, 0u};
+  auto page_of = [&](int tile) -> Pages {  // page ids of this wave's halves of a tile, -1 if none
+    Pages pg;
+#pragma unroll
+    for (int q = 0; q < CPT; ++q) {
+      const int first = p0 + tile * 32 + half_of(q) * 16;
+      int id = first < p1 ? pt_row[first >> kv.log2_page] : -1;
+      id = __builtin_amdgcn_readfirstlane(id);
+      bad_page |= id >= kv.num_pages;
+      pg.p[q] = checked_page(id, kv.num_pages);
     }
-    *reinterpret_cast<u32x4*>(st + skey * RS + sch * 8) = k;
-    *reinterpret_cast<u32x4*>(st + 32 * RS + skey * RS + sch * 8) = v;
+    return pg;
+  };
+  auto load_tile = [&](int tile, const Pages& pg, Tile& tl) {
+#pragma unroll
+    for (int q = 0; q < CPT; ++q) {
+      const int first = p0 + tile * 32 + half_of(q) * 16;
+      const int nvalid = min(max(p1 - first, 0), 16);
+      tl.k[q] = buf_load_chunk(prefix_half_rsrc<EB>(kv.k, kv, pg.p[q], first, nvalid, head_off, D), lane_off,
+                               (Raw*)nullptr);
+      tl.v[q] = buf_load_chunk(prefix_half_rsrc<EB>(kv.v, kv, pg.p[q], first, nvalid, head_off, D), lane_off,
+                               (Raw*)nullptr);
+    }
+  };
+  // Thread tid's chunks of a tile into a stage (chunk q zeroed where bit q of
+  // `keep` is clear).
+  auto skey = [&](int q) { return (tid + q * NT) >> 4; };
+  const int sch = tid & 15;
+  constexpr int kKeepAll = (1 << CPT) - 1;
+  auto stage = [&](const Tile& tl, int keep, uint16_t* st) {
+#pragma unroll
+    for (int q = 0; q < CPT; ++q) {
+      u32x4 k = widen_bf16(tl.k[q]), v = widen_bf16(tl.v[q]);
+      if (!((keep >> q) & 1)) {
+        k = u32x4{0u, 0u, 0u, 0u};
+        v = u32x4{0u, 0u, 0u, 0u};
+      }
+      *reinterpret_cast<u32x4*>(st + skey(q) * RS + sch * 8) = k;
+      *reinterpret_cast<u32x4*>(st + 32 * RS + skey(q) * RS + sch * 8) = v;
+    }
   };
 
   // DEPTH tiles requested before the first one is staged; `pgn` holds the
-  // page of the next tile to be requested.
-  Raw kq[DEPTH], vq[DEPTH];
-  int pgn = page_of(0);
+  // pages of the next tile to be requested.
+  Tile ring[DEPTH];
+  Pages pgn = page_of(0);
 #pragma unroll
   for (int k = 0; k < DEPTH; ++k) {
-    load_tile(k, pgn, kq[k], vq[k]);
+    load_tile(k, pgn, ring[k]);
     pgn = page_of(k + 1);
   }
 
@@ -262,8 +289,8 @@ rows_kernel(const AttnArgs a) {
   const bool drafts = (kVerify && split == 0 && !slot_mode) || (kDraft && !slot_mode);
   const bool lds_bnd = nb <= NBCAP;
   int dlo = 0;
-  Raw dk, dv;  // the first draft tile, requested after the tables
-  bool dkeep = false;
+  Tile dt;  // the first draft tile, requested after the tables
+  int dkeep = 0;
   auto branch_at = [&](int x) -> int {  // local branch of request token x
     if (lds_bnd) {
       int lo = 0, hi = nb - 1;
@@ -280,45 +307,50 @@ rows_kernel(const AttnArgs a) {
     return lds_bnd ? t_dst[jl] : (a.draft_start ? a.draft_start[jb + jl] : 0);
   };
   const int64_t last_row = pool_last_row(kv, a.num_kv_heads);
-  // Key base + tid / 16 of a draft tile (request tokens), chunk tid % 16;
+  // Keys base + skey(q) of a draft tile (request tokens), chunk tid % 16;
   // zeros for keys past dhi and for bad slots or pages (flagged).
-  auto load_draft = [&](int base, Raw& kr, Raw& vr, bool& keep) {
-    const int x = base + skey;
-    int64_t off = -2;  // element offset of the key's row (kv head included)
-    if (x < dhi) {
-      if (x - dlo < KEYCAP) {
-        off = t_doff[x - dlo];
-        if (off >= 0) off += head_off;
-      } else {
-        off = draft_offset(kv, a.branch_qo_indptr, a.draft_page_table, a.draft_page_table_stride,
-                           a.draft_start, jb, je, x, g);
+  auto load_draft = [&](int base, Tile& tl, int& keep) {
+    keep = 0;
+#pragma unroll
+    for (int q = 0; q < CPT; ++q) {
+      const int x = base + skey(q);
+      int64_t off = -2;  // element offset of the key's row (kv head included)
+      if (x < dhi) {
+        if (x - dlo < KEYCAP) {
+          off = t_doff[x - dlo];
+          if (off >= 0) off += head_off;
+        } else {
+          off = draft_offset(kv, a.branch_qo_indptr, a.draft_page_table, a.draft_page_table_stride,
+                             a.draft_start, jb, je, x, g);
+        }
+        if (off == -1) atomicOr(&g_device_error, kErrPage);
       }
-      if (off == -1) atomicOr(&g_device_error, kErrPage);
+      const bool ok = off >= 0;
+      keep |= ok ? (1 << q) : 0;
+      const int64_t e = clamp_row(off, last_row) + sch * 8;
+      tl.k[q] = ok ? load_key_chunk<Raw, EB>(kv.k, e) : Raw{};
+      tl.v[q] = ok ? load_key_chunk<Raw, EB>(kv.v, e) : Raw{};
     }
-    keep = off >= 0;
-    const int64_t e = clamp_row(off, last_row) + sch * 8;
-    kr = keep ? load_key_chunk<Raw, EB>(kv.k, e) : Raw{};
-    vr = keep ? load_key_chunk<Raw, EB>(kv.v, e) : Raw{};
   };
   if constexpr (kTables) {
     if (drafts) {
       if (lds_bnd) {
-        for (int t = tid; t <= nb; t += 512) t_bnd[t] = a.branch_qo_indptr[jb + t];
-        for (int t = tid; t < nb; t += 512) t_dst[t] = a.draft_start ? a.draft_start[jb + t] : 0;
+        for (int t = tid; t <= nb; t += NT) t_bnd[t] = a.branch_qo_indptr[jb + t];
+        for (int t = tid; t < nb; t += NT) t_dst[t] = a.draft_start ? a.draft_start[jb + t] : 0;
       }
       __syncthreads();
       dlo = __builtin_amdgcn_readfirstlane(branch_start(branch_at(tok_first)));
-      for (int t = tid; t <= tok_last - tok_first; t += 512) t_rbs[t] = branch_start(branch_at(tok_first + t));
+      for (int t = tid; t <= tok_last - tok_first; t += NT) t_rbs[t] = branch_start(branch_at(tok_first + t));
       const int nk = min(dhi - dlo, KEYCAP);
       const int dstride = a.draft_page_table_stride;
-      for (int t = tid; t < nk; t += 512) {
+      for (int t = tid; t < nk; t += NT) {
         const int x = dlo + t;
         const int jl = branch_at(x);
         const int slot = branch_dstart(jl) + (x - branch_start(jl));
         t_doff[t] = draft_slot_offset(kv, a.draft_page_table + (int64_t)(jb + jl) * dstride, dstride, slot);
       }
       __syncthreads();
-      load_draft(dlo, dk, dv, dkeep);
+      load_draft(dlo, dt, dkeep);
     }
   }
 
@@ -456,8 +488,13 @@ rows_kernel(const AttnArgs a) {
   // nothing.
   auto key_loop = [&](auto kind_tag) {
     constexpr int KIND = decltype(kind_tag)::value;
-    stage(kq[0], vq[0], p0 + skey >= front, stg[0]);
-    load_tile(DEPTH, pgn, kq[0], vq[0]);
+    {
+      int keep = 0;
+#pragma unroll
+      for (int q = 0; q < CPT; ++q) keep |= p0 + skey(q) >= front ? (1 << q) : 0;
+      stage(ring[0], keep, stg[0]);
+    }
+    load_tile(DEPTH, pgn, ring[0]);
     pgn = page_of(DEPTH + 1);
     __syncthreads();
     for (int t0 = 0; t0 < nt; t0 += DEPTH) {
@@ -465,8 +502,8 @@ rows_kernel(const AttnArgs a) {
       for (int k = 0; k < DEPTH; ++k) {
         const int t = t0 + k;
         const int sn = (k + 1) % DEPTH;
-        stage(kq[sn], vq[sn], true, stg[(k + 1) & 1]);
-        load_tile(t + 1 + DEPTH, pgn, kq[sn], vq[sn]);
+        stage(ring[sn], kKeepAll, stg[(k + 1) & 1]);
+        load_tile(t + 1 + DEPTH, pgn, ring[sn]);
         pgn = page_of(t + 2 + DEPTH);
         if (wave_rows && t < nt) {
           // A slot-mode chain tile that ends at or before the wave's first
@@ -495,7 +532,7 @@ rows_kernel(const AttnArgs a) {
       pgn = page_of(0);
 #pragma unroll
       for (int j = 0; j < DEPTH; ++j) {
-        load_tile(j, pgn, kq[j], vq[j]);
+        load_tile(j, pgn, ring[j]);
         pgn = page_of(j + 1);
       }
       key_loop(KeyKind<1>{});
@@ -512,8 +549,8 @@ rows_kernel(const AttnArgs a) {
           if (tree) ranc[rb] = a.draft_mask[tok0 + rtok[rb]];
         }
       for (int base = dlo; base < dhi; base += 32) {
-        if (base != dlo) load_draft(base, dk, dv, dkeep);
-        stage(dk, dv, dkeep, stg[0]);
+        if (base != dlo) load_draft(base, dt, dkeep);
+        stage(dt, dkeep, stg[0]);
         __syncthreads();
         if (wave_rows) compute(stg[0], base, dhi, 1);
         __syncthreads();
