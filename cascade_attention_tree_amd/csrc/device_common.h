@@ -221,8 +221,12 @@ __device__ __forceinline__ uint16_t f32_to_bf16_bits(float f) {
   return __builtin_bit_cast(uint16_t, (__bf16)f);
 }
 
+// Two floats to two bf16 (RNE) in one register, lo in the low half: one
+// v_cvt_pk_bf16_f32 with both operands.
+typedef __attribute__((ext_vector_type(2))) float f32x2;
+typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2;
 __device__ __forceinline__ unsigned int pack_bf16x2(float lo, float hi) {
-  return (unsigned int)f32_to_bf16_bits(lo) | ((unsigned int)f32_to_bf16_bits(hi) << 16);
+  return __builtin_bit_cast(unsigned int, __builtin_convertvector((f32x2){lo, hi}, bf16x2));
 }
 
 }  // namespace casc
