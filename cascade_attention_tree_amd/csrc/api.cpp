@@ -106,6 +106,8 @@ casc::KvView kv_view(const cascade_paged_kv* kv) {
   v.log2_page = ilog2(kv->page_size);
   v.page_bytes = (int32_t)page_extent_bytes(kv);
   v.elem_bytes = elem_bytes(kv);
+  v.page_stride_b = (uint32_t)(kv->page_stride * elem_bytes(kv));
+  v.token_stride_b = (uint32_t)(kv->token_stride * elem_bytes(kv));
   return v;
 }
 
@@ -134,6 +136,8 @@ cascade_status check_kv(const cascade_paged_kv* kv) {
     return fail(CASCADE_ERR_UNSUPPORTED, "kv->k and kv->v must be 16-byte aligned");
   if (page_extent_bytes(kv) >= (1ll << 30))
     return fail(CASCADE_ERR_UNSUPPORTED, "one page spans more than 1 GiB");
+  if (kv->page_stride * elem_bytes(kv) >= (1ll << 31))
+    return fail(CASCADE_ERR_UNSUPPORTED, "page_stride spans 2 GiB or more");
   return CASCADE_OK;
 }
 

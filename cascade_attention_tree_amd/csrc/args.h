@@ -20,6 +20,8 @@ struct KvView {
                        // its buffer descriptor, so reads past it return zero
   int32_t elem_bytes;  // 2: bf16 elements; 1: FP8 E4M3 codes (offsets above
                        // count elements, so they are byte offsets for FP8)
+  uint32_t page_stride_b;   // page_stride and token_stride in bytes (each below
+  uint32_t token_stride_b;  // 2 GiB: the prefix tile address arithmetic is 32x32-bit)
 };
 
 // Query rows per chunk of the pair kernel (three 16-row MFMA blocks).

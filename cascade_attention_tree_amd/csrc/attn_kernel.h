@@ -332,14 +332,16 @@ attn_kernel(const AttnArgs a) {
   int lane_off[NV];
 #pragma unroll
   for (int i = 0; i < NV; ++i) lane_off[i] = prefix_lane_offset<EB>(kv, i * TPI + lane / CPR, head_off, lane % CPR);
+  const int tail_bytes = (int)((head_off + D) * EB);
   auto load_rows = [&](const int (&pg)[2], int base, int end, Raw (&kr)[NI], Raw (&vr)[NI]) {
     __amdgpu_buffer_rsrc_t rk[2], rv[2];
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
       const int first = base + kb * 16;
       const int nvalid = min(max(end - first, 0), 16);
-      rk[kb] = prefix_half_rsrc<EB>(kv.k, kv, pg[kb], first, nvalid, head_off, D);
-      rv[kb] = prefix_half_rsrc<EB>(kv.v, kv, pg[kb], first, nvalid, head_off, D);
+      const HalfSpan h = prefix_half_span(kv, pg[kb], first, nvalid, tail_bytes);
+      rk[kb] = half_rsrc(kv.k, h);
+      rv[kb] = half_rsrc(kv.v, h);
     }
 #pragma unroll
     for (int n = 0; n < NI; ++n) {

@@ -149,22 +149,40 @@ __device__ __forceinline__ u32x2 buf_load8(__amdgpu_buffer_rsrc_t r, int byte_of
 
 // Prefix tiles start at multiples of 32 slots and pages hold >= 16 tokens,
 // so each 16-key half of a tile lies in one page.  The half's buffer
-// descriptor starts at its first key's row (slot `first` of page `page`, kv
-// head at element offset `head_off`) and ends after the row of its last valid
-// key (`nvalid` keys), so lanes addressing keys past the end -- and every key
+// descriptor starts at its first key's row (slot `first` of page `page`) and
+// ends after the row of its last valid key (`nvalid` keys), kv head and head
+// dim included (`tail_bytes` = bytes from a key row's start to the end of the
+// kv head's elements), so lanes addressing keys past the end -- and every key
 // of a half whose page id is -1 (none, or outside the pool) -- read zeros.
-// EB is the pool's element size in bytes, D the head dim.  The attention
-// kernels and the prefix gather hook build their prefix loads from these two
-// functions.
+// K and V pools share their strides, so one span serves both descriptors.
+// The attention kernels and the prefix gather hook build their prefix loads
+// from these functions.
+struct HalfSpan {
+  uint64_t off;  // byte offset of the half's first key row in a pool
+  int bytes;     // descriptor range
+};
+__device__ __forceinline__ HalfSpan prefix_half_span(const KvView& kv, int page, int first, int nvalid,
+                                                     int tail_bytes) {
+  const bool ok = page >= 0 && nvalid > 0;
+  const uint32_t slot = (uint32_t)(first & ((1 << kv.log2_page) - 1));
+  const uint64_t off = ok ? (uint64_t)(uint32_t)page * kv.page_stride_b + (uint64_t)slot * kv.token_stride_b : 0;
+  // Every input is wave-uniform (a tile's keys are the same for all lanes);
+  // stating it keeps the descriptor in scalar registers -- a descriptor the
+  // compiler takes for divergent costs a loop over lanes around every load.
+  HalfSpan h;
+  h.off = ((uint64_t)__builtin_amdgcn_readfirstlane((uint32_t)(off >> 32)) << 32) |
+          (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)off);
+  h.bytes = __builtin_amdgcn_readfirstlane(ok ? (nvalid - 1) * (int)kv.token_stride_b + tail_bytes : 0);
+  return h;
+}
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t half_rsrc(const void* pool, const HalfSpan& h) {
+  return page_rsrc(static_cast<const unsigned char*>(pool) + h.off, h.bytes);
+}
 template <int EB>
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t prefix_half_rsrc(const void* pool, const KvView& kv, int page,
                                                                    int first, int nvalid, int64_t head_off,
                                                                    int D) {
-  const bool ok = page >= 0 && nvalid > 0;
-  const int64_t base = (int64_t)(ok ? page : 0) * kv.page_stride +
-                       (int64_t)(first & ((1 << kv.log2_page) - 1)) * kv.token_stride;
-  const int bytes = ok ? (int)(((int64_t)(nvalid - 1) * kv.token_stride + head_off + D) * EB) : 0;
-  return page_rsrc(static_cast<const unsigned char*>(pool) + base * EB, bytes);
+  return half_rsrc(pool, prefix_half_span(kv, page, first, nvalid, (int)((head_off + D) * EB)));
 }
 // Byte offset, inside its half's descriptor, of 8-channel chunk `chunk` of
 // the key `key` places after the half's first key.

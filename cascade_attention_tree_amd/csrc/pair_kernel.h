@@ -166,22 +166,27 @@ pair_kernel(const AttnArgs a) {
 #pragma unroll
   for (int i = 0; i < 16 / TPI; ++i) voff[i] = prefix_lane_offset<EB>(kv, i * TPI + lane / CPR, head_off, lane % CPR);
   const int koff = prefix_lane_offset<EB>(kv, l16, head_off, g4);
-  auto load_v = [&](const int (&pg)[2], int base, int end, Raw (&vr)[NL]) {
+  // The two halves' spans of a tile (one per 16 keys), shared by its K and V.
+  const int tail_bytes = (int)((head_off + D) * EB);
+  auto spans = [&](const int (&pg)[2], int base, int end, HalfSpan (&hs)[2]) {
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
       const int first = base + kb * 16;
-      const __amdgpu_buffer_rsrc_t r =
-          prefix_half_rsrc<EB>(kv.v, kv, pg[kb], first, min(max(end - first, 0), 16), head_off, D);
+      hs[kb] = prefix_half_span(kv, pg[kb], first, min(max(end - first, 0), 16), tail_bytes);
+    }
+  };
+  auto load_v = [&](const HalfSpan (&hs)[2], Raw (&vr)[NL]) {
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+      const __amdgpu_buffer_rsrc_t r = half_rsrc(kv.v, hs[kb]);
 #pragma unroll
       for (int i = 0; i < 16 / TPI; ++i) vr[kb * (16 / TPI) + i] = buf_load_chunk(r, voff[i], (Raw*)nullptr);
     }
   };
-  auto load_k = [&](const int (&pg)[2], int base, int end, Raw (&kr)[NL]) {
+  auto load_k = [&](const HalfSpan (&hs)[2], Raw (&kr)[NL]) {
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
-      const int first = base + kb * 16;
-      const __amdgpu_buffer_rsrc_t r =
-          prefix_half_rsrc<EB>(kv.k, kv, pg[kb], first, min(max(end - first, 0), 16), head_off, D);
+      const __amdgpu_buffer_rsrc_t r = half_rsrc(kv.k, hs[kb]);
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks) kr[kb * KS + ks] = buf_load_chunk(r, koff + ks * 32 * EB, (Raw*)nullptr);
     }
@@ -236,11 +241,13 @@ pair_kernel(const AttnArgs a) {
 
   Raw kr[NL], vr[NL];
   int pg[2] = {-1, -1};
+  HalfSpan hs[2];
   if (w < npt) {
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) pg[kb] = page_id(p0 + w * 32 + kb * 16 < p1 ? pt_first[kb] : -1);
-    load_v(pg, p0 + w * 32, p1, vr);
-    load_k(pg, p0 + w * 32, p1, kr);
+    spans(pg, p0 + w * 32, p1, hs);
+    load_v(hs, vr);
+    load_k(hs, kr);
   }
 
   int dlo = 0;
@@ -474,14 +481,15 @@ pair_kernel(const AttnArgs a) {
     if (verify_drafts && last) {
       load_draft(doff, vr, kv.v);
     } else {
-      load_v(pg, p0 + ld * 32, p1, vr);
+      spans(pg, p0 + ld * 32, p1, hs);
+      load_v(hs, vr);
     }
     f32x4 s[RB][2];
     scores(kr, s);
     if (verify_drafts && last) {
       load_draft(doff, kr, kv.k);
     } else {
-      load_k(pg, p0 + ld * 32, p1, kr);
+      load_k(hs, kr);
       pages_of(nxt + 4 < npt ? nxt + 4 : ld, pg);
     }
     if (base + 32 > p1) {

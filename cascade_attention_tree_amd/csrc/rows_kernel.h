@@ -246,15 +246,15 @@ rows_kernel(const AttnArgs a) {
     }
     return pg;
   };
+  const int tail_bytes = (int)((head_off + D) * EB);
   auto load_tile = [&](int tile, const Pages& pg, Tile& tl) {
 #pragma unroll
     for (int q = 0; q < CPT; ++q) {
       const int first = p0 + tile * 32 + half_of(q) * 16;
       const int nvalid = min(max(p1 - first, 0), 16);
-      tl.k[q] = buf_load_chunk(prefix_half_rsrc<EB>(kv.k, kv, pg.p[q], first, nvalid, head_off, D), lane_off,
-                               (Raw*)nullptr);
-      tl.v[q] = buf_load_chunk(prefix_half_rsrc<EB>(kv.v, kv, pg.p[q], first, nvalid, head_off, D), lane_off,
-                               (Raw*)nullptr);
+      const HalfSpan h = prefix_half_span(kv, pg.p[q], first, nvalid, tail_bytes);
+      tl.k[q] = buf_load_chunk(half_rsrc(kv.k, h), lane_off, (Raw*)nullptr);
+      tl.v[q] = buf_load_chunk(half_rsrc(kv.v, h), lane_off, (Raw*)nullptr);
     }
   };
   // Thread tid's chunks of a tile into a stage (chunk q zeroed where bit q of

@@ -105,7 +105,7 @@ hipError_t launch_split_merge(const SplitMergeArgs& a, hipStream_t s, hipEvent_t
 // Copies `count` tokens of one kv head with the gather functions of the
 // attention kernels.  which == 0, the prefix of request `index`: the token's
 // 16-key half gets its page id from the block-table row (checked_page) and
-// its buffer descriptor from prefix_half_rsrc, and the chunk is read at
+// its buffer descriptors from prefix_half_span / half_rsrc, and the chunk is read at
 // prefix_lane_offset -- the prefix tile loads of both attention kernels.
 // which == 1, the drafts of branch `index`: the slot resolves through
 // draft_slot_offset, the offset is clamped into the pool and the chunk read
@@ -129,8 +129,9 @@ __device__ __forceinline__ void debug_gather_token(const DebugArgs& a, int t, in
     const int pg = checked_page(id, kv.num_pages);
     const int nvalid = min(max(end - first, 0), 16);
     const int off = prefix_lane_offset<EB>(kv, t - first, head_off, c8);
-    k = buf_load_chunk(prefix_half_rsrc<EB>(kv.k, kv, pg, first, nvalid, head_off, a.head_dim), off, (Raw*)nullptr);
-    v = buf_load_chunk(prefix_half_rsrc<EB>(kv.v, kv, pg, first, nvalid, head_off, a.head_dim), off, (Raw*)nullptr);
+    const HalfSpan h = prefix_half_span(kv, pg, first, nvalid, (int)((head_off + a.head_dim) * EB));
+    k = buf_load_chunk(half_rsrc(kv.k, h), off, (Raw*)nullptr);
+    v = buf_load_chunk(half_rsrc(kv.v, h), off, (Raw*)nullptr);
     bad = pg < 0 || t >= end;
   } else {
     const int j = a.index;
