@@ -51,15 +51,30 @@ HBM_PEAK_GBS = 8000.0
 METRIC = "cascade verify attn: KV GB/s (% HBM peak) + query tok/s vs naive expand"
 CSRC = os.path.join(ROOT, "cascade_attention_tree_amd", "csrc")
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "verify_headline_traffic.json")
+MFMA_FILE = os.path.join(ROOT, "profiles", "verify_headline_mfma.json")
+BUILD_SCRIPT = os.path.join(ROOT, "cascade_attention_tree_amd", "build_lib.py")
 
 
 def kernel_source_hash() -> str:
+    """Hash of the kernel sources and the build script (its flags shape the
+    code): counter records taken under another hash no longer describe the
+    kernel and are not reported."""
     h = hashlib.sha256()
-    for name in sorted(os.listdir(CSRC)):
-        with open(os.path.join(CSRC, name), "rb") as f:
-            h.update(name.encode())
+    for path in [os.path.join(CSRC, n) for n in sorted(os.listdir(CSRC))] + [BUILD_SCRIPT]:
+        with open(path, "rb") as f:
+            h.update(os.path.basename(path).encode())
             h.update(f.read())
     return h.hexdigest()[:16]
+
+
+def profiled(path, key):
+    """A value from a counter record under profiles/, if it was taken on the
+    current kernel sources; else None."""
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        rec = json.load(f)
+    return rec.get(key) if rec.get("kernel_hash") == kernel_source_hash() else None
 
 
 def workload_bytes(wl, kv_elem_bytes=2):
@@ -576,12 +591,7 @@ def main():
         }
     kv_gbs = kv_casc / (t_ms * 1e-3) / 1e9
     compulsory = kv_casc + q_bytes + o_bytes
-    traffic = None
-    if os.path.exists(TRAFFIC_FILE):
-        with open(TRAFFIC_FILE) as f:
-            tr = json.load(f)
-        if tr.get("kernel_hash") == kernel_source_hash():
-            traffic = tr.get("bytes_per_launch")
+    traffic = profiled(TRAFFIC_FILE, "bytes_per_launch")
     line = {
         "metric": METRIC,
         "value": kv_gbs,
@@ -610,11 +620,12 @@ def main():
                      "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": compulsory / (kernel_ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
                      "traffic": traffic,
-                     "kernel": "attn_kernel<128, 5, verify> (one launch per step)",
+                     "kernel": "attn_kernel<128, 5, verify> (key-split kernel, one launch per step)",
                      "algorithmic_bytes_per_launch": compulsory,
                      "kernel_ms": kernel_ms, "kernel_median_ms": float(np.median(k_ms)),
                      "kernel_timing": "HIP events recorded around the kernel launch "
-                                      "(hipExtLaunchKernel), mean of K cold steps"},
+                                      "(hipExtLaunchKernel), mean of K cold steps",
+                     "mfma_util_profiled": profiled(MFMA_FILE, "mfma_busy_frac")},
     }
     line.update(extra)
     if not args.only_verify:

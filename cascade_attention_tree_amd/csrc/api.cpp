@@ -47,6 +47,12 @@ bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) ==
 constexpr int kTargetItems = 256;
 constexpr int kPairTargetItems = 512;
 constexpr int kMinSplitKeys = 256;
+// The pair kernel splits a prefix only into splits of at least this many keys
+// (eight 32-key tiles per wave): a split's partial states cost a round trip
+// through the workspace and a merge launch, which shorter splits do not earn
+// back (GQA configuration, 8 requests x 1000 keys: 24.7 us unsplit in 16-row
+// chunks against 26.4-28.1 us split in two or four).
+constexpr int kPairMinSplitKeys = 1024;
 constexpr int kMaxSplitKeys = 4096;
 constexpr int kMaxRowBlocks = 5;
 
@@ -72,13 +78,13 @@ void plan_rows(Plan& p, int64_t rows_per_segment) {
 
 // Key splits for `items` work items: enough to reach `target` items when the
 // prefix is long enough, at most kMaxSplitKeys keys per split.
-void plan_splits(Plan& p, int max_len, int64_t items, int64_t target) {
+void plan_splits(Plan& p, int max_len, int64_t items, int64_t target, int min_split_keys = kMinSplitKeys) {
   const int len = max_len > 0 ? max_len : 1;
   int64_t n = 1;
   // An empty launch (no requests) has no items to fill the device with.
-  if (len > 2 * kMinSplitKeys && items > 0 && items < target) {
+  if (len > 2 * min_split_keys && items > 0 && items < target) {
     n = cdiv(target, items);
-    const int64_t cap = cdiv(len, kMinSplitKeys);
+    const int64_t cap = cdiv(len, min_split_keys);
     if (n > cap) n = cap;
   }
   if (cdiv(len, n) > kMaxSplitKeys) n = cdiv(len, kMaxSplitKeys);
@@ -250,9 +256,9 @@ constexpr int64_t kRowKernelMinRows = 1024;
 // each: there the key-split kernel, one workgroup per CU holding all rows,
 // measured faster (60.6 against 64.5 us at 32 requests x 8 kv heads x 80
 // rows), while the pair kernel is faster over FP8 pools, on the ragged
-// batch and at equal speed on the GQA configuration.  A request with 32 rows
-// or more is cut in two chunks when there are too few (request, kv head)
-// pairs to fill the device.
+// batch and at equal speed on the GQA configuration.  With too few (request,
+// kv head) pairs to fill the device, a request's rows are cut in more chunks,
+// down to 16 rows each, before its prefix is split.
 Plan plan_request(const cascade_query* q, const cascade_paged_kv* kv, const cascade_tree* t) {
   Plan p;
   p.group = q->num_qo_heads / kv->num_kv_heads;
@@ -264,9 +270,11 @@ Plan plan_request(const cascade_query* q, const cascade_paged_kv* kv, const casc
   p.pair = kv->head_dim == 128 && rows > 0 && rows < kRowKernelMinRows && !one_chunk_fills;
   if (p.pair) {
     p.pair_chunks = (int)cdiv(rows, casc::kPairRows);
-    if (p.pair_chunks == 1 && rows >= 32 && pairs < kPairTargetItems) p.pair_chunks = 2;
+    // Few (request, kv head) pairs: smaller chunks (down to one 16-row block)
+    // until the launch holds a workgroup per CU.
+    while (pairs * p.pair_chunks < kTargetItems && cdiv(rows, p.pair_chunks + 1) >= 16) ++p.pair_chunks;
     p.pair_rows = (int)cdiv(rows, p.pair_chunks);
-    plan_splits(p, t->max_prefix_len, pairs * p.pair_chunks, kPairTargetItems);
+    plan_splits(p, t->max_prefix_len, pairs * p.pair_chunks, kPairTargetItems, kPairMinSplitKeys);
   } else {
     plan_splits(p, t->max_prefix_len, p.items, kTargetItems);
   }

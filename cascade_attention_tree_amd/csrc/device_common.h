@@ -156,7 +156,7 @@ __device__ __forceinline__ u32x2 buf_load8(__amdgpu_buffer_rsrc_t r, int byte_of
 // of a half whose page id is -1 (none, or outside the pool) -- read zeros.
 // K and V pools share their strides, so one span serves both descriptors.
 // The attention kernels and the prefix gather hook build their prefix loads
-// from these functions.
+// from prefix_half_span, half_rsrc and prefix_lane_offset.
 struct HalfSpan {
   uint64_t off;  // byte offset of the half's first key row in a pool
   int bytes;     // descriptor range
@@ -178,12 +178,7 @@ __device__ __forceinline__ HalfSpan prefix_half_span(const KvView& kv, int page,
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t half_rsrc(const void* pool, const HalfSpan& h) {
   return page_rsrc(static_cast<const unsigned char*>(pool) + h.off, h.bytes);
 }
-template <int EB>
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t prefix_half_rsrc(const void* pool, const KvView& kv, int page,
-                                                                   int first, int nvalid, int64_t head_off,
-                                                                   int D) {
-  return half_rsrc(pool, prefix_half_span(kv, page, first, nvalid, (int)((head_off + D) * EB)));
-}
+
 // Byte offset, inside its half's descriptor, of 8-channel chunk `chunk` of
 // the key `key` places after the half's first key.
 template <int EB>
