@@ -256,18 +256,29 @@ constexpr int64_t kRowKernelMinRows = 1024;
 // each: there the key-split kernel, one workgroup per CU holding all rows,
 // measured faster (60.6 against 64.5 us at 32 requests x 8 kv heads x 80
 // rows), while the pair kernel is faster over FP8 pools, on the ragged
-// batch and at equal speed on the GQA configuration.  With too few (request,
-// kv head) pairs to fill the device, a request's rows are cut in more chunks,
-// down to 16 rows each, before its prefix is split.
+// batch.  With too few (request, kv head) pairs to fill the device, a
+// request's rows are cut in more chunks before its prefix is split; when
+// they are at most 16 * kMaxRowBlocks and even one 16-row block per chunk
+// leaves at most a workgroup per CU (the GQA
+// configuration: 8 requests x 8 kv heads x 48 rows, 192 chunks), the
+// key-split kernel runs those 16-row chunks, its four waves sharing each
+// chunk's prefix (19.9 us there, against 21.5 us on the pair kernel with
+// 12-row chunks and 24.8 us with 16-row chunks padded to 48), and a prefix
+// is split only past 2 * kPairMinSplitKeys keys.
 Plan plan_request(const cascade_query* q, const cascade_paged_kv* kv, const cascade_tree* t) {
   Plan p;
   p.group = q->num_qo_heads / kv->num_kv_heads;
   const int64_t rows = (int64_t)t->max_request_rows * p.group;
   plan_rows(p, rows);
-  p.items = (int64_t)t->batch_size * kv->num_kv_heads * p.n_chunks;
   const int64_t pairs = (int64_t)t->batch_size * kv->num_kv_heads;
+  const bool thin = rows > 0 && rows <= 16 * kMaxRowBlocks && pairs * cdiv(rows, 16) <= kTargetItems;
+  if (thin) {
+    p.rb = 1;
+    p.n_chunks = (int)cdiv(rows, 16);
+  }
+  p.items = pairs * p.n_chunks;
   const bool one_chunk_fills = !kv_fp8(kv) && rows <= 16 * kMaxRowBlocks && pairs >= kTargetItems;
-  p.pair = kv->head_dim == 128 && rows > 0 && rows < kRowKernelMinRows && !one_chunk_fills;
+  p.pair = !thin && kv->head_dim == 128 && rows > 0 && rows < kRowKernelMinRows && !one_chunk_fills;
   if (p.pair) {
     p.pair_chunks = (int)cdiv(rows, casc::kPairRows);
     // Few (request, kv head) pairs: smaller chunks (down to one 16-row block)
@@ -276,7 +287,7 @@ Plan plan_request(const cascade_query* q, const cascade_paged_kv* kv, const casc
     p.pair_rows = (int)cdiv(rows, p.pair_chunks);
     plan_splits(p, t->max_prefix_len, pairs * p.pair_chunks, kPairTargetItems, kPairMinSplitKeys);
   } else {
-    plan_splits(p, t->max_prefix_len, p.items, kTargetItems);
+    plan_splits(p, t->max_prefix_len, p.items, kTargetItems, thin ? kPairMinSplitKeys : kMinSplitKeys);
   }
   return p;
 }

@@ -640,9 +640,18 @@ template <bool KV8>
 static hipError_t launch_pair(int mode, const AttnArgs& a, int grid, hipStream_t s, hipEvent_t e0,
                               hipEvent_t e1) {
   const dim3 g(grid), b(256);
+  // Chunks of one 16-row block (few rows per kv head) run the one-block
+  // instance: no MFMA work or state for the empty blocks.
+  const bool one = a.chunk_rows <= 16;
   switch (mode) {
-    case kModePrefix: go(pair_kernel<kPairRowBlocks, kModePrefix, KV8>, g, b, s, e0, e1, a); break;
-    case kModeVerify: go(pair_kernel<kPairRowBlocks, kModeVerify, KV8>, g, b, s, e0, e1, a); break;
+    case kModePrefix:
+      if (one) go(pair_kernel<1, kModePrefix, KV8>, g, b, s, e0, e1, a);
+      else go(pair_kernel<kPairRowBlocks, kModePrefix, KV8>, g, b, s, e0, e1, a);
+      break;
+    case kModeVerify:
+      if (one) go(pair_kernel<1, kModeVerify, KV8>, g, b, s, e0, e1, a);
+      else go(pair_kernel<kPairRowBlocks, kModeVerify, KV8>, g, b, s, e0, e1, a);
+      break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();

@@ -72,6 +72,12 @@ def cases():
         # block table one by one.
         "suffix600": lambda: W.build_workload("suffix600", [100, 37], [[600], [530]], 8, 2, 128, 16, seed=49,
                                               suffix_in_prefix_pages=True),
+        # Few pairs: 16-row chunks of the key-split kernel with a split
+        # prefix, and the pair kernel's one-block instance.
+        "thin_split": lambda: W.build_workload("thin_split", [2500, 300, 0], [[3, 2], [5], [1, 1, 1]],
+                                               8, 2, 128, 16, seed=53),
+        "pair_16row": lambda: W.build_workload("pair_16row", [1300, 77], [[4, 4, 4], [6, 6]], 16, 2, 128, 16,
+                                               seed=54),
     }
 
 

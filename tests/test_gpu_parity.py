@@ -64,6 +64,14 @@ def small_cases():
         "long_split": lambda: W.build_workload("long_split", [5000, 2500], [[4, 4], [2]], 8, 8, 128, 32,
                                                seed=24),
         "topk1": lambda: W.build_workload("topk1", [90, 17], [[6], [9]], 4, 2, 128, 16, seed=25),
+        # Few (request, kv head) pairs with few rows: 16-row chunks of the
+        # key-split kernel, the longest prefix split in three.
+        "thin_split": lambda: W.build_workload("thin_split", [2500, 300, 0], [[3, 2], [5], [1, 1, 1]],
+                                               8, 2, 128, 16, seed=51),
+        # 96 rows per (request, kv head) over 4 pairs: six 16-row chunks on
+        # the pair kernel's one-block instance.
+        "pair_16row": lambda: W.build_workload("pair_16row", [1300, 77], [[4, 4, 4], [6, 6]], 16, 2, 128, 16,
+                                               seed=52),
         # More branches per request than one wave has lanes (70), and more than
         # the per-workgroup branch window holds (130): the tree tables' slow paths.
         "wide_tree": lambda: W.build_workload("wide_tree", [300, 50], [[1] * 70, [2] * 130], 4, 2, 64, 16,
