@@ -124,6 +124,12 @@ __device__ __forceinline__ i16x4 lds_read_tr16(const uint16_t* p) {
   return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(p));
 }
 
+// A wave index as a type (merge code specialised per wave).
+template <int W>
+struct WaveIndex {
+  static constexpr int value = W;
+};
+
 // KV8: the pools hold FP8 E4M3 codes (half the bytes per key); each chunk is
 // widened to bf16 when staged, so everything from the LDS stage on is shared.
 template <int D, int RB, int MODE, bool KV8 = false>
@@ -908,6 +914,11 @@ attn_kernel(const AttnArgs a) {
   mfma_drain();
 
   // ---- merge the four waves' states (LSE identity) ----------------------
+  // Each wave publishes its rows' (m, l); after the barrier (which also ends
+  // every wave's use of its stage) it sends its unscaled O blocks to their
+  // owners and forms the merge weights of its rows; after the second barrier
+  // owner ow of channel blocks [ow*DBW, ow*DBW + DBW) sums the four waves'
+  // blocks, each times its weight 2^(m_w - M) / sum_w' l_w' 2^(m_w' - M).
 #pragma unroll
   for (int rb = 0; rb < RB; ++rb) l[rb] = rowgroup_sum(l[rb]);
   if (g4 == 0) {
@@ -918,25 +929,6 @@ attn_kernel(const AttnArgs a) {
     }
   }
   __syncthreads();
-#pragma unroll
-  for (int rb = 0; rb < RB; ++rb) {
-    const int r = rb * 16 + l16;
-    float M = kNegInf;
-#pragma unroll
-    for (int w2 = 0; w2 < 4; ++w2) M = fmaxf(M, ml[(w2 * ROWS + r) * 2]);
-    const float ms = M == kNegInf ? 0.f : M;
-    float tot = 0.f;
-#pragma unroll
-    for (int w2 = 0; w2 < 4; ++w2)
-      tot += ml[(w2 * ROWS + r) * 2 + 1] * fast_exp2(ml[(w2 * ROWS + r) * 2] - ms);
-    // FP8 pools: the V scale multiplies every normalised output once, here.
-    const float f = tot > 0.f ? fast_exp2(m[rb] - ms) / tot * (KV8 ? a.v_scale : 1.f) : 0.f;
-    lse2[rb] = tot > 0.f ? M + fast_log2(tot) : kNegInf;
-#pragma unroll
-    for (int db = 0; db < DB; ++db) o[rb][db] *= f;
-  }
-  // Owner ow of channel blocks [ow*DBW, ow*DBW + DBW) receives the other
-  // waves' scaled blocks through LDS and sums all four in wave order.
   float* xbuf = reinterpret_cast<float*>(smem);
   auto slot = [](int owner, int src) { return owner * 3 + (src < owner ? src : src - 1); };
 #pragma unroll
@@ -949,25 +941,57 @@ attn_kernel(const AttnArgs a) {
       for (int dbl = 0; dbl < DBW; ++dbl)
         *reinterpret_cast<f32x4*>(dst + ((rb * DBW + dbl) * 64 + lane) * 4) = o[rb][ow * DBW + dbl];
   }
-  __syncthreads();
+  float wt[RB][4];
 #pragma unroll
   for (int rb = 0; rb < RB; ++rb) {
+    const int r = rb * 16 + l16;
+    float mw[4], lw[4];
 #pragma unroll
-    for (int dbl = 0; dbl < DBW; ++dbl) {
-      f32x4 own = o[rb][dbl];
-#pragma unroll
-      for (int ow = 1; ow < 4; ++ow)
-        if (ow == w) own = o[rb][ow * DBW + dbl];
-      f32x4 sum = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int w2 = 0; w2 < 4; ++w2) {
-        const f32x4 x = w2 == w ? own
-                                : *reinterpret_cast<const f32x4*>(
-                                      xbuf + slot(w, w2) * XSLOT + ((rb * DBW + dbl) * 64 + lane) * 4);
-        sum += x;
-      }
-      acc[rb][dbl] = sum;
+    for (int w2 = 0; w2 < 4; ++w2) {
+      mw[w2] = ml[(w2 * ROWS + r) * 2];
+      lw[w2] = ml[(w2 * ROWS + r) * 2 + 1];
     }
+    const float M = fmaxf(fmaxf(mw[0], mw[1]), fmaxf(mw[2], mw[3]));
+    const float ms = M == kNegInf ? 0.f : M;
+    float e[4], tot = 0.f;
+#pragma unroll
+    for (int w2 = 0; w2 < 4; ++w2) {
+      e[w2] = fast_exp2(mw[w2] - ms);
+      tot += lw[w2] * e[w2];
+    }
+    // FP8 pools: the V scale multiplies every normalised output once, here.
+    const float inv = tot > 0.f ? (KV8 ? a.v_scale : 1.f) / tot : 0.f;
+#pragma unroll
+    for (int w2 = 0; w2 < 4; ++w2) wt[rb][w2] = e[w2] * inv;
+    lse2[rb] = tot > 0.f ? M + fast_log2(tot) : kNegInf;
+  }
+  __syncthreads();
+  // The owner's own blocks stay in registers: one specialisation per wave
+  // index (a uniform branch), so no block is selected lane by lane.
+  auto combine = [&](auto owner) {
+    constexpr int OW = decltype(owner)::value;
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb) {
+#pragma unroll
+      for (int dbl = 0; dbl < DBW; ++dbl) {
+        f32x4 sum = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int w2 = 0; w2 < 4; ++w2) {
+          const f32x4 x = w2 == OW ? o[rb][OW * DBW + dbl]
+                                   : *reinterpret_cast<const f32x4*>(
+                                         xbuf + slot(OW, w2) * XSLOT + ((rb * DBW + dbl) * 64 + lane) * 4);
+#pragma unroll
+          for (int i = 0; i < 4; ++i) sum[i] = fmaf(wt[rb][w2], x[i], sum[i]);
+        }
+        acc[rb][dbl] = sum;
+      }
+    }
+  };
+  switch (w) {
+    case 0: combine(WaveIndex<0>{}); break;
+    case 1: combine(WaveIndex<1>{}); break;
+    case 2: combine(WaveIndex<2>{}); break;
+    default: combine(WaveIndex<3>{}); break;
   }
 
   // Split prefix passes stop at a partial state; everything else is final.
@@ -975,32 +999,57 @@ attn_kernel(const AttnArgs a) {
   if constexpr (MODE == kModePrefix || MODE == kModeVerify) partial = a.n_splits > 1;
 
   // ---- output ----------------------------------------------------------------
+  // Row addresses and values are formed first and the stores issued back to
+  // back, one uniform branch per output kind: no store waits for an earlier
+  // one to release its registers.
   const int64_t plane = (int64_t)a.total_rows * a.num_qo_heads;
+  int64_t orow[RB];
+  bool rv[RB];
 #pragma unroll
   for (int rb = 0; rb < RB; ++rb) {
-    if (!row_valid(rb)) continue;
-    const int64_t orow = row_out(rb);
-    if (partial) {
+    rv[rb] = row_valid(rb);
+    orow[rb] = rv[rb] ? row_out(rb) : 0;
+  }
+  const int cw = w * DBW * 16 + g4 * 4;  // first channel of this lane's blocks
+  if (partial) {
 #pragma unroll
-      for (int dbl = 0; dbl < DBW; ++dbl) {
-        const int c = (w * DBW + dbl) * 16 + g4 * 4;
-        *reinterpret_cast<f32x4*>(a.ws_o + (split * plane + orow) * D + c) = acc[rb][dbl];
-      }
-      if (w == 0 && g4 == 0) a.ws_lse[split * plane + orow] = lse2[rb];
-      continue;
-    }
+    for (int rb = 0; rb < RB; ++rb) {
+      if (!rv[rb]) continue;
+      float* dst = a.ws_o + (split * plane + orow[rb]) * D + cw;
 #pragma unroll
-    for (int dbl = 0; dbl < DBW; ++dbl) {
-      const int c = (w * DBW + dbl) * 16 + g4 * 4;
-      const f32x4 x = acc[rb][dbl];
-      if (a.o_bf16) {
-        *reinterpret_cast<u32x2*>(reinterpret_cast<uint16_t*>(a.o) + orow * D + c) =
-            u32x2{pack_bf16x2(x[0], x[1]), pack_bf16x2(x[2], x[3])};
-      } else {
-        *reinterpret_cast<f32x4*>(reinterpret_cast<float*>(a.o) + orow * D + c) = x;
-      }
+      for (int dbl = 0; dbl < DBW; ++dbl) *reinterpret_cast<f32x4*>(dst + dbl * 16) = acc[rb][dbl];
+      if (w == 0 && g4 == 0) a.ws_lse[split * plane + orow[rb]] = lse2[rb];
     }
-    if (w == 0 && g4 == 0 && a.lse) a.lse[orow] = lse2[rb] * kLn2;
+    return;
+  }
+  if (a.o_bf16) {
+    u32x2 pk[RB][DBW];
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb)
+#pragma unroll
+      for (int dbl = 0; dbl < DBW; ++dbl)
+        pk[rb][dbl] = u32x2{pack_bf16x2(acc[rb][dbl][0], acc[rb][dbl][1]),
+                            pack_bf16x2(acc[rb][dbl][2], acc[rb][dbl][3])};
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb) {
+      if (!rv[rb]) continue;
+      uint16_t* dst = reinterpret_cast<uint16_t*>(a.o) + orow[rb] * D + cw;
+#pragma unroll
+      for (int dbl = 0; dbl < DBW; ++dbl) *reinterpret_cast<u32x2*>(dst + dbl * 16) = pk[rb][dbl];
+    }
+  } else {
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb) {
+      if (!rv[rb]) continue;
+      float* dst = reinterpret_cast<float*>(a.o) + orow[rb] * D + cw;
+#pragma unroll
+      for (int dbl = 0; dbl < DBW; ++dbl) *reinterpret_cast<f32x4*>(dst + dbl * 16) = acc[rb][dbl];
+    }
+  }
+  if (w == 0 && g4 == 0 && a.lse) {
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb)
+      if (rv[rb]) a.lse[orow[rb]] = lse2[rb] * kLn2;
   }
 }
 
