@@ -247,23 +247,6 @@ attn_kernel(const AttnArgs a) {
   if constexpr (MODE == kModePrefix || MODE == kModeVerify) {
     if (split != 0 && (int64_t)split * a.split_len >= L_in) return;
   }
-  const int tok0 = cqo[jb];
-  const int tok1 = cqo[je];
-  // Keeps the length load in the same round trip as the branch-range loads
-  // (otherwise it is sunk past the checks below).
-  asm volatile("" ::"s"(L_in));
-  if (tok0 < 0 || tok1 < tok0 || tok1 > a.total_rows) {
-    if (threadIdx.x == 0) atomicOr(&g_device_error, kErrRow);
-    return;
-  }
-  const int ntok = tok1 - tok0;
-  const int nrows = ntok * a.group;
-  const int row0 = chunk * ROWS;
-  if (chunk == 0 && split == 0 && threadIdx.x == 0 && nrows > a.n_chunks * ROWS)
-    atomicOr(&g_device_error, kErrRow);  // rows past the planned chunks are not computed
-  if (row0 >= nrows) return;
-  const int row_end = min(nrows, row0 + ROWS);
-
   int L = L_in;
   {
     const int cap = a.page_table_stride << a.kv.log2_page;
@@ -285,38 +268,6 @@ attn_kernel(const AttnArgs a) {
   const KvView kv = a.kv;
   const float c2 = a.scale_log2;
   const int64_t head_off = (int64_t)g * kv.head_stride;
-  // Segment tokens of this chunk's rows, and the draft keys [dlo, dhi) they
-  // can see (dlo, the start of the first row's branch, is set below).
-  const int tok_first = row0 / a.group;
-  const int tok_last = (row_end - 1) / a.group;
-  const int dhi = tok_last + 1;
-
-  // ---- rows of this lane (column l16 of each 16-row block of S^T / O^T) --
-  // Recomputed where needed rather than kept live across the key loop.
-  auto row_valid = [&](int rb) { return row0 + rb * 16 + l16 < nrows; };
-  auto row_tok = [&](int rb) {  // segment token of the row (tok_first for padding rows)
-    const int rho = row0 + rb * 16 + l16;
-    return rho < nrows ? rho / a.group : tok_first;
-  };
-  auto row_out = [&](int rb) -> int64_t {  // index of (row, head) in [total_rows, Hq]
-    const int rho = row0 + rb * 16 + l16;
-    const int t = rho / a.group;
-    return (int64_t)(tok0 + t) * a.num_qo_heads + g * a.group + (rho - t * a.group);
-  };
-  // Per row: its segment token, its branch's first token, and with a draft
-  // tree its ancestor mask.
-  int rtok[RB] = {}, rbs[RB] = {};
-  uint64_t ranc[RB] = {};
-  const bool tree = a.draft_mask != nullptr;
-  auto load_row_masks = [&]() {
-#pragma unroll
-    for (int rb = 0; rb < RB; ++rb) {
-      rtok[rb] = row_tok(rb);
-      rbs[rb] = t_rbs[rtok[rb] - tok_first];
-      if (tree) ranc[rb] = a.draft_mask[tok0 + rtok[rb]];
-    }
-  };
-
   // ---- per-tile building blocks ----------------------------------------
 
   // A tile's K and V arrive in registers, 16 bytes per lane and load, in one
@@ -384,6 +335,89 @@ attn_kernel(const AttnArgs a) {
   }
   const int npt = (p1 - p0 + 31) >> 5;
 
+  // Writes a tile's K and V rows into the wave's stage (row = key, RS stride).
+  auto stage = [&](const Raw (&kr)[NI], const Raw (&vr)[NI], bool rows, int ok, uint16_t* st) {
+#pragma unroll
+    for (int r = 0; r < NI; ++r) {
+      int key, ch;
+      u32x4 v = widen_bf16(vr[r]);
+      if (rows) {
+        key = r * TPI + lane / CPR;
+        ch = lane % CPR;
+      } else {
+        key = (r / KS) * 16 + l16;
+        ch = (r % KS) * 4 + g4;
+        if (!((ok >> (r / KS)) & 1)) v = u32x4{0u, 0u, 0u, 0u};
+      }
+      *reinterpret_cast<u32x4*>(st + key * RS + ch * 8) = widen_bf16(kr[r]);
+      *reinterpret_cast<u32x4*>(st + 32 * RS + key * RS + ch * 8) = v;
+    }
+  };
+
+  // The first prefix tile goes out now, one round trip of small loads after
+  // the start (its block-table entries came with the request's length); Q
+  // follows once the branch range has given the rows.
+  Raw kr[NI], vr[NI];
+  int pg[2] = {-1, -1};
+  if (w < npt) {
+    if constexpr (MODE == kModePrefix || MODE == kModeVerify) {
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) pg[kb] = page_id(p0 + w * 32 + kb * 16 < p1 ? pt_first[kb] : -1);
+    } else {
+      prefix_pages(p0 + w * 32, p1, pg);
+    }
+    load_rows(pg, p0 + w * 32, p1, kr, vr);
+  }
+
+  const int tok0 = cqo[jb];
+  const int tok1 = cqo[je];
+  // Keeps the length load in the same round trip as the branch-range loads
+  // (otherwise it is sunk past the checks below).
+  asm volatile("" ::"s"(L_in));
+  if (tok0 < 0 || tok1 < tok0 || tok1 > a.total_rows) {
+    if (threadIdx.x == 0) atomicOr(&g_device_error, kErrRow);
+    return;
+  }
+  const int ntok = tok1 - tok0;
+  const int nrows = ntok * a.group;
+  const int row0 = chunk * ROWS;
+  if (chunk == 0 && split == 0 && threadIdx.x == 0 && nrows > a.n_chunks * ROWS)
+    atomicOr(&g_device_error, kErrRow);  // rows past the planned chunks are not computed
+  if (row0 >= nrows) return;
+  const int row_end = min(nrows, row0 + ROWS);
+
+  // Segment tokens of this chunk's rows, and the draft keys [dlo, dhi) they
+  // can see (dlo, the start of the first row's branch, is set below).
+  const int tok_first = row0 / a.group;
+  const int tok_last = (row_end - 1) / a.group;
+  const int dhi = tok_last + 1;
+
+  // ---- rows of this lane (column l16 of each 16-row block of S^T / O^T) --
+  // Recomputed where needed rather than kept live across the key loop.
+  auto row_valid = [&](int rb) { return row0 + rb * 16 + l16 < nrows; };
+  auto row_tok = [&](int rb) {  // segment token of the row (tok_first for padding rows)
+    const int rho = row0 + rb * 16 + l16;
+    return rho < nrows ? rho / a.group : tok_first;
+  };
+  auto row_out = [&](int rb) -> int64_t {  // index of (row, head) in [total_rows, Hq]
+    const int rho = row0 + rb * 16 + l16;
+    const int t = rho / a.group;
+    return (int64_t)(tok0 + t) * a.num_qo_heads + g * a.group + (rho - t * a.group);
+  };
+  // Per row: its segment token, its branch's first token, and with a draft
+  // tree its ancestor mask.
+  int rtok[RB] = {}, rbs[RB] = {};
+  uint64_t ranc[RB] = {};
+  const bool tree = a.draft_mask != nullptr;
+  auto load_row_masks = [&]() {
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb) {
+      rtok[rb] = row_tok(rb);
+      rbs[rb] = t_rbs[rtok[rb] - tok_first];
+      if (tree) ranc[rb] = a.draft_mask[tok0 + rtok[rb]];
+    }
+  };
+
   // ---- Q rows of the chunk (into registers now, into LDS below) ---------
   constexpr int kQChunks = D / 8;
   constexpr int QIT = (ROWS * kQChunks + 255) / 256;
@@ -426,19 +460,6 @@ attn_kernel(const AttnArgs a) {
         td_reg[i] = t < nb && a.draft_start ? a.draft_start[jb + t] : 0;
       }
     }
-  }
-
-  // The first prefix tile goes out after Q, which the first scores need.
-  Raw kr[NI], vr[NI];
-  int pg[2] = {-1, -1};
-  if (w < npt) {
-    if constexpr (MODE == kModePrefix || MODE == kModeVerify) {
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb) pg[kb] = page_id(p0 + w * 32 + kb * 16 < p1 ? pt_first[kb] : -1);
-    } else {
-      prefix_pages(p0 + w * 32, p1, pg);
-    }
-    load_rows(pg, p0 + w * 32, p1, kr, vr);
   }
 
   // ---- tree tables ---------------------------------------------------------
@@ -573,24 +594,6 @@ attn_kernel(const AttnArgs a) {
     int64_t off[2];
     draft_offsets(base, end, off);
     load_draft_at(off, kr, vr, ok);
-  };
-  // Writes a tile's K and V rows into the wave's stage (row = key, RS stride).
-  auto stage = [&](const Raw (&kr)[NI], const Raw (&vr)[NI], bool rows, int ok, uint16_t* st) {
-#pragma unroll
-    for (int r = 0; r < NI; ++r) {
-      int key, ch;
-      u32x4 v = widen_bf16(vr[r]);
-      if (rows) {
-        key = r * TPI + lane / CPR;
-        ch = lane % CPR;
-      } else {
-        key = (r / KS) * 16 + l16;
-        ch = (r % KS) * 4 + g4;
-        if (!((ok >> (r / KS)) & 1)) v = u32x4{0u, 0u, 0u, 0u};
-      }
-      *reinterpret_cast<u32x4*>(st + key * RS + ch * 8) = widen_bf16(kr[r]);
-      *reinterpret_cast<u32x4*>(st + 32 * RS + key * RS + ch * 8) = v;
-    }
   };
 
 
