@@ -626,15 +626,17 @@ attn_kernel(const AttnArgs a) {
       for (int kb = 0; kb < 2; ++kb) asm volatile("" : "+v"(s[rb][kb]));
   };
 
-  // Prefix keys: only the bound `end`.
+  // Prefix keys: only the bound `end`.  Key base + kb*16 + g4*4 + i is kept
+  // iff g4*4 < end - base - kb*16 - i: a uniform bound per key, so no key
+  // index is formed per lane.
   auto mask_prefix = [&](int base, int end, f32x4 (&s)[RB][2]) {
+    const int n = end - base;
 #pragma unroll
     for (int rb = 0; rb < RB; ++rb)
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
-          s[rb][kb][i] = base + kb * 16 + g4 * 4 + i < end ? s[rb][kb][i] : kNegInf;
+        for (int i = 0; i < 4; ++i) s[rb][kb][i] = g4 * 4 < n - (kb * 16 + i) ? s[rb][kb][i] : kNegInf;
   };
   // Draft keys: the bound `end` and the in-branch ancestor rule (rtok / rbs
   // must have been loaded by load_row_masks).

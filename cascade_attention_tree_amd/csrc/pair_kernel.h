@@ -493,12 +493,14 @@ pair_kernel(const AttnArgs a) {
       pages_of(nxt + 4 < npt ? nxt + 4 : ld, pg);
     }
     if (base + 32 > p1) {
+      // Key base + kb*16 + g4*4 + i is kept iff g4*4 < p1 - base - kb*16 - i.
+      const int n = p1 - base;
 #pragma unroll
       for (int rb = 0; rb < RB; ++rb)
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-          for (int i = 0; i < 4; ++i) s[rb][kb][i] = base + kb * 16 + g4 * 4 + i < p1 ? s[rb][kb][i] : kNegInf;
+          for (int i = 0; i < 4; ++i) s[rb][kb][i] = g4 * 4 < n - (kb * 16 + i) ? s[rb][kb][i] : kNegInf;
     }
     accumulate(s);
   }

@@ -422,10 +422,13 @@ rows_kernel(const AttnArgs a) {
             s[rb][kb][i] = vis ? s[rb][kb][i] : kNegInf;
           }
       } else if (base + 32 > end) {
+        // The tile's last keys lie past `end`: key base + kb*16 + g4*4 + i is
+        // kept iff g4*4 < end - base - kb*16 - i (a uniform bound per key).
+        const int n = end - base;
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-          for (int i = 0; i < 4; ++i) s[rb][kb][i] = base + kb * 16 + g4 * 4 + i < end ? s[rb][kb][i] : kNegInf;
+          for (int i = 0; i < 4; ++i) s[rb][kb][i] = g4 * 4 < n - (kb * 16 + i) ? s[rb][kb][i] : kNegInf;
       }
       // Online softmax in base 2; the carried max is raised only past a slack.
       const float lm = fmaxf(fmaxf(fmaxf(s[rb][0][0], s[rb][0][1]), fmaxf(s[rb][0][2], s[rb][0][3])),
