@@ -242,7 +242,7 @@ casc::AttnArgs make_args(const cascade_query* q, const cascade_paged_kv* kv, con
 }
 
 // Query rows per (request, kv head) from which pass A, the fused verify pass
-// and pass B run the row-split kernel (head dim 128, bf16 pools): at least
+// and pass B run the row-split kernel (head dim 128, bf16 or FP8 pools): at least
 // four full work items of kRowsPerItem rows, where its two waves per SIMD keep
 // the matrix pipes busy (a prefix-hit suffix prefill).
 constexpr int64_t kRowKernelMinRows = 1024;
@@ -357,7 +357,7 @@ hipError_t launch(int mode, int head_dim, int rb, casc::AttnArgs a, int64_t seg_
 
 
 // Pass A, the fused verify pass or pass B (`mode`), unsplit or one launch of
-// the splits: the row-split kernel (head dim 128, bf16 pools, row-heavy
+// the splits: the row-split kernel (head dim 128, row-heavy
 // requests) over chunks of up to kRowsPerItem query rows, else the key-split
 // kernel of the plan.
 hipError_t launch_row_modes(int mode, const cascade_paged_kv* kv,
@@ -372,12 +372,13 @@ hipError_t launch_row_modes(int mode, const cascade_paged_kv* kv,
                       : casc::launch_pair_d128(mode, a, (int)grid, s, e0, e1);
   }
   const int64_t rows = (int64_t)t->max_request_rows * p.group;
-  if (kv->head_dim != 128 || kv_fp8(kv) || rows < kRowKernelMinRows)
+  if (kv->head_dim != 128 || rows < kRowKernelMinRows)
     return launch(mode, kv->head_dim, p.rb, a, (int64_t)t->batch_size * kv->num_kv_heads, splits, s, e0, e1);
   a.n_chunks = (int)(rows > 0 ? cdiv(rows, casc::kRowsPerItem) : 1);
   const int64_t grid = (int64_t)t->batch_size * kv->num_kv_heads * a.n_chunks * splits;
   if (grid <= 0) return hipSuccess;
-  return casc::launch_rows_d128(mode, a, (int)grid, s, e0, e1);
+  return kv_fp8(kv) ? casc::launch_rows_d128_fp8(mode, a, (int)grid, s, e0, e1)
+                    : casc::launch_rows_d128(mode, a, (int)grid, s, e0, e1);
 }
 
 // Kernel timing of cascade_verify_attn (per thread; see the header).

@@ -41,13 +41,14 @@ constexpr int kRowDepth = 4;
 // 16-row blocks per wave: each K and V fragment read out of LDS serves them all.
 constexpr int kRowBlocks = 2;
 
+template <bool KV8>
 static inline hipError_t launch_rows(int mode, const AttnArgs& a, int grid, hipStream_t s, hipEvent_t e0,
                                      hipEvent_t e1) {
   const dim3 g(grid), b(64 * kRowWaves);
   switch (mode) {
-    case kModePrefix: go(rows_kernel<kModePrefix, kRowDepth, kRowBlocks>, g, b, s, e0, e1, a); break;
-    case kModeVerify: go(rows_kernel<kModeVerify, kRowDepth, kRowBlocks>, g, b, s, e0, e1, a); break;
-    case kModeDraft: go(rows_kernel<kModeDraft, kRowDepth, kRowBlocks>, g, b, s, e0, e1, a); break;
+    case kModePrefix: go(rows_kernel<kModePrefix, kRowDepth, kRowBlocks, KV8>, g, b, s, e0, e1, a); break;
+    case kModeVerify: go(rows_kernel<kModeVerify, kRowDepth, kRowBlocks, KV8>, g, b, s, e0, e1, a); break;
+    case kModeDraft: go(rows_kernel<kModeDraft, kRowDepth, kRowBlocks, KV8>, g, b, s, e0, e1, a); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();

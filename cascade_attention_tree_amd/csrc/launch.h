@@ -20,11 +20,13 @@ hipError_t launch_attn_d64_fp8(int mode, int rb, const AttnArgs& a, int grid, hi
 hipError_t launch_attn_d128_fp8(int mode, int rb, const AttnArgs& a, int grid, hipStream_t s,
                                 hipEvent_t ev_start, hipEvent_t ev_stop);
 
-// Row-split kernel for head_dim 128 and bf16 pools, modes kModePrefix,
+// Row-split kernel for head_dim 128 (bf16 / FP8 pools), modes kModePrefix,
 // kModeVerify and kModeDraft: work items of at most kRowsPerItem query rows
 // (a.n_chunks counts chunks of that size).
 hipError_t launch_rows_d128(int mode, const AttnArgs& a, int grid, hipStream_t s, hipEvent_t ev_start,
                             hipEvent_t ev_stop);
+hipError_t launch_rows_d128_fp8(int mode, const AttnArgs& a, int grid, hipStream_t s, hipEvent_t ev_start,
+                                hipEvent_t ev_stop);
 
 // Pair kernel, head_dim 128 (bf16 / FP8 pools), modes kModePrefix and
 // kModeVerify: a.n_chunks chunks of a.chunk_rows rows per (request, kv head),

@@ -1,5 +1,7 @@
 // Row-split attention kernel for row-heavy launches (pass A, pass B and the
-// fused verify pass), head_dim 128, bf16 pools.
+// fused verify pass), head_dim 128, bf16 or FP8 E4M3 pools (KV8: 8-byte code
+// chunks per load, widened to bf16 when staged; the K scale is in the
+// softmax scale, the V scale is applied to the normalised output).
 //
 // One workgroup of kRowWaves = 4 waves (one per SIMD; two workgroups share a
 // CU, so every SIMD runs two waves of independent workgroups) handles one
@@ -44,7 +46,7 @@ struct KeyKind {
   static constexpr int value = K;
 };
 
-template <int MODE, int DEPTH, int RBW>
+template <int MODE, int DEPTH, int RBW, bool KV8>
 __global__ void __launch_bounds__(64 * kRowWaves) __attribute__((amdgpu_waves_per_eu(2, 2)))
 rows_kernel(const AttnArgs a) {
   static_assert(MODE == kModePrefix || MODE == kModeVerify || MODE == kModeDraft, "pass A, verify, pass B");
@@ -57,8 +59,10 @@ rows_kernel(const AttnArgs a) {
   constexpr int CPR = D / 8;   // 8-channel chunks per key row (16)
   constexpr int RS = D + 16;   // LDS row stride: rows 8 banks apart
   constexpr int STAGE = 2 * 32 * RS;  // bf16 elements of one stage: K tile, then V tile
-  constexpr int EB = 2;  // bf16 pools
-  typedef u32x4 Raw;
+  // Bytes per pool element; a chunk of 8 channels as loaded (16 bytes of
+  // bf16, or 8 bytes of FP8 E4M3 codes widened to bf16 when staged).
+  constexpr int EB = KV8 ? 1 : 2;
+  typedef typename KvChunk<KV8>::T Raw;
   // The workgroup's NT threads cover a tile's 32 keys x 16 chunks of K (and
   // of V); thread tid holds chunks tid + q*NT, q < CPT.
   constexpr int NT = 64 * kRowWaves;
@@ -570,7 +574,8 @@ rows_kernel(const AttnArgs a) {
     l[rb] = rowgroup_sum(l[rb]);
     if (!rvalid[rb]) continue;
     const float lse2 = l[rb] > 0.f ? m[rb] + fast_log2(l[rb]) : kNegInf;
-    const float f = l[rb] > 0.f ? 1.f / l[rb] : 0.f;
+    // FP8 pools: the V scale multiplies every normalised output once, here.
+    const float f = l[rb] > 0.f ? (KV8 ? a.v_scale : 1.f) / l[rb] : 0.f;
     if (a.n_splits > 1) {
 #pragma unroll
       for (int db = 0; db < DB; ++db)

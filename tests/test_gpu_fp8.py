@@ -78,6 +78,17 @@ def cases():
                                                8, 2, 128, 16, seed=53),
         "pair_16row": lambda: W.build_workload("pair_16row", [1300, 77], [[4, 4, 4], [6, 6]], 16, 2, 128, 16,
                                                seed=54),
+        # At least 1024 query rows per (request, kv head): the row-split
+        # kernel over FP8 pools -- chains over several draft tiles, a split
+        # prefix, a suffix streamed from its prefix pages (64-token pages),
+        # and draft trees.
+        "rows_chains": lambda: W.build_workload("rows_chains", [700, 0, 45], [[40] * 4, [30] * 5, [1]],
+                                                16, 2, 128, 16, seed=55),
+        "rows_split": lambda: W.build_workload("rows_split", [9000], [[64, 64]], 16, 2, 128, 16, seed=56),
+        "rows_suffix_p64": lambda: W.build_workload("rows_suffix_p64", [600], [[200]], 16, 2, 128, 64,
+                                                    seed=57, suffix_in_prefix_pages=True),
+        "rows_tree": lambda: W.attach_random_trees(
+            W.build_workload("rows_tree", [300, 90], [[64], [50]], 32, 2, 128, 16, seed=58), 59),
     }
 
 
