@@ -44,7 +44,8 @@ class PagedKV(ctypes.Structure):
                 ("num_kv_heads", ctypes.c_int32), ("head_dim", ctypes.c_int32),
                 ("page_stride", ctypes.c_int64), ("token_stride", ctypes.c_int64),
                 ("head_stride", ctypes.c_int64), ("dtype", ctypes.c_int32),
-                ("k_scale", ctypes.c_float), ("v_scale", ctypes.c_float)]
+                ("k_scale", ctypes.c_float), ("v_scale", ctypes.c_float),
+                ("k_channel_scale", ctypes.c_void_p), ("v_channel_scale", ctypes.c_void_p)]
 
 
 KV_BF16 = 0
@@ -163,6 +164,8 @@ class DeviceInputs:
     kv: PagedKV
     tree: Tree
     draft_mask: Optional[torch.Tensor] = None   # int64 view of the uint64 ancestor masks
+    k_channel_scale: Optional[torch.Tensor] = None  # fp32 [Hkv, d] (FP8 per-channel scales)
+    v_channel_scale: Optional[torch.Tensor] = None
 
     @property
     def total_rows(self) -> int:
@@ -177,11 +180,13 @@ def _bf16_tensor(x: np.ndarray, device) -> torch.Tensor:
 def make_structs(q, k_pool, v_pool, page_table, cache_seqlens, req_branch_indptr,
                  branch_qo_indptr, draft_page_table, draft_start, sm_scale,
                  max_prefix_len, max_request_rows, max_draft_len, layout="NHD",
-                 draft_mask=None, k_scale=1.0, v_scale=1.0):
+                 draft_mask=None, k_scale=1.0, v_scale=1.0, k_channel_scale=None,
+                 v_channel_scale=None):
     """layout "NHD": pools are [pages, P, Hkv, d]; "HND": [pages, Hkv, P, d].
     Pools are bf16, or uint8 / float8_e4m3fn E4M3 codes with the per-tensor
-    scales k_scale, v_scale.  draft_mask: optional 64-bit ancestor masks per
-    row (draft trees)."""
+    scales k_scale, v_scale and optional per-channel scales (fp32 device
+    tensors [Hkv, d]).  draft_mask: optional 64-bit ancestor masks per row
+    (draft trees)."""
     R, Hq, d = q.shape
     assert k_pool.stride() == v_pool.stride()
     if layout == "NHD":
@@ -197,7 +202,8 @@ def make_structs(q, k_pool, v_pool, page_table, cache_seqlens, req_branch_indptr
     assert k_pool.dtype == v_pool.dtype and (fp8 or k_pool.dtype == torch.bfloat16)
     kv = PagedKV(k_pool.data_ptr(), v_pool.data_ptr(), num_pages, P, Hkv, d, ps, ts, hs,
                  KV_FP8_E4M3 if fp8 else KV_BF16, float(k_scale) if fp8 else 0.0,
-                 float(v_scale) if fp8 else 0.0)
+                 float(v_scale) if fp8 else 0.0, _ptr(k_channel_scale) if fp8 else None,
+                 _ptr(v_channel_scale) if fp8 else None)
     tree = Tree(int(cache_seqlens.shape[0]), int(branch_qo_indptr.shape[0] - 1),
                 page_table.data_ptr(), page_table.stride(0), cache_seqlens.data_ptr(),
                 req_branch_indptr.data_ptr(), branch_qo_indptr.data_ptr(),
@@ -231,11 +237,16 @@ def to_device(wl: "_wl.Workload", device="cuda", layout="NHD") -> DeviceInputs:
     dm = None
     if getattr(wl, "draft_mask", None) is not None:
         dm = torch.from_numpy(np.ascontiguousarray(wl.draft_mask, np.uint64).view(np.int64)).to(device)
+    kcs = vcs = None
+    if fp8 and getattr(wl, "k_channel_scale", None) is not None:
+        f32 = lambda a: torch.from_numpy(np.ascontiguousarray(a, np.float32)).to(device)
+        kcs, vcs = f32(wl.k_channel_scale), f32(wl.v_channel_scale)
     query, kv, tree = make_structs(q, k, v, pt, cs, rb, qo, dpt, ds, wl.sm_scale,
                                    wl.max_prefix_len(), wl.max_rows_per_request(),
                                    wl.max_draft_len(), layout, draft_mask=dm,
-                                   k_scale=wl.k_scale if fp8 else 1.0, v_scale=wl.v_scale if fp8 else 1.0)
-    return DeviceInputs(q, k, v, pt, cs, rb, qo, dpt, ds, query, kv, tree, dm)
+                                   k_scale=wl.k_scale if fp8 else 1.0, v_scale=wl.v_scale if fp8 else 1.0,
+                                   k_channel_scale=kcs, v_channel_scale=vcs)
+    return DeviceInputs(q, k, v, pt, cs, rb, qo, dpt, ds, query, kv, tree, dm, kcs, vcs)
 
 
 # ---------------------------------------------------------------------------

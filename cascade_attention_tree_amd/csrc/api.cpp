@@ -127,6 +127,8 @@ cascade_status check_kv(const cascade_paged_kv* kv) {
   if (kv_fp8(kv) && !(std::isfinite(kv->k_scale) && kv->k_scale > 0.f && std::isfinite(kv->v_scale) &&
                       kv->v_scale > 0.f))
     return fail(CASCADE_ERR_SHAPE, "fp8 kv needs finite k_scale and v_scale > 0");
+  if (kv_fp8(kv) && !(aligned16(kv->k_channel_scale) && aligned16(kv->v_channel_scale)))
+    return fail(CASCADE_ERR_UNSUPPORTED, "fp8 channel scales must be 16-byte aligned");
   if (kv->head_dim != 64 && kv->head_dim != 128)
     return fail(CASCADE_ERR_UNSUPPORTED, "head_dim %d not supported (64 or 128)", kv->head_dim);
   if (!is_pow2(kv->page_size) || kv->page_size < 16 || kv->page_size > 4096)
@@ -222,6 +224,8 @@ casc::AttnArgs make_args(const cascade_query* q, const cascade_paged_kv* kv, con
   const double k_scale = kv_fp8(kv) ? (double)kv->k_scale : 1.0;
   a.scale_log2 = (float)((double)q->sm_scale * k_scale * 1.4426950408889634);
   a.v_scale = kv_fp8(kv) ? kv->v_scale : 1.f;
+  a.k_cs = kv_fp8(kv) ? kv->k_channel_scale : nullptr;
+  a.v_cs = kv_fp8(kv) ? kv->v_channel_scale : nullptr;
   a.kv = kv_view(kv);
   a.num_kv_heads = kv->num_kv_heads;
   a.batch_size = t->batch_size;

@@ -48,6 +48,10 @@ struct AttnArgs {
   int32_t total_rows;
   float scale_log2;  // sm_scale * k_scale * log2(e): scores are kept in base 2
   float v_scale;     // FP8 pools: the V scale, applied to normalised outputs
+  // FP8 pools, per-channel scales [Hkv, D] or NULL: K's multiply the query
+  // row (rounded to bf16) as it is loaded, V's each normalised output channel.
+  const float* k_cs;
+  const float* v_cs;
   KvView kv;
   int32_t num_kv_heads;
   int32_t batch_size;

@@ -434,6 +434,9 @@ attn_kernel(const AttnArgs a) {
         const int h = g * a.group + (rho - t * a.group);
         qtmp[it] = *reinterpret_cast<const u32x4*>(a.q + (int64_t)(tok0 + t) * a.q_row_stride +
                                                    (int64_t)h * a.q_head_stride + c * 8);
+        if constexpr (KV8) {
+          if (a.k_cs) qtmp[it] = scale_q_chunk(qtmp[it], a.k_cs + (int64_t)g * D + c * 8);
+        }
       }
     }
   }
@@ -532,8 +535,14 @@ attn_kernel(const AttnArgs a) {
                            (int64_t)(g * a.group + (rho - t * a.group)) * a.q_head_stride + g4 * 8;
       const bool ok = row_valid(rb);
 #pragma unroll
-      for (int ks = 0; ks < KS; ++ks)
+      for (int ks = 0; ks < KS; ++ks) {
         qf[rb][ks] = ok ? *reinterpret_cast<const bf16x8*>(qp + ks * 32) : bf16x8{};
+        if constexpr (KV8) {
+          if (a.k_cs)
+            qf[rb][ks] = __builtin_bit_cast(
+                bf16x8, scale_q_chunk(__builtin_bit_cast(u32x4, qf[rb][ks]), a.k_cs + (int64_t)g * D + ks * 32 + g4 * 8));
+        }
+      }
     }
   }
   auto qfrag = [&](int rb, int ks) -> bf16x8 {
@@ -1016,6 +1025,17 @@ attn_kernel(const AttnArgs a) {
     orow[rb] = rv[rb] ? row_out(rb) : 0;
   }
   const int cw = w * DBW * 16 + g4 * 4;  // first channel of this lane's blocks
+  if constexpr (KV8) {
+    // Per-channel V scales multiply each normalised output channel.
+    if (a.v_cs) {
+#pragma unroll
+      for (int dbl = 0; dbl < DBW; ++dbl) {
+        const f32x4 vs = *reinterpret_cast<const f32x4*>(a.v_cs + (int64_t)g * D + cw + dbl * 16);
+#pragma unroll
+        for (int rb = 0; rb < RB; ++rb) acc[rb][dbl] *= vs;
+      }
+    }
+  }
   if (partial) {
 #pragma unroll
     for (int rb = 0; rb < RB; ++rb) {

@@ -242,4 +242,22 @@ __device__ __forceinline__ unsigned int pack_bf16x2(float lo, float hi) {
   return __builtin_bit_cast(unsigned int, __builtin_convertvector((f32x2){lo, hi}, bf16x2));
 }
 
+// FP8 pools with per-channel K scales: q . (k * s) = (q * s) . k, so the
+// eight bf16 query channels of a 16-byte chunk are multiplied by their
+// channel scales (cs: 8 floats, 16-byte aligned) and rounded back to bf16
+// (nearest even) as they are loaded.
+__device__ __forceinline__ u32x4 scale_q_chunk(u32x4 q, const float* cs) {
+  const f32x4 s0 = *reinterpret_cast<const f32x4*>(cs);
+  const f32x4 s1 = *reinterpret_cast<const f32x4*>(cs + 4);
+  const float s[8] = {s0[0], s0[1], s0[2], s0[3], s1[0], s1[1], s1[2], s1[3]};
+  u32x4 r;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const float lo = __builtin_bit_cast(float, q[i] << 16);
+    const float hi = __builtin_bit_cast(float, q[i] & 0xffff0000u);
+    r[i] = pack_bf16x2(lo * s[2 * i], hi * s[2 * i + 1]);
+  }
+  return r;
+}
+
 }  // namespace casc

@@ -219,6 +219,9 @@ pair_kernel(const AttnArgs a) {
       const int h = g * a.group + (rho - t * a.group);
       qtmp[it] = *reinterpret_cast<const u32x4*>(a.q + (int64_t)(tok0 + t) * a.q_row_stride +
                                                  (int64_t)h * a.q_head_stride + c * 8);
+      if constexpr (KV8) {
+        if (a.k_cs) qtmp[it] = scale_q_chunk(qtmp[it], a.k_cs + (int64_t)g * D + c * 8);
+      }
     }
   }
 
@@ -610,6 +613,17 @@ pair_kernel(const AttnArgs a) {
   // ---- output ---------------------------------------------------------------------
   const bool partial = a.n_splits > 1;
   const int64_t plane = (int64_t)a.total_rows * a.num_qo_heads;
+  if constexpr (KV8) {
+    // Per-channel V scales multiply each normalised output channel.
+    if (a.v_cs) {
+#pragma unroll
+      for (int dbl = 0; dbl < DBW; ++dbl) {
+        const f32x4 vs = *reinterpret_cast<const f32x4*>(a.v_cs + (int64_t)g * D + (w * DBW + dbl) * 16 + g4 * 4);
+#pragma unroll
+        for (int rb = 0; rb < RB; ++rb) acc[rb][dbl] *= vs;
+      }
+    }
+  }
 #pragma unroll
   for (int rb = 0; rb < RB; ++rb) {
     if (!row_valid(rb)) continue;

@@ -222,8 +222,14 @@ rows_kernel(const AttnArgs a) {
     orow[rb] = (int64_t)(tok0 + rtok[rb]) * a.num_qo_heads + hq;
     const uint16_t* qp = a.q + (int64_t)(tok0 + rtok[rb]) * a.q_row_stride + (int64_t)hq * a.q_head_stride + g4 * 8;
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks)
+    for (int ks = 0; ks < KS; ++ks) {
       qf[rb][ks] = rvalid[rb] ? *reinterpret_cast<const bf16x8*>(qp + ks * 32) : bf16x8{};
+      if constexpr (KV8) {
+        if (a.k_cs)
+          qf[rb][ks] = __builtin_bit_cast(
+              bf16x8, scale_q_chunk(__builtin_bit_cast(u32x4, qf[rb][ks]), a.k_cs + (int64_t)g * D + ks * 32 + g4 * 8));
+      }
+    }
   }
 
   // ---- prefix tile loads -------------------------------------------------
@@ -574,8 +580,16 @@ rows_kernel(const AttnArgs a) {
     l[rb] = rowgroup_sum(l[rb]);
     if (!rvalid[rb]) continue;
     const float lse2 = l[rb] > 0.f ? m[rb] + fast_log2(l[rb]) : kNegInf;
-    // FP8 pools: the V scale multiplies every normalised output once, here.
+    // FP8 pools: the V scale multiplies every normalised output once, here,
+    // and per-channel V scales each output channel.
     const float f = l[rb] > 0.f ? (KV8 ? a.v_scale : 1.f) / l[rb] : 0.f;
+    if constexpr (KV8) {
+      if (a.v_cs) {
+#pragma unroll
+        for (int db = 0; db < DB; ++db)
+          o[rb][db] *= *reinterpret_cast<const f32x4*>(a.v_cs + (int64_t)g * D + db * 16 + g4 * 4);
+      }
+    }
     if (a.n_splits > 1) {
 #pragma unroll
       for (int db = 0; db < DB; ++db)

@@ -89,6 +89,10 @@ class Workload:
     v_codes: Optional[np.ndarray] = None
     k_scale: float = 1.0
     v_scale: float = 1.0
+    # Optional per-channel scales [Hkv, d] (float32): element (page, slot, g, c)
+    # is held as code(x / (scale * channel_scale[g, c])).
+    k_channel_scale: Optional[np.ndarray] = None
+    v_channel_scale: Optional[np.ndarray] = None
     # Logical (unpaged) copies, kept only when asked for: per request the prefix
     # tokens [L_i, Hkv, d], per branch its draft tokens [S_j, Hkv, d].
     prefix_k: Optional[List[np.ndarray]] = None
@@ -370,24 +374,51 @@ CONFIGS = {
 }
 
 
-def with_fp8_kv(wl: Workload, headroom: float = 440.0) -> Workload:
+def with_fp8_kv(wl: Workload, headroom: float = 440.0, per_channel: bool = False,
+                channel_spread: float = 0.0, seed: int = 0) -> Workload:
     """The same workload with FP8 KV: per-tensor scales amax(|pool|) / headroom
     (rounded to float32) and E4M3 codes of pool / scale, rounded to nearest
     even by torch's float8_e4m3fn cast.  NaN slots (never-written tokens and
     spare pages) stay NaN codes.  headroom < 448 keeps every finite value
-    below the largest code, so nothing saturates."""
+    below the largest code, so nothing saturates.
+
+    per_channel: scales per (kv head, channel) instead, the power of two at or
+    above amax over that channel / headroom, with the per-tensor scales set to
+    1 (powers of two keep the scaled bf16 query exact).  channel_spread > 0 first
+    multiplies each channel of the pools by 2^u, u uniform in
+    [-channel_spread, 0] (seeded), so that channels differ in range as real K/V
+    do (without growing any value past the unscaled pools' range)."""
     import dataclasses
 
     import torch
 
-    def encode(pool):
+    if channel_spread > 0:
+        rng = np.random.default_rng(seed)
+        Hkv, d = wl.k_pool.shape[2], wl.k_pool.shape[3]
+        fk = np.exp2(rng.uniform(-channel_spread, 0.0, (Hkv, d))).astype(np.float32)
+        fv = np.exp2(rng.uniform(-channel_spread, 0.0, (Hkv, d))).astype(np.float32)
+        wl = dataclasses.replace(wl, k_pool=(wl.k_pool * fk).astype(np.float32),
+                                 v_pool=(wl.v_pool * fv).astype(np.float32),
+                                 prefix_k=None, prefix_v=None, draft_k=None, draft_v=None)
+
+    def encode(pool, div):
+        x = torch.from_numpy(np.ascontiguousarray(pool, np.float32) / div)
+        return x.to(torch.float8_e4m3fn).view(torch.uint8).numpy().copy()
+
+    def tensor_scale(pool):
         fin = np.isfinite(pool)
         amax = float(np.max(np.abs(pool[fin]))) if fin.any() else 1.0
-        scale = float(np.float32(amax / headroom if amax > 0 else 1.0))
-        x = torch.from_numpy(np.ascontiguousarray(pool, np.float32) / np.float32(scale))
-        codes = x.to(torch.float8_e4m3fn).view(torch.uint8).numpy().copy()
-        return codes, scale
+        return float(np.float32(amax / headroom if amax > 0 else 1.0))
 
-    kc, ks = encode(wl.k_pool)
-    vc, vs = encode(wl.v_pool)
-    return dataclasses.replace(wl, name=wl.name + "_fp8", k_codes=kc, v_codes=vc, k_scale=ks, v_scale=vs)
+    def channel_scales(pool):   # pool [pages, P, Hkv, d] -> [Hkv, d]
+        a = np.where(np.isfinite(pool), np.abs(pool), 0.0).max(axis=(0, 1))
+        return np.exp2(np.ceil(np.log2(np.where(a > 0, a / headroom, 1.0)))).astype(np.float32)
+
+    if per_channel:
+        kcs, vcs = channel_scales(wl.k_pool), channel_scales(wl.v_pool)
+        return dataclasses.replace(wl, name=wl.name + "_fp8c", k_codes=encode(wl.k_pool, kcs),
+                                   v_codes=encode(wl.v_pool, vcs), k_scale=1.0, v_scale=1.0,
+                                   k_channel_scale=kcs, v_channel_scale=vcs)
+    ks, vs = tensor_scale(wl.k_pool), tensor_scale(wl.v_pool)
+    return dataclasses.replace(wl, name=wl.name + "_fp8", k_codes=encode(wl.k_pool, np.float32(ks)),
+                               v_codes=encode(wl.v_pool, np.float32(vs)), k_scale=ks, v_scale=vs)

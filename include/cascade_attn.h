@@ -66,10 +66,12 @@ typedef enum {
 typedef enum { CASCADE_F32 = 0, CASCADE_BF16 = 1 } cascade_dtype;
 
 /* Element type of the K/V pools.  FP8 KV (KV-cache tutorial page, section
- * 4.5: FP8 KV cache with a per-tensor scale): each element is an OCP FP8
- * E4M3 code (1 sign bit, 4 exponent bits with bias 7, 3 mantissa bits; no
- * infinities; 0x7F and 0xFF are NaN; largest finite 448), and stands for
- * code_value * k_scale in K, code_value * v_scale in V. */
+ * 4.5: FP8 KV cache with per-tensor or per-channel scales): each element is
+ * an OCP FP8 E4M3 code (1 sign bit, 4 exponent bits with bias 7, 3 mantissa
+ * bits; no infinities; 0x7F and 0xFF are NaN; largest finite 448), and
+ * element (page, slot, g, c) stands for code_value * k_scale *
+ * k_channel_scale[g * head_dim + c] in K (1 in place of the channel factor
+ * when k_channel_scale is NULL), and likewise with the v_ scales in V. */
 typedef enum { CASCADE_KV_BF16 = 0, CASCADE_KV_FP8_E4M3 = 1 } cascade_kv_dtype;
 
 /* One layer's paged K and V.  Element (page, slot, kv_head, c) of K is at
@@ -78,7 +80,8 @@ typedef enum { CASCADE_KV_BF16 = 0, CASCADE_KV_FP8_E4M3 = 1 } cascade_kv_dtype;
  * Requirements: head_dim in {64, 128}; page_size a power of two in [16, 4096];
  * the three strides are multiples of 8 elements, token_stride >= head_dim;
  * k and v 16-byte aligned.  dtype is a cascade_kv_dtype (0 = bf16); for FP8,
- * k_scale and v_scale must be finite and > 0 (they are ignored for bf16).
+ * k_scale and v_scale must be finite and > 0 (they and the channel scales
+ * are ignored for bf16).
  * The default layout [num_pages, page_size, Hkv, head_dim] has
  * page_stride = page_size*Hkv*head_dim, token_stride = Hkv*head_dim,
  * head_stride = head_dim. */
@@ -95,6 +98,15 @@ typedef struct {
   int32_t dtype;
   float k_scale;
   float v_scale;
+  /* FP8 only (ignored for bf16): optional per-channel scales, device fp32
+   * arrays [num_kv_heads, head_dim] (element (g, c) at g * head_dim + c),
+   * 16-byte aligned, NULL = all ones; borrowed for the call; the caller keeps
+   * them finite and > 0.  K's channel scales are applied to the query row
+   * (q . (k * s) = (q * s) . k; the scaled query is rounded to bf16, which is
+   * exact when the channel scales are powers of two), V's to each normalised
+   * output channel. */
+  const float *k_channel_scale;
+  const float *v_channel_scale;
 } cascade_paged_kv;
 
 /* Queries, bf16 [total_rows, Hq, head_dim]; element (row, h, c) at

@@ -78,13 +78,19 @@ def e4m3_value(codes):
 
 def dequantize_kv(wl):
     """The workload with its K/V pools replaced by the values its FP8 codes
-    stand for (value(code) * scale, float64).  A workload without codes is
-    returned unchanged."""
+    stand for, float64: value(code) * scale, times the channel's scale when
+    the workload has per-channel scales (tutorial page, section 4.5: per-tensor
+    or per-channel scales; pools [pages, P, Hkv, d], channel scales [Hkv, d]).
+    A workload without codes is returned unchanged."""
     import dataclasses
     if getattr(wl, "k_codes", None) is None:
         return wl
-    return dataclasses.replace(wl, k_pool=e4m3_value(wl.k_codes) * float(wl.k_scale),
-                               v_pool=e4m3_value(wl.v_codes) * float(wl.v_scale),
+    k = e4m3_value(wl.k_codes) * float(wl.k_scale)
+    v = e4m3_value(wl.v_codes) * float(wl.v_scale)
+    if getattr(wl, "k_channel_scale", None) is not None:
+        k = k * np.asarray(wl.k_channel_scale, np.float64)[None, None, :, :]
+        v = v * np.asarray(wl.v_channel_scale, np.float64)[None, None, :, :]
+    return dataclasses.replace(wl, k_pool=k, v_pool=v,
                                prefix_k=None, prefix_v=None, draft_k=None, draft_v=None)
 
 

@@ -196,7 +196,15 @@ def test_fp8_kv_checks():
         kv.dtype, kv.k_scale, kv.v_scale = B.KV_FP8_E4M3, ks, vs
         assert call_verify(q, kv, t) == B.CASCADE_ERR_SHAPE
         assert b"k_scale" in B.lib().cascade_last_error()
+    # Per-channel scales must be 16-byte aligned (FP8 only; bf16 ignores them).
+    for kcs, vcs in ((FAKE + 4, 0), (0, FAKE + 8), (FAKE + 4, FAKE + 4)):
+        q, kv, t = make()
+        kv.dtype, kv.k_scale, kv.v_scale = B.KV_FP8_E4M3, 1.0, 1.0
+        kv.k_channel_scale, kv.v_channel_scale = kcs, vcs
+        assert call_verify(q, kv, t) == B.CASCADE_ERR_UNSUPPORTED
+        assert b"channel scales" in B.lib().cascade_last_error()
     q, kv, t = make()
+    kv.k_channel_scale = FAKE + 4
     assert kv.dtype == B.KV_BF16 and kv.k_scale == 0.0
     kv.head_dim = 96   # a later check still runs: the scales were not the problem
     assert call_verify(q, kv, t) == B.CASCADE_ERR_UNSUPPORTED

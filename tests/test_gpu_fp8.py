@@ -137,6 +137,47 @@ def test_fp8_headline_all_rows(B, layout):
     assert B.cascade_device_error(clear=True) == 0
 
 
+# Per-channel scales through each kernel: key-split (16-row chunks, d 128 and
+# d 64, split prefixes, trees), pair (one-block chunks), row-split.
+CHANNEL_CASES = ["gqa_ragged", "page64_d64", "long_split", "draft_tree", "pair_16row", "rows_split"]
+
+
+@pytest.mark.parametrize("case", CHANNEL_CASES)
+def test_fp8_channel_scales(B, case):
+    """FP8 pools with per-channel scales (tutorial page, section 4.5), one
+    power of two per (kv head, channel), over pools whose channels span a
+    16x range: the fused verify, the three calls and naive expansion against
+    the oracle over the dequantised pools."""
+    wl = W.with_fp8_kv(cases()[case](), per_channel=True, channel_spread=4.0, seed=61)
+    note(f"fp8 channel scales {case}")
+    x = B.to_device(wl, layout="HND")
+    ref = O.dequantize_kv(wl)
+    ro, rl = O.cascade(ref)
+    o, l = B.cascade_verify_attn(x)
+    oa, la = B.cascade_prefix_attn(x)
+    ob, lb = B.cascade_draft_attn(x)
+    o3, l3 = B.merge_state(oa, la, ob, lb)
+    on, ln = B.naive_expand(x)
+    torch.cuda.synchronize()
+    cmp(o, l, ro, rl)
+    cmp(o3, l3, ro, rl)
+    cmp(on, ln, ro, rl)
+    assert B.cascade_device_error(clear=True) == 0
+
+
+def test_fp8_channel_scales_headline(B):
+    """The headline shapes over FP8 pools with per-channel scales: the fused
+    verify launch (pair kernel, 40-row chunks), all rows."""
+    wl = W.with_fp8_kv(W.headline(), per_channel=True, channel_spread=4.0, seed=62)
+    note("fp8 channel scales headline")
+    x = B.to_device(wl, layout="HND")
+    o, l = B.cascade_verify_attn(x, out_dtype=torch.bfloat16)
+    torch.cuda.synchronize()
+    ro, rl = O.cascade(O.dequantize_kv(wl))
+    cmp(o, l, ro, rl)
+    assert B.cascade_device_error(clear=True) == 0
+
+
 @pytest.mark.parametrize("case", CASES)
 def test_fp8_naive_expand(B, case):
     wl = fp8_case(case)

@@ -523,7 +523,48 @@ def pin_fp8_dequantize(O):
     assert dq.v_pool[0, 0, 0, 0] == wl.v_scale and dq.v_pool[0, 0, 0, 1] == -wl.v_scale
 
 
-ALL_PINS = [pin_e4m3_values, pin_fp8_dequantize, pin_gather, pin_single_key, pin_attention_vs_library, pin_merge_identity,
+def pin_fp8_channel_dequantize(O):
+    """Per-channel FP8 scales (tutorial page, section 4.5): element
+    (page, slot, g, c) stands for value(code) * scale * channel_scale[g, c].
+    Checked against torch's decode of the same codes times the channel scales,
+    against the format's rounding bound of the quantised values (per channel:
+    2^-4 relative for normal codes, 2^-10 * channel scale for subnormal ones),
+    and in the special case of equal channel scales, which is the per-tensor
+    case with that scale."""
+    base = W.build_workload("fp8c", [37, 0, 70], [[3, 2], [4], [1, 5]], 4, 2, 16, 16, seed=16,
+                            values="fp32")
+    wl = W.with_fp8_kv(base, per_channel=True, channel_spread=3.0, seed=17)
+    assert wl.k_channel_scale.shape == (2, 16) and np.ptp(wl.k_channel_scale) > 0
+    assert not np.array_equal(wl.k_channel_scale, wl.v_channel_scale)
+    dq = O.dequantize_kv(wl)
+    for codes, cs, pool in ((wl.k_codes, wl.k_channel_scale, dq.k_pool), (wl.v_codes, wl.v_channel_scale, dq.v_pool)):
+        lib = torch.from_numpy(codes.copy()).view(torch.float8_e4m3fn).to(torch.float64).numpy()
+        lib = lib * cs.astype(np.float64)[None, None, :, :]
+        assert np.array_equal(np.isnan(pool), np.isnan(lib))
+        fin = ~np.isnan(lib)
+        assert np.array_equal(pool[fin], lib[fin])
+    spread = W.with_fp8_kv(base, per_channel=False, channel_spread=3.0, seed=17)  # the same spread pools
+    for ref, pool, cs in ((spread.k_pool, dq.k_pool, wl.k_channel_scale), (spread.v_pool, dq.v_pool, wl.v_channel_scale)):
+        fin = np.isfinite(ref)
+        x = ref.astype(np.float64)
+        bound = np.maximum(np.abs(x) * 2.0 ** -4, cs.astype(np.float64)[None, None] * 2.0 ** -10) * (1 + 1e-12)
+        assert np.all(np.abs(pool - x)[fin] <= bound[fin])
+    # Equal channel scales s: the per-tensor dequantisation with scale s.
+    import dataclasses
+    s = np.float32(0.37)
+    same = dataclasses.replace(wl, k_channel_scale=np.full_like(wl.k_channel_scale, s),
+                               v_channel_scale=np.full_like(wl.v_channel_scale, s))
+    tensor = dataclasses.replace(wl, k_channel_scale=None, v_channel_scale=None, k_scale=float(s), v_scale=float(s))
+    a, b = O.dequantize_kv(same), O.dequantize_kv(tensor)
+    assert np.array_equal(np.isnan(a.k_pool), np.isnan(b.k_pool))
+    fin = ~np.isnan(a.k_pool)
+    assert np.array_equal(a.k_pool[fin], b.k_pool[fin]) and np.array_equal(a.v_pool[fin], b.v_pool[fin])
+    # A code of 1.0 in channel (g, c) stands for that channel's scale.
+    wl.k_codes[0, 0, 1, 5] = 0x38
+    assert O.dequantize_kv(wl).k_pool[0, 0, 1, 5] == float(wl.k_channel_scale[1, 5])
+
+
+ALL_PINS = [pin_e4m3_values, pin_fp8_dequantize, pin_fp8_channel_dequantize, pin_gather, pin_single_key, pin_attention_vs_library, pin_merge_identity,
             pin_merge_closed_forms, pin_brute_force, pin_topk1_is_causal, pin_zero_query,
             pin_chain_as_tree, pin_append_commit, pin_read_counts, pin_prefix_hit_pairs,
             pin_block_table_sharing]
@@ -556,8 +597,10 @@ MUTATIONS = {
     "e4m3 exponent bias 8": ("np.ldexp(1.0 + m / 8.0, (e - 7).astype(np.int32))", "np.ldexp(1.0 + m / 8.0, (e - 8).astype(np.int32))"),
     "e4m3 subnormals as normals": ("np.ldexp(m / 8.0, -6)", "np.ldexp(1.0 + m / 8.0, -7)"),
     "e4m3 sign ignored": ("sign = np.where(c & 0x80, -1.0, 1.0)", "sign = np.where(c & 0x40, -1.0, 1.0)"),
-    "fp8 scale dropped": ("k_pool=e4m3_value(wl.k_codes) * float(wl.k_scale)", "k_pool=e4m3_value(wl.k_codes)"),
-    "fp8 V takes the K scale": ("v_pool=e4m3_value(wl.v_codes) * float(wl.v_scale)", "v_pool=e4m3_value(wl.v_codes) * float(wl.k_scale)"),
+    "fp8 scale dropped": ("k = e4m3_value(wl.k_codes) * float(wl.k_scale)", "k = e4m3_value(wl.k_codes)"),
+    "fp8 V takes the K scale": ("v = e4m3_value(wl.v_codes) * float(wl.v_scale)", "v = e4m3_value(wl.v_codes) * float(wl.k_scale)"),
+    "fp8 channel scale dropped": ("k = k * np.asarray(wl.k_channel_scale, np.float64)[None, None, :, :]", "k = k * 1.0"),
+    "fp8 V takes the K channel scales": ("v = v * np.asarray(wl.v_channel_scale, np.float64)", "v = v * np.asarray(wl.k_channel_scale, np.float64)"),
     "append ignores draft_start": ("k_pool = scatter_slots(k_pool, wl.draft_page_table[j], int(wl.draft_start[j]),",
                                    "k_pool = scatter_slots(k_pool, wl.draft_page_table[j], 0,"),
 }
