@@ -65,7 +65,8 @@ class Tree(ctypes.Structure):
                 ("branch_qo_indptr", ctypes.c_void_p), ("draft_page_table", ctypes.c_void_p),
                 ("draft_page_table_stride", ctypes.c_int32), ("draft_start", ctypes.c_void_p),
                 ("max_prefix_len", ctypes.c_int32), ("max_request_rows", ctypes.c_int32),
-                ("max_draft_len", ctypes.c_int32), ("draft_mask", ctypes.c_void_p)]
+                ("max_draft_len", ctypes.c_int32), ("draft_mask", ctypes.c_void_p),
+                ("draft_mask_words", ctypes.c_int32)]
 
 
 class CascadeError(RuntimeError):
@@ -185,8 +186,8 @@ def make_structs(q, k_pool, v_pool, page_table, cache_seqlens, req_branch_indptr
     """layout "NHD": pools are [pages, P, Hkv, d]; "HND": [pages, Hkv, P, d].
     Pools are bf16, or uint8 / float8_e4m3fn E4M3 codes with the per-tensor
     scales k_scale, v_scale and optional per-channel scales (fp32 device
-    tensors [Hkv, d]).  draft_mask: optional 64-bit ancestor masks per row
-    (draft trees)."""
+    tensors [Hkv, d]).  draft_mask: optional ancestor masks (draft trees), one
+    64-bit word per row ([rows]) or W words per row ([rows, W])."""
     R, Hq, d = q.shape
     assert k_pool.stride() == v_pool.stride()
     if layout == "NHD":
@@ -209,7 +210,7 @@ def make_structs(q, k_pool, v_pool, page_table, cache_seqlens, req_branch_indptr
                 req_branch_indptr.data_ptr(), branch_qo_indptr.data_ptr(),
                 draft_page_table.data_ptr(), draft_page_table.stride(0),
                 _ptr(draft_start), int(max_prefix_len), int(max_request_rows), int(max_draft_len),
-                _ptr(draft_mask))
+                _ptr(draft_mask), 1 if draft_mask is None or draft_mask.dim() == 1 else int(draft_mask.shape[1]))
     return query, kv, tree
 
 

@@ -93,6 +93,11 @@ void plan_splits(Plan& p, int max_len, int64_t items, int64_t target, int min_sp
 }
 
 bool kv_fp8(const cascade_paged_kv* kv) { return kv->dtype == CASCADE_KV_FP8_E4M3; }
+
+// 64-bit words per row of a draft-tree mask (0 is taken as 1), and the most
+// a launch accepts (4096 nodes per branch).
+constexpr int kMaxMaskWords = 64;
+int mask_words(const cascade_tree* t) { return t->draft_mask_words > 1 ? t->draft_mask_words : 1; }
 int elem_bytes(const cascade_paged_kv* kv) { return kv_fp8(kv) ? 1 : 2; }
 
 // Bytes from the start of a page to the end of its last (token, head) row.
@@ -193,8 +198,14 @@ cascade_status check_tree(const cascade_tree* t, const cascade_paged_kv* kv) {
       (int64_t)t->draft_page_table_stride * kv->page_size < t->max_draft_len)
     return fail(CASCADE_ERR_SHAPE, "draft_page_table_stride * page_size < max_draft_len");
   if (t->draft_mask) {
-    if (t->max_draft_len > 64)
-      return fail(CASCADE_ERR_UNSUPPORTED, "draft trees (draft_mask) are limited to 64 nodes per branch");
+    const int words = mask_words(t);
+    if (t->draft_mask_words < 0 || words > kMaxMaskWords)
+      return fail(CASCADE_ERR_UNSUPPORTED, "draft_mask_words %d not supported (0 .. %d)", (int)t->draft_mask_words,
+                  kMaxMaskWords);
+    if (t->max_draft_len > 64 * words)
+      return fail(CASCADE_ERR_UNSUPPORTED,
+                  "draft trees (draft_mask) are limited to 64 * draft_mask_words = %d nodes per branch",
+                  64 * words);
     if (reinterpret_cast<uintptr_t>(t->draft_mask) & 7u)
       return fail(CASCADE_ERR_UNSUPPORTED, "draft_mask must be 8-byte aligned");
   }
@@ -238,6 +249,7 @@ casc::AttnArgs make_args(const cascade_query* q, const cascade_paged_kv* kv, con
   a.draft_page_table_stride = t->draft_page_table_stride;
   a.draft_start = t->draft_start;
   a.draft_mask = t->draft_mask;
+  a.draft_mask_words = mask_words(t);
   a.n_chunks = p.n_chunks;
   a.grid_splits = 1;
   a.n_splits = p.n_splits;
@@ -635,6 +647,7 @@ cascade_status cascade_debug_gather(const cascade_paged_kv* kv, const cascade_tr
   a.draft_page_table_stride = t->draft_page_table_stride;
   a.draft_start = t->draft_start;
   a.draft_mask = t->draft_mask;
+  a.draft_mask_words = mask_words(t);
   a.which = which;
   a.index = index;
   a.kv_head = kv_head;
@@ -656,6 +669,9 @@ cascade_status cascade_debug_mask(const cascade_tree* t, int32_t branch, uint8_t
   if (mask_cols < 0) return fail(CASCADE_ERR_SHAPE, "mask_cols must be >= 0");
   if (t->draft_mask && (reinterpret_cast<uintptr_t>(t->draft_mask) & 7u))
     return fail(CASCADE_ERR_UNSUPPORTED, "draft_mask must be 8-byte aligned");
+  if (t->draft_mask && (t->draft_mask_words < 0 || mask_words(t) > kMaxMaskWords))
+    return fail(CASCADE_ERR_UNSUPPORTED, "draft_mask_words %d not supported (0 .. %d)", (int)t->draft_mask_words,
+                kMaxMaskWords);
   int32_t ends[2];
   hipError_t e = hipMemcpy(ends, t->branch_qo_indptr + branch, 2 * sizeof(int32_t), hipMemcpyDeviceToHost);
   if (e != hipSuccess) return hip_fail(e, "reading branch length");
@@ -665,6 +681,7 @@ cascade_status cascade_debug_mask(const cascade_tree* t, int32_t branch, uint8_t
   a.req_branch_indptr = t->req_branch_indptr;
   a.branch_qo_indptr = t->branch_qo_indptr;
   a.draft_mask = t->draft_mask;
+  a.draft_mask_words = mask_words(t);
   a.index = branch;
   a.count = ends[1] - ends[0];
   a.cols = mask_cols;

@@ -64,6 +64,7 @@ struct AttnArgs {
   int32_t draft_page_table_stride;
   const int32_t* draft_start;
   const uint64_t* draft_mask;  // per row: ancestor set over its branch's nodes (NULL: chains)
+  int32_t draft_mask_words;    // 64-bit words per row of draft_mask (>= 1)
   int32_t n_seg_items;  // (segment, kv head) pairs of the launch (key-split kernel)
   int32_t n_chunks;     // row chunks per segment and kv head
   int32_t chunk_rows;   // pair kernel: query rows per chunk (<= 16 * its row blocks)
@@ -163,6 +164,7 @@ struct DebugArgs {
   int32_t draft_page_table_stride;
   const int32_t* draft_start;
   const uint64_t* draft_mask;
+  int32_t draft_mask_words;
   int32_t which;
   int32_t index;
   int32_t kv_head;

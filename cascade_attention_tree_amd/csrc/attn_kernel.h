@@ -414,8 +414,18 @@ attn_kernel(const AttnArgs a) {
     for (int rb = 0; rb < RB; ++rb) {
       rtok[rb] = row_tok(rb);
       rbs[rb] = t_rbs[rtok[rb] - tok_first];
-      if (tree) ranc[rb] = a.draft_mask[tok0 + rtok[rb]];
+      if (tree) ranc[rb] = a.draft_mask[(int64_t)(tok0 + rtok[rb]) * a.draft_mask_words];
     }
+  };
+  // The window of row block rb's ancestor set for a tile from token `base`
+  // on (a one-word set from its register, more words from memory), and the
+  // token of the window's first node.
+  auto tree_win = [&](int rb, int base, uint64_t& win, int& wbs) {
+    const int ws = max(base - rbs[rb], 0);
+    win = a.draft_mask_words == 1
+              ? tree_window1(ranc[rb], ws)
+              : tree_window(a.draft_mask + (int64_t)(tok0 + rtok[rb]) * a.draft_mask_words, a.draft_mask_words, ws);
+    wbs = rbs[rb] + ws;
   };
 
   // ---- Q rows of the chunk (into registers now, into LDS below) ---------
@@ -654,12 +664,15 @@ attn_kernel(const AttnArgs a) {
     if (tree) {
 #pragma unroll
       for (int rb = 0; rb < RB; ++rb) {
+        uint64_t win;
+        int wbs;
+        tree_win(rb, base, win, wbs);
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb) {
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
             const int key = base + kb * 16 + g4 * 4 + i;
-            const bool vis = (key < end) & draft_visible_tree(ranc[rb], rbs[rb], key);
+            const bool vis = (key < end) & draft_visible_tree(win, wbs, key);
             s[rb][kb][i] = vis ? s[rb][kb][i] : kNegInf;
           }
         }

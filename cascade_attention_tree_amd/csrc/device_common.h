@@ -90,6 +90,20 @@ __device__ __forceinline__ bool draft_visible_tree(uint64_t anc, int bs, int kt)
   const int u = kt - bs;
   return (u >= 0) & (u < 64) & (((anc >> (u & 63)) & 1ull) != 0ull);
 }
+// Trees of more than 64 nodes keep a row's ancestor set in `words` 64-bit
+// words (bit u % 64 of word u / 64: node u).  A tile of keys from token
+// `base` on sees the 64-node window of the set that starts at node
+// ws = max(base - bs, 0): tree_window returns it (bit v: node ws + v, zeros
+// past the last word), and draft_visible_tree(window, bs + ws, kt) decides
+// every key kt of the tile.  tree_window1: the same for a one-word set held
+// in a register.
+__device__ __forceinline__ uint64_t tree_window(const uint64_t* row_mask, int words, int ws) {
+  const int i = ws >> 6, sh = ws & 63;
+  const uint64_t lo = i < words ? row_mask[i] : 0ull;
+  const uint64_t hi = i + 1 < words ? row_mask[i + 1] : 0ull;
+  return (lo >> sh) | ((hi << 1) << (63 - sh));
+}
+__device__ __forceinline__ uint64_t tree_window1(uint64_t anc, int ws) { return ws < 64 ? anc >> ws : 0ull; }
 
 // Element offset (kv head excluded) of logical slot `slot` of draft
 // block-table row `row` (`stride` entries), or -1 when the slot lies outside

@@ -517,7 +517,7 @@ pair_kernel(const AttnArgs a) {
     for (int rb = 0; rb < RB; ++rb) {
       rtok[rb] = row_tok(rb);
       rbs[rb] = t_rbs[rtok[rb] - tok_first];
-      if (tree) ranc[rb] = a.draft_mask[tok0 + rtok[rb]];
+      if (tree) ranc[rb] = a.draft_mask[(int64_t)(tok0 + rtok[rb]) * a.draft_mask_words];
     }
     for (int base = dlo; base < dhi; base += 32) {
       if (base != dlo) {
@@ -530,16 +530,27 @@ pair_kernel(const AttnArgs a) {
       f32x4 s[RB][2];
       scores(kr, s);
 #pragma unroll
-      for (int rb = 0; rb < RB; ++rb)
+      for (int rb = 0; rb < RB; ++rb) {
+        // The tree's window for this tile (see tree_window).
+        uint64_t win = 0;
+        int wbs = 0;
+        if (tree) {
+          const int ws = max(base - rbs[rb], 0);
+          win = a.draft_mask_words == 1 ? tree_window1(ranc[rb], ws)
+                                        : tree_window(a.draft_mask + (int64_t)(tok0 + rtok[rb]) * a.draft_mask_words,
+                                                      a.draft_mask_words, ws);
+          wbs = rbs[rb] + ws;
+        }
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
             const int key = base + kb * 16 + g4 * 4 + i;
-            const bool vis = (key < dhi) & (tree ? draft_visible_tree(ranc[rb], rbs[rb], key)
+            const bool vis = (key < dhi) & (tree ? draft_visible_tree(win, wbs, key)
                                                  : draft_visible(rtok[rb], rbs[rb], key));
             s[rb][kb][i] = vis ? s[rb][kb][i] : kNegInf;
           }
+      }
       accumulate(s);
     }
   }

@@ -414,12 +414,19 @@ rows_kernel(const AttnArgs a) {
     for (int rb = 0; rb < RBW; ++rb) {
       // One uniform branch per tile picks the rule (tree masks or chains).
       if (kind == 1 && tree) {
+        // The tree's window for this tile (see tree_window).
+        const int ws = max(base - rbs[rb], 0);
+        const uint64_t win =
+            a.draft_mask_words == 1
+                ? tree_window1(ranc[rb], ws)
+                : tree_window(a.draft_mask + (int64_t)(tok0 + rtok[rb]) * a.draft_mask_words, a.draft_mask_words, ws);
+        const int wbs = rbs[rb] + ws;
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
             const int key = base + kb * 16 + g4 * 4 + i;
-            const bool vis = (key < end) & draft_visible_tree(ranc[rb], rbs[rb], key);
+            const bool vis = (key < end) & draft_visible_tree(win, wbs, key);
             s[rb][kb][i] = vis ? s[rb][kb][i] : kNegInf;
           }
       } else if (kind == 1) {
@@ -485,7 +492,7 @@ rows_kernel(const AttnArgs a) {
   if ((kDraft || kVerify) && slot_mode && tree) {
 #pragma unroll
     for (int rb = 0; rb < RBW; ++rb)
-      if (rvalid[rb]) ranc[rb] = a.draft_mask[tok0 + rtok[rb]];
+      if (rvalid[rb]) ranc[rb] = a.draft_mask[(int64_t)(tok0 + rtok[rb]) * a.draft_mask_words];
   }
   // The key loop over the current key range, its first DEPTH tiles requested:
   // tile 0 into stage 0 (slots in front of `front` as zeros); its slot then
@@ -559,7 +566,7 @@ rows_kernel(const AttnArgs a) {
       for (int rb = 0; rb < RBW; ++rb)
         if (rvalid[rb]) {
           rbs[rb] = t_rbs[rtok[rb] - tok_first];
-          if (tree) ranc[rb] = a.draft_mask[tok0 + rtok[rb]];
+          if (tree) ranc[rb] = a.draft_mask[(int64_t)(tok0 + rtok[rb]) * a.draft_mask_words];
         }
       for (int base = dlo; base < dhi; base += 32) {
         if (base != dlo) load_draft(base, dt, dkeep);

@@ -183,7 +183,12 @@ __global__ void __launch_bounds__(256) debug_mask_kernel(const DebugArgs a) {
     vis = 1;
   } else if (t < L + S) {
     const int kt = bs + (t - L);
-    vis = (a.draft_mask ? draft_visible_tree(a.draft_mask[a.branch_qo_indptr[j] + s], bs, kt)
+    // The kernels' tree rule: the window of the row's set from key kt on.
+    const int ws = kt - bs;
+    vis = (a.draft_mask ? draft_visible_tree(
+                              tree_window(a.draft_mask + (int64_t)(a.branch_qo_indptr[j] + s) * a.draft_mask_words,
+                                          a.draft_mask_words, ws),
+                              bs + ws, kt)
                         : draft_visible(bs + s, bs, kt))
               ? 1
               : 0;

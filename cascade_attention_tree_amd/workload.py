@@ -263,20 +263,22 @@ def build_workload(name: str,
 
 
 def attach_random_trees(wl: Workload, seed: int, max_children: int = 4) -> Workload:
-    """Turn every branch of ``wl`` into a random draft tree over its S_j nodes
-    (S_j <= 64): nodes are created level by level, each node of a level picking
-    its parent uniformly among the previous level's nodes that still have fewer
-    than ``max_children`` children (level 0 hangs off the prefix).  Sets
-    ``draft_parent`` and ``draft_mask`` (uint64 per row)."""
+    """Turn every branch of ``wl`` into a random draft tree over its S_j nodes:
+    nodes are created level by level, each node of a level picking its parent
+    uniformly among the previous level's nodes that still have fewer than
+    ``max_children`` children (level 0 hangs off the prefix).  Sets
+    ``draft_parent`` and ``draft_mask``: one uint64 per row when every S_j <= 64,
+    else [rows, W] uint64 words with W = ceil(max S_j / 64) (bit u % 64 of word
+    u // 64: node u)."""
     rng = np.random.default_rng(seed)
     R = wl.total_rows
     parent = np.full(R, -1, np.int32)
-    mask = np.zeros(R, np.uint64)
     qo = wl.branch_qo_indptr
+    max_s = int(np.max(np.diff(qo))) if wl.num_branches else 0
+    words = max(1, -(-max_s // 64))
+    mask = np.zeros((R, words), np.uint64)
     for j in range(wl.num_branches):
         r0, S = int(qo[j]), int(qo[j + 1] - qo[j])
-        if S > 64:
-            raise ValueError("draft trees are limited to 64 nodes per branch")
         par = np.full(S, -1, np.int64)
         prev = [-1]                      # level 0: children of the prefix
         nxt: List[int] = []
@@ -294,15 +296,15 @@ def attach_random_trees(wl: Workload, seed: int, max_children: int = 4) -> Workl
             u += 1
             if rng.random() < 0.35 and nxt:
                 prev, nxt = prev + nxt, []
-        m = np.zeros(S, np.uint64)
+        m = [0] * S                      # ancestor sets as Python integers
         for u in range(S):
-            m[u] = np.uint64(1) << np.uint64(u)
-            if par[u] >= 0:
-                m[u] |= m[par[u]]
+            m[u] = (1 << u) | (m[par[u]] if par[u] >= 0 else 0)
         parent[r0:r0 + S] = par
-        mask[r0:r0 + S] = m
+        for u in range(S):
+            for w in range(words):
+                mask[r0 + u, w] = np.uint64((m[u] >> (64 * w)) & 0xFFFFFFFFFFFFFFFF)
     wl.draft_parent = parent
-    wl.draft_mask = mask
+    wl.draft_mask = mask[:, 0].copy() if words == 1 else mask
     wl.meta["trees"] = {"seed": seed, "max_children": max_children}
     return wl
 

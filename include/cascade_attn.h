@@ -135,14 +135,16 @@ typedef struct {
  *                    (the per-branch page table of pass B)
  *  draft_start       [num_branches] or NULL: draft token u of branch j sits at logical
  *                    slot draft_start[j] + u of its row (NULL means 0).
- *  draft_mask        uint64 [total_rows] or NULL (8-byte aligned).  NULL: every branch
- *                    is a chain, its position s attends its positions 0..s.  Else
- *                    a general draft tree (tree attention mask, tutorial page section
+ *  draft_mask        uint64 [total_rows, W] or NULL (8-byte aligned), W =
+ *                    draft_mask_words (0 is taken as 1).  NULL: every branch is a
+ *                    chain, its position s attends its positions 0..s.  Else a
+ *                    general draft tree (tree attention mask, tutorial page section
  *                    8.2): the row of branch j's position s attends branch j's draft
- *                    positions u whose bit u is set (its ancestors and itself; a
- *                    request's tree is one branch holding all of its nodes, numbered
- *                    so that parents precede children).  Requires max_draft_len <= 64
- *                    (CASCADE_ERR_UNSUPPORTED otherwise); bits at or past S_j are ignored.
+ *                    positions u whose bit u % 64 of word u / 64 is set (its ancestors
+ *                    and itself; a request's tree is one branch holding all of its
+ *                    nodes, numbered so that parents precede children).  Requires
+ *                    max_draft_len <= 64 * W and W <= 64 (CASCADE_ERR_UNSUPPORTED
+ *                    otherwise); bits at or past S_j must be zero.
  * Host-side maxima, used to size launches; the caller promises them:
  *  max_prefix_len    >= every L_i
  *  max_request_rows  >= the number of query rows of every request
@@ -162,6 +164,7 @@ typedef struct {
   int32_t max_request_rows;
   int32_t max_draft_len;
   const uint64_t *draft_mask;
+  int32_t draft_mask_words;
 } cascade_tree;
 
 /* Bytes of workspace cascade_prefix_attn and cascade_verify_attn need for these

@@ -270,7 +270,9 @@ def draft_visible(wl, j, s):
         return np.arange(s + 1)
     r0 = int(wl.branch_qo_indptr[j])
     S = int(wl.branch_qo_indptr[j + 1]) - r0
-    m = int(wl.draft_mask[r0 + s])
+    # One 64-bit word per row, or W words (bit u % 64 of word u // 64: node u).
+    words = np.atleast_1d(np.asarray(wl.draft_mask[r0 + s], np.uint64))
+    m = sum(int(x) << (64 * w) for w, x in enumerate(words))
     return np.array([u for u in range(S) if (m >> u) & 1], np.int64)
 
 

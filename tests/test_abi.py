@@ -159,12 +159,26 @@ def test_kernel_timing_without_a_timed_call():
 
 
 def test_draft_tree_limits():
+    """A tree of S nodes needs ceil(S / 64) mask words per row (0 words is
+    one), at most 64 words; masks are 8-byte aligned."""
     q, kv, t = make(dmax=65)
     t.draft_page_table_stride = 8
     mask = (ctypes.c_uint64 * 64)()
     t.draft_mask = ctypes.addressof(mask)
+    for words in (0, 1):
+        t.draft_mask_words = words
+        assert call_verify(q, kv, t) == B.CASCADE_ERR_UNSUPPORTED
+        assert b"64 * draft_mask_words = 64 nodes" in B.lib().cascade_last_error()
+    for words in (-1, 65):
+        t.draft_mask_words = words
+        assert call_verify(q, kv, t) == B.CASCADE_ERR_UNSUPPORTED
+        assert b"draft_mask_words" in B.lib().cascade_last_error()
+    q, kv, t = make(dmax=129)
+    t.draft_page_table_stride = 16
+    t.draft_mask = ctypes.addressof(mask)
+    t.draft_mask_words = 2
     assert call_verify(q, kv, t) == B.CASCADE_ERR_UNSUPPORTED
-    assert b"64 nodes" in B.lib().cascade_last_error()
+    assert b"= 128 nodes" in B.lib().cascade_last_error()
     q, kv, t = make(dmax=64)
     t.draft_page_table_stride = 8
     t.draft_mask = ctypes.addressof(mask) + 4

@@ -82,6 +82,14 @@ def small_cases():
             W.build_workload("draft_tree", [75, 0, 300], [[12], [7], [20]], 8, 2, 128, 16, seed=27), 28),
         "draft_tree_big": lambda: W.attach_random_trees(
             W.build_workload("draft_tree_big", [200, 40], [[64], [33]], 16, 2, 64, 16, seed=29), 30),
+        # Trees of more than 64 nodes (3-word ancestor masks): 150- and
+        # 70-node trees on the pair kernel (600 rows per kv head) and in pass B
+        # and naive expansion on the key-split kernel; at d = 64 on the
+        # key-split kernel throughout.
+        "wide_tree_masks": lambda: W.attach_random_trees(
+            W.build_workload("wide_tree_masks", [300, 0], [[150], [70]], 8, 2, 128, 16, seed=63), 64),
+        "wide_tree_masks_d64": lambda: W.attach_random_trees(
+            W.build_workload("wide_tree_masks_d64", [130, 77], [[100], [129]], 4, 2, 64, 16, seed=65), 66),
         # At least 1024 query rows per (request, kv head) at d = 128: pass A
         # and the fused verify pass run the row-split kernel.  Chains whose
         # 40-token branches span several draft tiles of a 128-row chunk, an
@@ -107,6 +115,10 @@ def small_cases():
                                                     seed=37),
         "rows_split_slot_tree": lambda: W.attach_random_trees(
             W.build_workload("rows_split_slot_tree", [5000, 2100], [[64], [40]], 32, 2, 128, 16, seed=38), 39),
+        # A 300-node tree streamed through the row-split kernel's ring loop
+        # (1200 rows per kv head; 5-word masks), with a split prefix.
+        "rows_wide_tree": lambda: W.attach_random_trees(
+            W.build_workload("rows_wide_tree", [4500], [[300]], 8, 2, 128, 16, seed=67), 68),
         # A 600-token suffix (one branch continuing its prefix pages) at d = 64,
         # which the key-split kernel runs: row chunks near the end of the
         # suffix see more than 512 draft keys, past the LDS table of draft-key
@@ -374,12 +386,15 @@ def _check_gather(B, wl, layout, label):
     assert B.cascade_device_error(clear=True) == 0
 
 
-@pytest.mark.parametrize("tree", [False, True])
+@pytest.mark.parametrize("tree", ["chains", "tree", "wide_tree"])
 def test_mask_hook_bit_exact(B, tree):
     wl = W.build_workload("gm", [75, 0, 300], [[2, 4, 1], [3], [1, 5]], 8, 2, 128, 16, seed=51)
-    if tree:
+    if tree == "tree":
         wl = W.build_workload("gm_tree", [75, 0, 300], [[13], [3], [40]], 8, 2, 128, 16, seed=52)
         W.attach_random_trees(wl, 53)
+    elif tree == "wide_tree":   # 2- and 3-word ancestor masks
+        wl = W.build_workload("gm_wide_tree", [75, 0, 30], [[130], [3], [90]], 8, 2, 128, 16, seed=54)
+        W.attach_random_trees(wl, 55)
     x = B.to_device(wl)
     note("debug mask")
     for j in range(wl.num_branches):

@@ -80,6 +80,24 @@ def wl_chain_masks(seed=14):
     return wl
 
 
+def wl_big_trees(seed=18):
+    # Trees of more than 64 nodes (150 and 70: 3-word ancestor masks), and a
+    # 130-node chain written out as a tree.
+    wl = W.build_workload("pin_big_trees", [21, 0], [[150], [70]], 4, 2, 16, page_size=8,
+                          seed=seed, values="fp32", keep_logical=True)
+    return W.attach_random_trees(wl, seed + 1)
+
+
+def wl_long_chain_masks(seed=20):
+    wl = W.build_workload("pin_long_chain", [9], [[130]], 2, 1, 16, page_size=16,
+                          seed=seed, values="fp32", keep_logical=True)
+    S = 130
+    wl.draft_parent = np.arange(-1, S - 1).astype(np.int32)
+    m = [(1 << (u + 1)) - 1 for u in range(S)]
+    wl.draft_mask = np.array([[(x >> (64 * w)) & 0xFFFFFFFFFFFFFFFF for w in range(3)] for x in m], np.uint64)
+    return wl
+
+
 def ancestors(wl, j, s):
     """Draft node s of branch j and its ancestors, by walking the parent array
     (chains: parent u - 1)."""
@@ -327,14 +345,22 @@ def pin_chain_as_tree(O):
     n0, m0 = O.naive_expand(wl)
     assert np.array_equal(o1, o0) and np.array_equal(l1, l0)
     assert np.array_equal(n1, n0) and np.array_equal(m1, m0)
-    wl = wl_trees()
-    for j in range(wl.num_branches):
-        S = int(wl.branch_qo_indptr[j + 1] - wl.branch_qo_indptr[j])
-        for s in range(S):
-            assert list(O.draft_visible(wl, j, s)) == ancestors(wl, j, s)
+    # Past 64 nodes the masks span several words: a long chain as a tree again
+    # gives the chain's bits, and random trees' masks are their ancestor sets.
+    wl = wl_long_chain_masks()
+    assert wl.draft_mask.shape == (130, 3)
+    o1, l1 = O.cascade(wl)
+    wl.draft_parent, wl.draft_mask = None, None
+    o0, l0 = O.cascade(wl)
+    assert np.array_equal(o1, o0) and np.array_equal(l1, l0)
+    for wl in (wl_trees(), wl_big_trees()):
+        for j in range(wl.num_branches):
+            S = int(wl.branch_qo_indptr[j + 1] - wl.branch_qo_indptr[j])
             vm = O.visibility_mask(wl, j)
             L = vm.shape[1] - S
-            assert vm[s, L:].nonzero()[0].tolist() == ancestors(wl, j, s)
+            for s in range(S):
+                assert list(O.draft_visible(wl, j, s)) == ancestors(wl, j, s)
+                assert vm[s, L:].nonzero()[0].tolist() == ancestors(wl, j, s)
 
 
 def pin_append_commit(O):
@@ -584,7 +610,9 @@ MUTATIONS = {
     "slot/page swapped": ("return np.asarray(pool[pages, t % page_size]", "return np.asarray(pool[pages, t // page_size % page_size]"),
     "draft excludes self (chains)": ("return np.arange(s + 1)", "return np.arange(s)"),
     "tree mask shifted": ("if (m >> u) & 1]", "if (m >> (u + 1)) & 1]"),
-    "tree mask ignored": ("m = int(wl.draft_mask[r0 + s])", "m = (2 << s) - 1"),
+    "tree mask ignored": ("m = sum(int(x) << (64 * w) for w, x in enumerate(words))", "m = (2 << s) - 1"),
+    "tree mask words reversed": ("m = sum(int(x) << (64 * w) for w, x in enumerate(words))",
+                                 "m = sum(int(x) << (64 * w) for w, x in enumerate(words[::-1]))"),
     "naive drops the drafts": ("k = np.concatenate([kp, kd[vis]], axis=0)", "k = np.concatenate([kp, kd[vis[:1]]], axis=0)"),
     "merge weights swapped": ("o = wa[..., None] * o_a + wb[..., None] * o_b", "o = wb[..., None] * o_a + wa[..., None] * o_b"),
     "merge without log": ("lse = np.where(empty, -np.inf, m_safe + np.log(np.where(empty, 1.0, tot)))", "lse = np.where(empty, -np.inf, m_safe + np.where(empty, 1.0, tot) - 1)"),
