@@ -391,7 +391,8 @@ hipError_t launch_row_modes(int mode, const cascade_paged_kv* kv,
   if (kv->head_dim != 128 || rows < kRowKernelMinRows)
     return launch(mode, kv->head_dim, p.rb, a, (int64_t)t->batch_size * kv->num_kv_heads, splits, s, e0, e1);
   a.n_chunks = (int)(rows > 0 ? cdiv(rows, casc::kRowsPerItem) : 1);
-  const int64_t grid = (int64_t)t->batch_size * kv->num_kv_heads * a.n_chunks * splits;
+  a.n_seg_items = (int32_t)((int64_t)t->batch_size * kv->num_kv_heads);
+  const int64_t grid = xcd_grid(a.n_seg_items, a.n_chunks, splits);
   if (grid <= 0) return hipSuccess;
   return kv_fp8(kv) ? casc::launch_rows_d128_fp8(mode, a, (int)grid, s, e0, e1)
                     : casc::launch_rows_d128(mode, a, (int)grid, s, e0, e1);

@@ -65,7 +65,7 @@ struct AttnArgs {
   const int32_t* draft_start;
   const uint64_t* draft_mask;  // per row: ancestor set over its branch's nodes (NULL: chains)
   int32_t draft_mask_words;    // 64-bit words per row of draft_mask (>= 1)
-  int32_t n_seg_items;  // (segment, kv head) pairs of the launch (key-split kernel)
+  int32_t n_seg_items;  // (segment, kv head) pairs of the launch (key-split and row-split kernels)
   int32_t n_chunks;     // row chunks per segment and kv head
   int32_t chunk_rows;   // pair kernel: query rows per chunk (<= 16 * its row blocks)
   int32_t grid_splits;  // key splits in this launch's grid

@@ -92,17 +92,23 @@ rows_kernel(const AttnArgs a) {
   const int l16 = lane & 15;
   const int g4 = lane >> 4;
 
-  // ---- work item: key splits slowest, row chunks fastest (as attn_kernel) --
-  int item = blockIdx.x;
+  // ---- work item: key splits slowest; within a split, workgroup u goes to
+  // XCD u % 8 (round-robin dispatch) and u / 8 walks the row chunks of one
+  // (request, kv head) pair, then the next pair of that XCD.  The chunks of a
+  // pair then run side by side on one L2 and stream the same key tiles at
+  // about the same time, so the tiles come from HBM once per XCD, not once
+  // per chunk.
   const int per_split = (int)gridDim.x / a.grid_splits;
-  const int split = item / per_split;
-  item -= split * per_split;
+  const int split = (int)blockIdx.x / per_split;
+  const int u = (int)blockIdx.x - split * per_split;
+  const int v8 = u >> 3;
   // Pass B is causal: a chunk's keys end at its last token, so later chunks
   // are longer (in pass B and in the fused verify).  They are handed out
   // longest first, so that the short ones fill in behind them instead of the
   // long ones forming the launch's tail.
-  const int chunk = (kDraft || kVerify) ? a.n_chunks - 1 - item % a.n_chunks : item % a.n_chunks;
-  item /= a.n_chunks;
+  const int chunk = (kDraft || kVerify) ? a.n_chunks - 1 - v8 % a.n_chunks : v8 % a.n_chunks;
+  const int item = (v8 / a.n_chunks) * 8 + (u & 7);
+  if (item >= a.n_seg_items) return;
   const int g = item % a.num_kv_heads;
   const int req = item / a.num_kv_heads;
   cint32* crb = as_const(a.req_branch_indptr);
