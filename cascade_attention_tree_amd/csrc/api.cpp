@@ -68,6 +68,10 @@ struct Plan {
   bool pair = false;
   int pair_chunks = 1;
   int pair_rows = 0;
+  // Pass A, the fused verify pass and pass B on the row-split kernel: chunks
+  // of kRowsPerItem rows, row_chunks per (request, kv head).
+  bool rows_kernel = false;
+  int row_chunks = 1;
 };
 
 void plan_rows(Plan& p, int64_t rows_per_segment) {
@@ -258,25 +262,26 @@ casc::AttnArgs make_args(const cascade_query* q, const cascade_paged_kv* kv, con
 }
 
 // Query rows per (request, kv head) from which pass A, the fused verify pass
-// and pass B run the row-split kernel (head dim 128, bf16 or FP8 pools): at least
-// four full work items of kRowsPerItem rows, where its two waves per SIMD keep
-// the matrix pipes busy (a prefix-hit suffix prefill).
-constexpr int64_t kRowKernelMinRows = 1024;
+// and pass B run the row-split kernel (head dim 128, bf16 or FP8 pools): more
+// than one key-split chunk holds.  Its workgroups share each K/V tile among
+// four waves of 32 rows through LDS, and with a workspace its items come from
+// a device-built work list, longest first and none empty: on the ragged batch
+// (64 requests, 48 to 512 rows per kv head, prefixes of 512 to 32768 keys)
+// 0.65 ms against 0.91 ms on the pair kernel in 48-row chunks.
+constexpr int64_t kRowKernelMinRows = 16 * kMaxRowBlocks + 1;
 
 // Plan of the per-request launches (pass A, pass B, verify).  At head_dim 128,
-// pass A and the fused verify pass of requests below kRowKernelMinRows rows
-// per kv head run on the pair kernel (chunks of up to kPairRows rows, two
-// workgroups per CU, the chunks of a (request, kv head) sharing its prefix
-// stream through one L2) -- except bf16 pools whose (request, kv head) pairs
-// already fill the device with one chunk of at most 16 * kMaxRowBlocks rows
-// each: there the key-split kernel, one workgroup per CU holding all rows,
-// measured faster (60.6 against 64.5 us at 32 requests x 8 kv heads x 80
-// rows), while the pair kernel is faster over FP8 pools, on the ragged
-// batch.  With too few (request, kv head) pairs to fill the device, a
-// request's rows are cut in more chunks before its prefix is split; when
-// they are at most 16 * kMaxRowBlocks and even one 16-row block per chunk
-// leaves at most a workgroup per CU (the GQA
-// configuration: 8 requests x 8 kv heads x 48 rows, 192 chunks), the
+// pass A and the fused verify pass of requests with at most 16 * kMaxRowBlocks
+// rows per kv head run on the pair kernel (chunks of up to kPairRows rows,
+// two workgroups per CU, the chunks of a (request, kv head) sharing its
+// prefix stream through one L2) -- except bf16 pools whose (request, kv head)
+// pairs already fill the device with one chunk each: there the key-split
+// kernel, one workgroup per CU holding all rows, measured faster (60.6 against
+// 64.5 us at 32 requests x 8 kv heads x 80 rows), while the pair kernel is
+// faster over FP8 pools.  With too few (request, kv head) pairs to fill the
+// device, a request's rows are cut in more chunks before its prefix is split;
+// when even one 16-row block per chunk leaves at most a workgroup per CU (the
+// GQA configuration: 8 requests x 8 kv heads x 48 rows, 192 chunks), the
 // key-split kernel runs those 16-row chunks, its four waves sharing each
 // chunk's prefix (19.9 us there, against 21.5 us on the pair kernel with
 // 12-row chunks and 24.8 us with 16-row chunks padded to 48), and a prefix
@@ -295,7 +300,13 @@ Plan plan_request(const cascade_query* q, const cascade_paged_kv* kv, const casc
   p.items = pairs * p.n_chunks;
   const bool one_chunk_fills = !kv_fp8(kv) && rows <= 16 * kMaxRowBlocks && pairs >= kTargetItems;
   p.pair = !thin && kv->head_dim == 128 && rows > 0 && rows < kRowKernelMinRows && !one_chunk_fills;
-  if (p.pair) {
+  p.rows_kernel = kv->head_dim == 128 && rows >= kRowKernelMinRows;
+  if (p.rows_kernel) {
+    // Splits planned from the row-split kernel's own work items (two
+    // workgroups per CU).
+    p.row_chunks = (int)cdiv(rows, casc::kRowsPerItem);
+    plan_splits(p, t->max_prefix_len, pairs * p.row_chunks, kPairTargetItems);
+  } else if (p.pair) {
     p.pair_chunks = (int)cdiv(rows, casc::kPairRows);
     // Few (request, kv head) pairs: smaller chunks (down to one 16-row block)
     // until the launch holds a workgroup per CU.
@@ -314,19 +325,43 @@ int64_t pair_grid_per_split(const cascade_tree* t, const cascade_paged_kv* kv, c
   return cdiv((int64_t)t->batch_size * kv->num_kv_heads, 8) * 8 * p.pair_chunks;
 }
 
+// Workspace: the split partial states (required when the prefix is split),
+// then the row-split kernel's work list (optional: without room for it the
+// launch takes its items in the fixed grid order).
 struct WsLayout {
-  size_t bytes = 0;
+  size_t required = 0;  // partial states
+  size_t bytes = 0;     // partial states and work list
   size_t lse_off = 0;
+  size_t list_off = 0;  // work-list count, then the entries 256 bytes on
+  int64_t list_entries = 0;
 };
 
-WsLayout ws_layout(const cascade_query* q, const cascade_paged_kv* kv, const Plan& p) {
+WsLayout ws_layout(const cascade_query* q, const cascade_paged_kv* kv, const cascade_tree* t, const Plan& p) {
   WsLayout w;
-  if (p.n_splits <= 1) return w;
-  const size_t plane = (size_t)q->total_rows * q->num_qo_heads;
-  const size_t o_bytes = (size_t)p.n_splits * plane * kv->head_dim * sizeof(float);
-  w.lse_off = (o_bytes + 255) / 256 * 256;
-  w.bytes = w.lse_off + (size_t)p.n_splits * plane * sizeof(float);
+  size_t end = 0;
+  if (p.n_splits > 1) {
+    const size_t plane = (size_t)q->total_rows * q->num_qo_heads;
+    const size_t o_bytes = (size_t)p.n_splits * plane * kv->head_dim * sizeof(float);
+    w.lse_off = (o_bytes + 255) / 256 * 256;
+    end = w.lse_off + (size_t)p.n_splits * plane * sizeof(float);
+  }
+  w.required = end;
+  if (p.rows_kernel && t->batch_size > 0) {
+    w.list_entries = (int64_t)t->batch_size * p.n_splits * p.row_chunks;
+    w.list_off = (end + 255) / 256 * 256;
+    end = w.list_off + 256 + (size_t)w.list_entries * sizeof(int32_t);
+  }
+  w.bytes = end;
   return w;
+}
+
+// The work list of a row-split launch in `ws`, or null when the workspace
+// has no room for it.
+void attach_work_list(casc::AttnArgs& a, const WsLayout& wl, void* ws, size_t ws_bytes) {
+  if (wl.list_entries <= 0 || !ws || ws_bytes < wl.bytes) return;
+  char* base = static_cast<char*>(ws) + wl.list_off;
+  a.work_count = reinterpret_cast<int32_t*>(base);
+  a.work_list = reinterpret_cast<int32_t*>(base + 256);
 }
 
 // Arguments of the split merge that follows a split prefix or verify pass.
@@ -387,12 +422,33 @@ hipError_t launch_row_modes(int mode, const cascade_paged_kv* kv,
     return kv_fp8(kv) ? casc::launch_pair_d128_fp8(mode, a, (int)grid, s, e0, e1)
                       : casc::launch_pair_d128(mode, a, (int)grid, s, e0, e1);
   }
-  const int64_t rows = (int64_t)t->max_request_rows * p.group;
-  if (kv->head_dim != 128 || rows < kRowKernelMinRows)
+  if (!p.rows_kernel)
     return launch(mode, kv->head_dim, p.rb, a, (int64_t)t->batch_size * kv->num_kv_heads, splits, s, e0, e1);
-  a.n_chunks = (int)(rows > 0 ? cdiv(rows, casc::kRowsPerItem) : 1);
+  a.n_chunks = p.row_chunks;
   a.n_seg_items = (int32_t)((int64_t)t->batch_size * kv->num_kv_heads);
-  const int64_t grid = xcd_grid(a.n_seg_items, a.n_chunks, splits);
+  int64_t grid = xcd_grid(a.n_seg_items, a.n_chunks, splits);
+  if (a.work_list) {
+    casc::WorkListArgs w{};
+    w.batch_size = t->batch_size;
+    w.cache_seqlens = t->cache_seqlens;
+    w.req_branch_indptr = t->req_branch_indptr;
+    w.branch_qo_indptr = t->branch_qo_indptr;
+    w.num_branches = t->num_branches;
+    w.group = p.group;
+    w.n_chunks = a.n_chunks;
+    w.n_splits = a.n_splits;
+    w.split_len = a.split_len;
+    w.drafts = mode != casc::kModePrefix;
+    // Work buckets of 2^shift tiles: the longest item below 256 buckets.
+    const int64_t most = cdiv(p.split_len, 32) + cdiv((int64_t)t->max_request_rows, 32);
+    while ((most >> w.bucket_shift) >= 255) ++w.bucket_shift;
+    w.list = const_cast<int32_t*>(a.work_list);
+    w.count = const_cast<int32_t*>(a.work_count);
+    const hipError_t e = casc::launch_worklist(w, s, e0);
+    if (e != hipSuccess) return e;
+    e0 = nullptr;
+    grid = (int64_t)t->batch_size * a.n_splits * a.n_chunks * kv->num_kv_heads;
+  }
   if (grid <= 0) return hipSuccess;
   return kv_fp8(kv) ? casc::launch_rows_d128_fp8(mode, a, (int)grid, s, e0, e1)
                     : casc::launch_rows_d128(mode, a, (int)grid, s, e0, e1);
@@ -438,7 +494,7 @@ const char* cascade_last_error(void) { return g_last_error.c_str(); }
 
 size_t cascade_workspace_size(const cascade_query* q, const cascade_paged_kv* kv, const cascade_tree* t) {
   if (check_all(q, kv, t) != CASCADE_OK) return 0;
-  return ws_layout(q, kv, plan_request(q, kv, t)).bytes;
+  return ws_layout(q, kv, t, plan_request(q, kv, t)).bytes;
 }
 
 cascade_status cascade_prefix_attn(const cascade_query* q, const cascade_paged_kv* kv,
@@ -449,14 +505,15 @@ cascade_status cascade_prefix_attn(const cascade_query* q, const cascade_paged_k
   if (q->total_rows > 0 && (!o_a || !lse_a)) return fail(CASCADE_ERR_NULL, "o_a and lse_a are required");
   if (o_a && !aligned16(o_a)) return fail(CASCADE_ERR_UNSUPPORTED, "o_a must be 16-byte aligned");
   const Plan p = plan_request(q, kv, t);
-  const WsLayout wl = ws_layout(q, kv, p);
-  if (wl.bytes > 0 && (!ws || ws_bytes < wl.bytes))
-    return fail(CASCADE_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", wl.bytes, ws ? ws_bytes : 0);
+  const WsLayout wl = ws_layout(q, kv, t, p);
+  if (wl.required > 0 && (!ws || ws_bytes < wl.required))
+    return fail(CASCADE_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", wl.required, ws ? ws_bytes : 0);
   if (ws && !aligned16(ws)) return fail(CASCADE_ERR_UNSUPPORTED, "workspace must be 16-byte aligned");
   if ((st = check_plan_grid(t, kv, p)) != CASCADE_OK) return st;
   if (q->total_rows == 0 || t->batch_size == 0) return CASCADE_OK;
   hipStream_t s = static_cast<hipStream_t>(stream);
   casc::AttnArgs a = make_args(q, kv, t, p);
+  attach_work_list(a, wl, ws, ws_bytes);
   a.o = o_a;
   a.o_bf16 = 0;
   a.lse = lse_a;
@@ -529,14 +586,15 @@ static cascade_status verify_impl(const cascade_query* q, const cascade_paged_kv
   if (q->total_rows > 0 && !o) return fail(CASCADE_ERR_NULL, "o is NULL");
   if (o && !aligned16(o)) return fail(CASCADE_ERR_UNSUPPORTED, "o must be 16-byte aligned");
   const Plan p = plan_request(q, kv, t);
-  const WsLayout wl = ws_layout(q, kv, p);
-  if (wl.bytes > 0 && (!ws || ws_bytes < wl.bytes))
-    return fail(CASCADE_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", wl.bytes, ws ? ws_bytes : 0);
+  const WsLayout wl = ws_layout(q, kv, t, p);
+  if (wl.required > 0 && (!ws || ws_bytes < wl.required))
+    return fail(CASCADE_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", wl.required, ws ? ws_bytes : 0);
   if (ws && !aligned16(ws)) return fail(CASCADE_ERR_UNSUPPORTED, "workspace must be 16-byte aligned");
   if ((st = check_plan_grid(t, kv, p)) != CASCADE_OK) return st;
   if (q->total_rows == 0 || t->batch_size == 0) return CASCADE_OK;
   hipStream_t s = static_cast<hipStream_t>(stream);
   casc::AttnArgs a = make_args(q, kv, t, p);
+  attach_work_list(a, wl, ws, ws_bytes);
   a.o = o;
   a.o_bf16 = o_dtype == CASCADE_BF16;
   a.lse = lse;
@@ -570,7 +628,7 @@ cascade_status cascade_verify_attn_noalloc(const cascade_query* q, const cascade
                                            float* lse, void* stream) {
   cascade_status st = check_all(q, kv, t);
   if (st != CASCADE_OK) return st;
-  const size_t need = ws_layout(q, kv, plan_request(q, kv, t)).bytes;
+  const size_t need = ws_layout(q, kv, t, plan_request(q, kv, t)).bytes;
   if (need > casc::kScratchBytes)
     return fail(CASCADE_ERR_WORKSPACE,
                 "these shapes need %zu bytes of workspace; the built-in workspace holds %zu "

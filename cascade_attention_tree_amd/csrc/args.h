@@ -76,6 +76,30 @@ struct AttnArgs {
   float* lse;
   float* ws_o;    // [n_splits, total_rows, Hq, D] normalised partial outputs
   float* ws_lse;  // [n_splits, total_rows, Hq] partial LSE, base 2
+  // Row-split kernel: the launch's work items, longest first (built on the
+  // device by worklist_kernel), or NULL for the fixed grid order.  Entry e
+  // of *work_count is (request * n_splits + split) * n_chunks + chunk;
+  // workgroup u takes entry u / num_kv_heads, kv head u % num_kv_heads.
+  const int32_t* work_list;
+  const int32_t* work_count;
+};
+
+// Work list of a row-split launch: every (request, key split, row chunk)
+// that has work, sorted by its 32-key tiles, longest first.
+struct WorkListArgs {
+  int32_t batch_size;
+  const int32_t* cache_seqlens;
+  const int32_t* req_branch_indptr;
+  const int32_t* branch_qo_indptr;
+  int32_t num_branches;
+  int32_t group;       // query heads per kv head
+  int32_t n_chunks;    // row chunks per request (kRowsPerItem rows each)
+  int32_t n_splits;    // key splits of the prefix
+  int32_t split_len;   // keys per split
+  int32_t drafts;      // 1: split 0 also takes the request's draft tiles
+  int32_t bucket_shift;  // work buckets hold 2^bucket_shift tiles each
+  int32_t* list;       // [batch_size * n_splits * n_chunks] entries (first *count used)
+  int32_t* count;      // entries written
 };
 
 // Merge of the key-split partial states of pass A or the fused verify pass

@@ -36,6 +36,9 @@ hipError_t launch_pair_d128(int mode, const AttnArgs& a, int grid, hipStream_t s
 hipError_t launch_pair_d128_fp8(int mode, const AttnArgs& a, int grid, hipStream_t s, hipEvent_t ev_start,
                                 hipEvent_t ev_stop);
 
+// Work list of a row-split launch (one workgroup); ev_start (may be null):
+// event recorded when it starts.
+hipError_t launch_worklist(const WorkListArgs& a, hipStream_t s, hipEvent_t ev_start);
 hipError_t launch_merge(const MergeArgs& a, hipStream_t s);
 // Merge of key-split partial states; e1 (may be null): event recorded when it ends.
 hipError_t launch_split_merge(const SplitMergeArgs& a, hipStream_t s, hipEvent_t e1);

@@ -98,19 +98,40 @@ rows_kernel(const AttnArgs a) {
   // pair then run side by side on one L2 and stream the same key tiles at
   // about the same time, so the tiles come from HBM once per XCD, not once
   // per chunk.
-  const int per_split = (int)gridDim.x / a.grid_splits;
-  const int split = (int)blockIdx.x / per_split;
-  const int u = (int)blockIdx.x - split * per_split;
-  const int v8 = u >> 3;
-  // Pass B is causal: a chunk's keys end at its last token, so later chunks
-  // are longer (in pass B and in the fused verify).  They are handed out
-  // longest first, so that the short ones fill in behind them instead of the
-  // long ones forming the launch's tail.
-  const int chunk = (kDraft || kVerify) ? a.n_chunks - 1 - v8 % a.n_chunks : v8 % a.n_chunks;
-  const int item = (v8 / a.n_chunks) * 8 + (u & 7);
-  if (item >= a.n_seg_items) return;
-  const int g = item % a.num_kv_heads;
-  const int req = item / a.num_kv_heads;
+  // With a work list (launches that have a workspace), workgroup u takes
+  // entry u / Hkv for kv head u % Hkv instead: the items come longest first
+  // and none is empty, and with 8 kv heads XCD x takes kv head x of every
+  // entry, so the XCDs get the same work in the same order.
+  int split, chunk, g, req;
+  if (a.work_list) {
+    const int u = (int)blockIdx.x;
+    const int e = u / a.num_kv_heads;
+    if (e >= *as_const(a.work_count)) return;
+    g = u - e * a.num_kv_heads;
+    const int c = as_const(a.work_list)[e];
+    chunk = c % a.n_chunks;
+    const int rs = c / a.n_chunks;
+    split = rs % a.n_splits;
+    req = rs / a.n_splits;
+  } else {
+    const int per_split = (int)gridDim.x / a.grid_splits;
+    split = (int)blockIdx.x / per_split;
+    const int u = (int)blockIdx.x - split * per_split;
+    const int v8 = u >> 3;
+    // Pass B is causal: a chunk's keys end at its last token, so later chunks
+    // are longer (in pass B and in the fused verify).  They are handed out
+    // longest first, so that the short ones fill in behind them instead of
+    // the long ones forming the launch's tail.
+    chunk = (kDraft || kVerify) ? a.n_chunks - 1 - v8 % a.n_chunks : v8 % a.n_chunks;
+    const int item = (v8 / a.n_chunks) * 8 + (u & 7);
+    if (item >= a.n_seg_items) return;
+    g = item % a.num_kv_heads;
+    req = item / a.num_kv_heads;
+  }
+  split = __builtin_amdgcn_readfirstlane(split);
+  chunk = __builtin_amdgcn_readfirstlane(chunk);
+  g = __builtin_amdgcn_readfirstlane(g);
+  req = __builtin_amdgcn_readfirstlane(req);
   cint32* crb = as_const(a.req_branch_indptr);
   cint32* cqo = as_const(a.branch_qo_indptr);
   const int jb = crb[req];
@@ -403,6 +424,10 @@ rows_kernel(const AttnArgs a) {
     for (int rb = 0; rb < RBW; ++rb)
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb) s[rb][kb] = f32x4{0.f, 0.f, 0.f, 0.f};
+    // The matrix phases run at raised wave priority: when the two waves of
+    // a SIMD (independent workgroups) both have work, the one with MFMAs to
+    // issue goes first and the other's softmax fills in behind it.
+    __builtin_amdgcn_s_setprio(1);
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
@@ -415,6 +440,7 @@ rows_kernel(const AttnArgs a) {
     for (int rb = 0; rb < RBW; ++rb)
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb) asm volatile("" : "+v"(s[rb][kb]));
+    __builtin_amdgcn_s_setprio(0);
     bf16x8 pf[RBW];
 #pragma unroll
     for (int rb = 0; rb < RBW; ++rb) {
@@ -484,12 +510,14 @@ rows_kernel(const AttnArgs a) {
                         pack_bf16x2(p[6], p[7])};
       pf[rb] = __builtin_bit_cast(bf16x8, pk);
     }
+    __builtin_amdgcn_s_setprio(1);
 #pragma unroll
     for (int db = 0; db < DB; ++db) {
       const bf16x8 vf = vt_frag(st, db);
 #pragma unroll
       for (int rb = 0; rb < RBW; ++rb) o[rb][db] = mfma16(vf, pf[rb], o[rb][db]);
     }
+    __builtin_amdgcn_s_setprio(0);
   };
 
   // Request token of the wave's first row (its rows' tokens are not smaller).

@@ -102,6 +102,86 @@ hipError_t launch_split_merge(const SplitMergeArgs& a, hipStream_t s, hipEvent_t
   return hipGetLastError();
 }
 
+// Work list of a row-split launch.  Every (request, key split, row chunk)
+// whose split starts inside the request's prefix (split 0 always) and whose
+// chunk starts inside its query rows (chunk 0 always) gets an entry, so the
+// list leaves out only items the row-split kernel would return from at once;
+// the entries are sorted by their 32-key tiles (prefix keys of the split,
+// plus the tiles of the draft keys its rows can see for split 0, shifted
+// right by bucket_shift), longest first, with a counting sort over
+// kWorkBuckets buckets in LDS.  Ties keep roughly the order of the entry
+// index (chunk fastest), so the chunks of one (request, split) stay side by
+// side.  One workgroup of 1024 threads.
+constexpr int kWorkBuckets = 256;
+
+__global__ void __launch_bounds__(1024) worklist_kernel(const WorkListArgs a) {
+  __shared__ int hist[kWorkBuckets];
+  __shared__ int cur[kWorkBuckets];
+  const int tid = (int)threadIdx.x;
+  for (int b = tid; b < kWorkBuckets; b += 1024) hist[b] = 0;
+  __syncthreads();
+  const int64_t n = (int64_t)a.batch_size * a.n_splits * a.n_chunks;
+  // Tiles of entry c, or -1 when the row-split kernel has nothing to do.
+  auto work = [&](int64_t c) -> int {
+    const int chunk = (int)(c % a.n_chunks);
+    const int64_t rs = c / a.n_chunks;
+    const int split = (int)(rs % a.n_splits);
+    const int req = (int)(rs / a.n_splits);
+    const int L = a.cache_seqlens[req];
+    const int64_t k0 = (int64_t)split * a.split_len;
+    if (split != 0 && k0 >= L) return -1;
+    const int jb = a.req_branch_indptr[req];
+    const int je = a.req_branch_indptr[req + 1];
+    int ntok = 0;
+    if (jb >= 0 && je >= jb && je <= a.num_branches) {
+      const int t0 = a.branch_qo_indptr[jb];
+      const int t1 = a.branch_qo_indptr[je];
+      ntok = t1 > t0 ? t1 - t0 : 0;
+    }
+    const int64_t nrows = (int64_t)ntok * a.group;
+    const int64_t row0 = (int64_t)chunk * kRowsPerItem;
+    if (chunk != 0 && row0 >= nrows) return -1;
+    int64_t keys = (int64_t)L - k0;
+    keys = keys < 0 ? 0 : (keys > a.split_len ? a.split_len : keys);
+    int64_t tiles = (keys + 31) / 32;
+    // Draft keys the chunk can see end after its last token.
+    if (split == 0 && a.drafts && nrows > row0) {
+      const int64_t last = (row0 + kRowsPerItem < nrows ? row0 + kRowsPerItem : nrows) - 1;
+      tiles += (last / a.group + 1 + 31) / 32;
+    }
+    tiles >>= a.bucket_shift;
+    return (int)(tiles < kWorkBuckets - 1 ? tiles : kWorkBuckets - 1);
+  };
+  for (int64_t c = tid; c < n; c += 1024) {
+    const int w = work(c);
+    if (w >= 0) atomicAdd(&hist[w], 1);
+  }
+  __syncthreads();
+  if (tid == 0) {
+    int acc = 0;
+    for (int b = kWorkBuckets - 1; b >= 0; --b) {
+      cur[b] = acc;
+      acc += hist[b];
+    }
+    *a.count = acc;
+  }
+  __syncthreads();
+  for (int64_t c = tid; c < n; c += 1024) {
+    const int w = work(c);
+    if (w >= 0) a.list[atomicAdd(&cur[w], 1)] = (int)c;
+  }
+}
+
+hipError_t launch_worklist(const WorkListArgs& a, hipStream_t s, hipEvent_t ev_start) {
+  const dim3 g(1), b(1024);
+  if (ev_start) {
+    hipExtLaunchKernelGGL(worklist_kernel, g, b, 0, s, ev_start, nullptr, 0, a);
+  } else {
+    hipLaunchKernelGGL(worklist_kernel, g, b, 0, s, a);
+  }
+  return hipGetLastError();
+}
+
 // Copies `count` tokens of one kv head with the gather functions of the
 // attention kernels.  which == 0, the prefix of request `index`: the token's
 // 16-key half gets its page id from the block-table row (checked_page) and

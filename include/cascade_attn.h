@@ -167,8 +167,14 @@ typedef struct {
   int32_t draft_mask_words;
 } cascade_tree;
 
-/* Bytes of workspace cascade_prefix_attn and cascade_verify_attn need for these
- * shapes (0 when the prefix pass runs unsplit).  Returns 0 on invalid arguments. */
+/* Bytes of workspace cascade_prefix_attn and cascade_verify_attn take for these
+ * shapes: the partial states of a split prefix, required when the prefix pass
+ * is split, then, for launches of more than 80 query rows per (request, kv
+ * head) at head_dim 128, room for a work list that the call builds on the
+ * device (the launch's work items, longest first).  The work list is
+ * optional: a workspace that holds the partial states but not the list (or
+ * none, when the prefix is unsplit) gives the same results with the items
+ * taken in a fixed order.  0 when neither applies; 0 on invalid arguments. */
 CASCADE_API size_t cascade_workspace_size(const cascade_query *q, const cascade_paged_kv *kv,
                               const cascade_tree *tree);
 

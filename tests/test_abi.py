@@ -128,6 +128,27 @@ def test_workspace_rules():
     assert lib.cascade_workspace_size(ctypes.byref(q), ctypes.byref(kv), ctypes.byref(t)) == 0
 
 
+def test_work_list_workspace():
+    lib = B.lib()
+    size = lambda q, kv, t: lib.cascade_workspace_size(ctypes.byref(q), ctypes.byref(kv), ctypes.byref(t))
+    # 40 query tokens x 8 query heads per kv head = 320 rows per (request, kv
+    # head) at head_dim 128, a 400-key prefix (unsplit): the workspace is only
+    # the row-split kernel's work list, a 256-byte count block and one int32
+    # per (request, split, 128-row chunk).
+    q, kv, t = make(B_=4, Hq=16, Hkv=2, L=400, rows=40, branches=8, dmax=10)
+    assert size(q, kv, t) == 256 + 4 * (4 * 1 * 3)
+    # 80 rows: the key-split or pair kernel, no work list.
+    q, kv, t = make(B_=4, Hq=16, Hkv=2, L=400, rows=10, branches=8, dmax=5)
+    assert size(q, kv, t) == 0
+    # d = 64 has no row-split kernel.
+    q, kv, t = make(B_=4, Hq=16, Hkv=2, d=64, L=400, rows=40, branches=8, dmax=10)
+    assert size(q, kv, t) == 0
+    # A split prefix: the partial states of at least two splits (rows x Hq x
+    # (d + 1) floats each), then the list.
+    q, kv, t = make(B_=1, Hq=16, Hkv=2, L=9000, rows=40, branches=4, dmax=10, npages=600)
+    assert size(q, kv, t) > 2 * 40 * 16 * 129 * 4 + 256
+
+
 def test_merge_state_validation():
     lib = B.lib()
     assert lib.merge_state(FAKE, FAKE, FAKE, FAKE, 4, 2, 6, FAKE, 0, None, None) == B.CASCADE_ERR_UNSUPPORTED

@@ -50,6 +50,13 @@ def cmp(o_gpu, lse_gpu, o_ref, lse_ref):
     assert err_l <= LSE_TOL, f"max |lse - ref| = {err_l}"
 
 
+# 28 requests of 5 query tokens, 80 rows per (request, kv head) over 56
+# pairs: the pair kernel's one-block instance (16-row chunks).
+PAIR16_LENS = [1300, 77, 0, 512, 33, 900, 260, 1, 640, 100, 1024, 7, 450, 300,
+               64, 1111, 16, 800, 5, 230, 999, 48, 700, 129, 31, 600, 2, 1200]
+PAIR16_BRANCHES = [[5], [4, 1], [2, 3], [1, 2, 2]] * 7
+
+
 def cases():
     """Several tiles and ragged tails, both head dims, page sizes 16/32/64, a
     split prefix, more branches than a wave has lanes, and draft trees."""
@@ -76,8 +83,11 @@ def cases():
         # prefix, and the pair kernel's one-block instance.
         "thin_split": lambda: W.build_workload("thin_split", [2500, 300, 0], [[3, 2], [5], [1, 1, 1]],
                                                8, 2, 128, 16, seed=53),
-        "pair_16row": lambda: W.build_workload("pair_16row", [1300, 77], [[4, 4, 4], [6, 6]], 16, 2, 128, 16,
+        "pair_16row": lambda: W.build_workload("pair_16row", PAIR16_LENS, PAIR16_BRANCHES, 32, 2, 128, 16,
                                                seed=54),
+        # 96 rows per (request, kv head): one row-split item each.
+        "rows_small": lambda: W.build_workload("rows_small", [1300, 77], [[4, 4, 4], [6, 6]], 16, 2, 128, 16,
+                                               seed=71),
         # At least 1024 query rows per (request, kv head): the row-split
         # kernel over FP8 pools -- chains over several draft tiles, a split
         # prefix, a suffix streamed from its prefix pages (64-token pages),

@@ -51,6 +51,12 @@ def cmp(o_gpu, lse_gpu, o_ref, lse_ref, rows=None, o_tol=O_TOL, lse_tol=LSE_TOL)
     return err_o, err_l
 
 
+# 28 requests of 5 query tokens (one to three branches), prefixes 0 to 1300.
+PAIR16_LENS = [1300, 77, 0, 512, 33, 900, 260, 1, 640, 100, 1024, 7, 450, 300,
+               64, 1111, 16, 800, 5, 230, 999, 48, 700, 129, 31, 600, 2, 1200]
+PAIR16_BRANCHES = [[5], [4, 1], [2, 3], [1, 2, 2]] * 7
+
+
 def small_cases():
     """Shapes chosen to span several tiles, ragged tails, splits and chunks."""
     return {
@@ -68,10 +74,15 @@ def small_cases():
         # key-split kernel, the longest prefix split in three.
         "thin_split": lambda: W.build_workload("thin_split", [2500, 300, 0], [[3, 2], [5], [1, 1, 1]],
                                                8, 2, 128, 16, seed=51),
-        # 96 rows per (request, kv head) over 4 pairs: six 16-row chunks on
-        # the pair kernel's one-block instance.
-        "pair_16row": lambda: W.build_workload("pair_16row", [1300, 77], [[4, 4, 4], [6, 6]], 16, 2, 128, 16,
+        # 80 rows per (request, kv head) over 56 pairs, too few to fill the
+        # device: five 16-row chunks each on the pair kernel's one-block
+        # instance.
+        "pair_16row": lambda: W.build_workload("pair_16row", PAIR16_LENS, PAIR16_BRANCHES, 32, 2, 128, 16,
                                                seed=52),
+        # 96 rows per (request, kv head) over 4 pairs: one row-split item each
+        # (three of its four waves hold rows), a 1300-key prefix split.
+        "rows_small": lambda: W.build_workload("rows_small", [1300, 77], [[4, 4, 4], [6, 6]], 16, 2, 128, 16,
+                                               seed=69),
         # More branches per request than one wave has lanes (70), and more than
         # the per-workgroup branch window holds (130): the tree tables' slow paths.
         "wide_tree": lambda: W.build_workload("wide_tree", [300, 50], [[1] * 70, [2] * 130], 4, 2, 64, 16,
@@ -83,7 +94,7 @@ def small_cases():
         "draft_tree_big": lambda: W.attach_random_trees(
             W.build_workload("draft_tree_big", [200, 40], [[64], [33]], 16, 2, 64, 16, seed=29), 30),
         # Trees of more than 64 nodes (3-word ancestor masks): 150- and
-        # 70-node trees on the pair kernel (600 rows per kv head) and in pass B
+        # 70-node trees on the row-split kernel (600 rows per kv head) and in pass B
         # and naive expansion on the key-split kernel; at d = 64 on the
         # key-split kernel throughout.
         "wide_tree_masks": lambda: W.attach_random_trees(
@@ -171,6 +182,31 @@ def test_verify_and_three_call_path(B, case, layout):
     torch.cuda.synchronize()
     cmp(o, l, ro, rl)
     cmp(o3, l3, ro, rl)
+
+
+@pytest.mark.parametrize("layout", ["NHD", "HND"])
+def test_rows_kernel_fixed_order(B, layout):
+    """The row-split kernel without room for its work list (no workspace, an
+    unsplit prefix): its items in the fixed grid order give results equal,
+    bit for bit, to the work-list order, and match the oracle."""
+    wl = W.build_workload("rows_short", [500, 0, 300, 45], [[40] * 4, [30] * 5, [12, 9], [1]], 16, 2, 128, 16,
+                          seed=70)
+    note(f"rows fixed order {layout}")
+    x = B.to_device(wl, layout=layout)
+    ws = B.workspace_for(x)
+    assert ws is not None and ws.numel() > 0, "the row-split launch has a work list"
+    none = torch.empty(0, dtype=torch.uint8, device="cuda")
+    o1, l1 = B.cascade_verify_attn(x, workspace=ws)
+    o0, l0 = B.cascade_verify_attn(x, workspace=none)
+    a1, la1 = B.cascade_prefix_attn(x, workspace=ws)
+    a0, la0 = B.cascade_prefix_attn(x, workspace=none)
+    torch.cuda.synchronize()
+    assert torch.equal(o0, o1) and torch.equal(l0, l1)
+    assert torch.equal(a0, a1) and torch.equal(la0, la1)
+    ro, rl = O.cascade(wl)
+    cmp(o0, l0, ro, rl)
+    ra, rla = O.prefix_pass(wl)
+    cmp(a0, la0, ra, rla)
 
 
 @pytest.mark.parametrize("layout", ["NHD", "HND"])
