@@ -1021,9 +1021,11 @@ attn_kernel(const AttnArgs a) {
     default: combine(WaveIndex<3>{}); break;
   }
 
-  // Split prefix passes stop at a partial state; everything else is final.
+  // Split prefix passes stop at a partial state; everything else is final,
+  // including a request whose keys all fall in split 0 (the split merge
+  // leaves its rows alone).
   bool partial = false;
-  if constexpr (MODE == kModePrefix || MODE == kModeVerify) partial = a.n_splits > 1;
+  if constexpr (MODE == kModePrefix || MODE == kModeVerify) partial = a.n_splits > 1 && L > a.split_len;
 
   // ---- output ----------------------------------------------------------------
   // Row addresses and values are formed first and the stores issued back to

@@ -622,7 +622,9 @@ pair_kernel(const AttnArgs a) {
   }
 
   // ---- output ---------------------------------------------------------------------
-  const bool partial = a.n_splits > 1;
+  // A request whose keys all fall in split 0 writes its final output (the
+  // split merge leaves its rows alone).
+  const bool partial = a.n_splits > 1 && L > a.split_len;
   const int64_t plane = (int64_t)a.total_rows * a.num_qo_heads;
   if constexpr (KV8) {
     // Per-channel V scales multiply each normalised output channel.

@@ -192,7 +192,11 @@ rows_kernel(const AttnArgs a) {
       pt_row = as_const(a.draft_page_table + (int64_t)jb * a.draft_page_table_stride);
       slot_range(p0, p1);
     }
-  } else {
+  }
+  // A request whose keys all fall in split 0 writes its final output (the
+  // split merge leaves its rows alone).
+  bool partial = false;
+  if constexpr (!kDraft) {
   int L = L_in;
   {
     const int cap = a.page_table_stride << a.kv.log2_page;
@@ -214,6 +218,7 @@ rows_kernel(const AttnArgs a) {
   p1 = min(L, p0 + a.split_len);
   if (a.n_splits > 1 && p0 >= L && (MODE == kModePrefix || split != 0)) return;
   if (p1 < p0) p1 = p0;
+  partial = a.n_splits > 1 && L > a.split_len;
   }
   p0 = __builtin_amdgcn_readfirstlane(p0);
   p1 = __builtin_amdgcn_readfirstlane(p1);
@@ -631,7 +636,7 @@ rows_kernel(const AttnArgs a) {
           o[rb][db] *= *reinterpret_cast<const f32x4*>(a.v_cs + (int64_t)g * D + db * 16 + g4 * 4);
       }
     }
-    if (a.n_splits > 1) {
+    if (partial) {
 #pragma unroll
       for (int db = 0; db < DB; ++db)
         *reinterpret_cast<f32x4*>(a.ws_o + (split * plane + orow[rb]) * D + db * 16 + g4 * 4) = o[rb][db] * f;

@@ -47,7 +47,8 @@ __global__ void __launch_bounds__(256) merge_state_kernel(const MergeArgs a) {
 // splittability of standard attention), splits in order.  A request with L
 // keys has partials for splits 0 .. ceil(L / split_len) - 1 (the fused
 // verify pass also for split 0 when L = 0: it holds the drafts); no partial
-// means o = 0, LSE = -inf.  One thread per 4 channels of one (row, head):
+// means o = 0, LSE = -inf.  Rows of a request with a single split are final
+// already (the attention kernels write them directly) and are skipped.  One thread per 4 channels of one (row, head):
 // every partial of that slice is loaded before any is combined.
 __global__ void __launch_bounds__(256) split_merge_kernel(const SplitMergeArgs a) {
   const int d4 = a.head_dim >> 2;
@@ -68,6 +69,8 @@ __global__ void __launch_bounds__(256) split_merge_kernel(const SplitMergeArgs a
   int nsp = (L + a.split_len - 1) / a.split_len;
   if (a.verify && nsp < 1) nsp = 1;
   if (nsp > a.n_splits) nsp = a.n_splits;
+  // One split: the attention kernel wrote the final output itself.
+  if (nsp == 1) return;
   float M = kNegInf;
   for (int sp = 0; sp < nsp; ++sp) M = fmaxf(M, a.ws_lse[sp * plane + rh]);
   const float ms = M == kNegInf ? 0.f : M;
