@@ -111,20 +111,25 @@ hipError_t launch_split_merge(const SplitMergeArgs& a, hipStream_t s, hipEvent_t
 // list leaves out only items the row-split kernel would return from at once;
 // the entries are sorted by their 32-key tiles (prefix keys of the split,
 // plus the tiles of the draft keys its rows can see for split 0, shifted
-// right by bucket_shift), longest first, with a counting sort over
-// kWorkBuckets buckets in LDS.  Ties keep roughly the order of the entry
+// right by bucket_shift, at most kWorkBuckets - 2), longest first, with a
+// counting sort over kWorkBuckets buckets in LDS.  Ties keep roughly the order of the entry
 // index (chunk fastest), so the chunks of one (request, split) stay side by
 // side.  One workgroup of 1024 threads.
 constexpr int kWorkBuckets = 256;
+// Entries whose bucket the first pass keeps in LDS for the second (larger
+// lists recompute it).
+constexpr int kWorkCache = 16384;
 
 __global__ void __launch_bounds__(1024) worklist_kernel(const WorkListArgs a) {
   __shared__ int hist[kWorkBuckets];
   __shared__ int cur[kWorkBuckets];
+  __shared__ int wsum[4];
+  __shared__ uint8_t bucket_of[kWorkCache];
   const int tid = (int)threadIdx.x;
-  for (int b = tid; b < kWorkBuckets; b += 1024) hist[b] = 0;
+  if (tid < kWorkBuckets) hist[tid] = 0;
   __syncthreads();
   const int64_t n = (int64_t)a.batch_size * a.n_splits * a.n_chunks;
-  // Tiles of entry c, or -1 when the row-split kernel has nothing to do.
+  // Bucket of entry c, or -1 when the row-split kernel has nothing to do.
   auto work = [&](int64_t c) -> int {
     const int chunk = (int)(c % a.n_chunks);
     const int64_t rs = c / a.n_chunks;
@@ -153,24 +158,38 @@ __global__ void __launch_bounds__(1024) worklist_kernel(const WorkListArgs a) {
       tiles += (last / a.group + 1 + 31) / 32;
     }
     tiles >>= a.bucket_shift;
-    return (int)(tiles < kWorkBuckets - 1 ? tiles : kWorkBuckets - 1);
+    return (int)(tiles < kWorkBuckets - 2 ? tiles : kWorkBuckets - 2);
   };
   for (int64_t c = tid; c < n; c += 1024) {
     const int w = work(c);
+    if (c < kWorkCache) bucket_of[c] = (uint8_t)(w < 0 ? kWorkBuckets - 1 : w);
     if (w >= 0) atomicAdd(&hist[w], 1);
   }
   __syncthreads();
-  if (tid == 0) {
-    int acc = 0;
-    for (int b = kWorkBuckets - 1; b >= 0; --b) {
-      cur[b] = acc;
-      acc += hist[b];
+  // Exclusive prefix sum over the buckets from the longest down: thread i
+  // holds bucket kWorkBuckets - 1 - i; a scan within each wave, then the
+  // wave totals.
+  int v = 0, incl = 0;
+  if (tid < kWorkBuckets) {
+    v = hist[kWorkBuckets - 1 - tid];
+    incl = v;
+#pragma unroll
+    for (int d = 1; d < 64; d <<= 1) {
+      const int y = __shfl_up(incl, d, 64);
+      if ((tid & 63) >= d) incl += y;
     }
-    *a.count = acc;
+    if ((tid & 63) == 63) wsum[tid >> 6] = incl;
+  }
+  __syncthreads();
+  if (tid < kWorkBuckets) {
+    int before = 0;
+    for (int q = 0; q < (tid >> 6); ++q) before += wsum[q];
+    cur[kWorkBuckets - 1 - tid] = before + incl - v;
+    if (tid == kWorkBuckets - 1) *a.count = before + incl;
   }
   __syncthreads();
   for (int64_t c = tid; c < n; c += 1024) {
-    const int w = work(c);
+    const int w = c < kWorkCache ? (bucket_of[c] == kWorkBuckets - 1 ? -1 : (int)bucket_of[c]) : work(c);
     if (w >= 0) a.list[atomicAdd(&cur[w], 1)] = (int)c;
   }
 }
