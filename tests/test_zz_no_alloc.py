@@ -52,9 +52,13 @@ def _check_against_workspace_call(B, wl, out_dtype):
 
 def test_noalloc_matches_workspace_entry_point(B):
     # the GQA verify shapes with a 5000-token prefix (split over workgroups),
-    # then a smaller split case on the same GPU
+    # a row-split launch (960 rows per kv head; split prefix and its work list
+    # in the built-in workspace), then a smaller split case on the same GPU
     _check_against_workspace_call(
         B, W.build_workload("long_gqa", [5000] * 8, [[3] * 4] * 8, 32, 8, 128, 16, seed=93), torch.float32)
+    _check_against_workspace_call(
+        B, W.build_workload("rows_noalloc", [6000, 1500], [[40] * 3, [20] * 2], 16, 2, 128, 16, seed=94),
+        torch.bfloat16)
     _check_against_workspace_call(
         B, W.build_workload("small_split", [2200, 600], [[3, 2], [4]], 8, 2, 128, 16, seed=91), torch.bfloat16)
     assert B.cascade_device_error(clear=True) == 0
