@@ -11,7 +11,9 @@ namespace casc {
 // merge_state: for each (row, head), with natural-log LSEs,
 //   LSE = ln(e^LSE_A + e^LSE_B), o = e^(LSE_A - LSE) o_A + e^(LSE_B - LSE) o_B.
 // Evaluated in base 2 after scaling the LSEs by log2(e), the larger one
-// factored out.  One thread per 4 channels of one (row, head).
+// factored out.  A side whose weight is 0 (LSE = -inf, an empty pass, or
+// negligible next to the other) contributes exactly 0 and is not read.  One
+// thread per 4 channels of one (row, head).
 __global__ void __launch_bounds__(256) merge_state_kernel(const MergeArgs a) {
   const int d4 = a.head_dim >> 2;
   const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
@@ -27,8 +29,9 @@ __global__ void __launch_bounds__(256) merge_state_kernel(const MergeArgs a) {
     const float l2 = mx + fast_log2(fast_exp2(la - mx) + fast_exp2(lb - mx));
     const float wa = fast_exp2(la - l2);
     const float wb = fast_exp2(lb - l2);
-    const f32x4 oa = *reinterpret_cast<const f32x4*>(a.o_a + r * a.head_dim + c);
-    const f32x4 ob = *reinterpret_cast<const f32x4*>(a.o_b + r * a.head_dim + c);
+    f32x4 oa = {0.f, 0.f, 0.f, 0.f}, ob = {0.f, 0.f, 0.f, 0.f};
+    if (wa != 0.f) oa = *reinterpret_cast<const f32x4*>(a.o_a + r * a.head_dim + c);
+    if (wb != 0.f) ob = *reinterpret_cast<const f32x4*>(a.o_b + r * a.head_dim + c);
 #pragma unroll
     for (int i = 0; i < 4; ++i) out[i] = (wa == 0.f ? 0.f : wa * oa[i]) + (wb == 0.f ? 0.f : wb * ob[i]);
     lse = l2 * kLn2;
@@ -48,8 +51,9 @@ __global__ void __launch_bounds__(256) merge_state_kernel(const MergeArgs a) {
 // keys has partials for splits 0 .. ceil(L / split_len) - 1 (the fused
 // verify pass also for split 0 when L = 0: it holds the drafts); no partial
 // means o = 0, LSE = -inf.  Rows of a request with a single split are final
-// already (the attention kernels write them directly) and are skipped.  One thread per 4 channels of one (row, head):
-// every partial of that slice is loaded before any is combined.
+// already (the attention kernels write them directly) and are skipped.  One
+// thread per 4 channels of one (row, head): the splits' LSEs give the max,
+// then the splits with nonzero weight are read and added in split order.
 __global__ void __launch_bounds__(256) split_merge_kernel(const SplitMergeArgs a) {
   const int d4 = a.head_dim >> 2;
   const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
@@ -78,9 +82,9 @@ __global__ void __launch_bounds__(256) split_merge_kernel(const SplitMergeArgs a
   float tot = 0.f;
   for (int sp = 0; sp < nsp; ++sp) {
     const float wgt = fast_exp2(a.ws_lse[sp * plane + rh] - ms);
-    const f32x4 x = *reinterpret_cast<const f32x4*>(a.ws_o + (sp * plane + rh) * a.head_dim + c);
     tot += wgt;
-    if (wgt != 0.f) acc += wgt * x;
+    // A split with weight 0 (no keys, or negligible) is not read.
+    if (wgt != 0.f) acc += wgt * *reinterpret_cast<const f32x4*>(a.ws_o + (sp * plane + rh) * a.head_dim + c);
   }
   const float inv = tot > 0.f ? 1.f / tot : 0.f;
   acc *= inv;
