@@ -13,14 +13,16 @@
 // every wave keeps its own rows' complete online softmax state and no state
 // is merged across waves.  The waves of a workgroup go through the same
 // 32-key tiles in lock step:
-//   * each thread loads 512 / (64 kRowWaves) 16-byte chunks of K and as many
-//     of V per tile (the workgroup's threads cover the 32 keys x 16 chunks of
-//     a tile; the 64 lanes of a wave read four whole 256-byte key rows of one
-//     page per chunk), DEPTH tiles ahead, into a ring of DEPTH register slots
-//     -- a handful of registers per tile, so many tiles are in flight;
-//   * per step the workgroup writes the next tile into one of two LDS
-//     stages, computes the current tile out of the other, and meets at one
-//     barrier;
+//   * bf16 pools: the tiles are copied from HBM straight into LDS (buffer
+//     loads into LDS, 16 bytes a lane; the 64 lanes of a wave fill four whole
+//     256-byte key rows of one page per copy) into four stages, three tiles
+//     ahead; per step each wave waits for its own copies of the current tile,
+//     the workgroup meets at one barrier, the stage the previous tile left
+//     gets the tile three ahead, and the current tile is computed.  No
+//     register holds a tile in flight;
+//   * FP8 pools: each thread loads its 8-byte code chunks DEPTH tiles ahead
+//     into a ring of registers, and per step widens the next tile into one of
+//     two LDS stages while the current one is computed out of the other;
 //   * a wave reads K back as MFMA A-fragments (S^T = K Q^T with
 //     v_mfma_f32_16x16x32_bf16, its rows' Q as B-fragments in registers),
 //     updates its rows' base-2 online softmax, and reads V back transposed
@@ -40,6 +42,19 @@
 
 namespace casc {
 
+// A 16-byte-per-lane copy global -> LDS: lane i's 16 bytes at `voff` in the
+// buffer land at LDS byte `lds` + 16 i.  Written out so that the compiler
+// does not order every later LDS read behind every copy in flight (it cannot
+// tell the stages apart); the key loop waits for the copies itself.  No
+// register is written.
+__device__ __forceinline__ void lds_copy16(__amdgpu_buffer_rsrc_t r, uint32_t lds, int voff) {
+  asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds" ::"s"(lds), "v"(voff), "s"(r)
+               : "memory", "m0");
+}
+__device__ __forceinline__ uint32_t lds_addr(const uint16_t* p) {
+  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) uint16_t*)p;
+}
+
 // Mask kind of a key range, as a type for the key loop.
 template <int K>
 struct KeyKind {
@@ -50,15 +65,24 @@ template <int MODE, int DEPTH, int RBW, bool KV8>
 __global__ void __launch_bounds__(64 * kRowWaves) __attribute__((amdgpu_waves_per_eu(2, 2)))
 rows_kernel(const AttnArgs a) {
   static_assert(MODE == kModePrefix || MODE == kModeVerify || MODE == kModeDraft, "pass A, verify, pass B");
-  static_assert(DEPTH % 2 == 0, "the two LDS stages alternate within the unrolled ring");
+  static_assert(DEPTH % 2 == 0, "the two LDS stages of the register ring alternate within the unrolled ring");
   static_assert(kRowsPerItem == kRowWaves * 16 * RBW, "RBW 16-row blocks per wave");
   constexpr int ROWS_W = 16 * RBW;  // query rows per wave
   constexpr int D = 128;
   constexpr int KS = D / 32;   // k-steps of the Q K^T contraction
   constexpr int DB = D / 16;   // 16-channel blocks of the head dim
   constexpr int CPR = D / 8;   // 8-channel chunks per key row (16)
-  constexpr int RS = D + 16;   // LDS row stride: rows 8 banks apart
-  constexpr int STAGE = 2 * 32 * RS;  // bf16 elements of one stage: K tile, then V tile
+  // Stage layout: the K tile's 32 rows, then the V tile's, 256 bytes each
+  // with no padding.  The 16-byte chunks of a row are XOR-swizzled by the
+  // key -- K: chunk c of key k at slot c ^ (k & 15); V: at slot c ^ 2(k & 3) --
+  // so that a K-fragment read (one chunk of 16 keys) and a transposed V read
+  // (two chunks of 4 keys) each touch every bank once.
+  constexpr int ROWE = D;             // bf16 elements per LDS row
+  constexpr int STAGE = 64 * ROWE;    // bf16 elements of one stage: K tile, then V tile
+  // bf16 pools are copied global -> LDS directly (buffer loads into LDS):
+  // four stages, three tiles in flight.  FP8 codes are widened in registers
+  // on the way (two stages, a register ring of DEPTH tiles).
+  constexpr bool kDma = !KV8;
   // Bytes per pool element; a chunk of 8 channels as loaded (16 bytes of
   // bf16, or 8 bytes of FP8 E4M3 codes widened to bf16 when staged).
   constexpr int EB = KV8 ? 1 : 2;
@@ -80,7 +104,13 @@ rows_kernel(const AttnArgs a) {
   constexpr int NBCAP = 128;   // branches of a request resolved in LDS
   constexpr int KEYCAP = 512;  // draft keys of a chunk resolved in LDS
 
-  __shared__ __attribute__((aligned(16))) uint16_t stg[2][STAGE];
+  // One LDS object per stage, so that the compiler can tell the stages apart
+  // when it orders reads of one stage against copies into another.
+  __shared__ __attribute__((aligned(16))) uint16_t stg0[STAGE];
+  __shared__ __attribute__((aligned(16))) uint16_t stg1[STAGE];
+  __shared__ __attribute__((aligned(16))) uint16_t stg2[kDma ? STAGE : 8];
+  __shared__ __attribute__((aligned(16))) uint16_t stg3[kDma ? STAGE : 8];
+  uint16_t* const stg[4] = {stg0, stg1, stg2, stg3};
   __shared__ int64_t t_doff[kTables ? KEYCAP : 1];
   __shared__ int t_bnd[kTables ? NBCAP + 1 : 1];
   __shared__ int t_dst[kTables ? NBCAP : 1];
@@ -299,6 +329,27 @@ rows_kernel(const AttnArgs a) {
       tl.v[q] = buf_load_chunk(half_rsrc(kv.v, h), lane_off, (Raw*)nullptr);
     }
   };
+  // bf16 pools: a tile copied straight into a stage.  Lane (g4, l16) of wave
+  // w fills slot l16 of key 4w + g4 of each 16-key half: K chunk
+  // l16 ^ (4w + g4) and V chunk l16 ^ 2 g4 (the swizzles, with k & 15 =
+  // 4w + g4 and k & 3 = g4); the 64 lanes' 16 bytes land side by side, four
+  // whole rows per copy.  Keys past the range read zeros through the
+  // descriptors; `front_zero` also zeroes the keys of tile 0 in front of
+  // `front` (an offset past every descriptor).
+  const int dma_off_k = prefix_lane_offset<EB>(kv, w * 4 + g4, head_off, l16 ^ (w * 4 + g4));
+  const int dma_off_v = prefix_lane_offset<EB>(kv, w * 4 + g4, head_off, l16 ^ (g4 << 1));
+  auto dma_tile = [&](int tile, const Pages& pg, uint16_t* st, bool front_zero) {
+#pragma unroll
+    for (int q = 0; q < CPT; ++q) {
+      const int first = p0 + tile * 32 + half_of(q) * 16;
+      const int nvalid = min(max(p1 - first, 0), 16);
+      const HalfSpan h = prefix_half_span(kv, pg.p[q], first, nvalid, tail_bytes);
+      const bool zero = front_zero && first + w * 4 + g4 < front;
+      const int row = half_of(q) * 16 + w * 4;
+      lds_copy16(half_rsrc(kv.k, h), lds_addr(st + row * ROWE), zero ? 0x7ffffff0 : dma_off_k);
+      lds_copy16(half_rsrc(kv.v, h), lds_addr(st + (32 + row) * ROWE), zero ? 0x7ffffff0 : dma_off_v);
+    }
+  };
   // Thread tid's chunks of a tile into a stage (chunk q zeroed where bit q of
   // `keep` is clear).
   auto skey = [&](int q) { return (tid + q * NT) >> 4; };
@@ -312,20 +363,32 @@ rows_kernel(const AttnArgs a) {
         k = u32x4{0u, 0u, 0u, 0u};
         v = u32x4{0u, 0u, 0u, 0u};
       }
-      *reinterpret_cast<u32x4*>(st + skey(q) * RS + sch * 8) = k;
-      *reinterpret_cast<u32x4*>(st + 32 * RS + skey(q) * RS + sch * 8) = v;
+      const int key = skey(q);
+      *reinterpret_cast<u32x4*>(st + key * ROWE + ((sch ^ (key & 15)) << 3)) = k;
+      *reinterpret_cast<u32x4*>(st + (32 + key) * ROWE + ((sch ^ ((key & 3) << 1)) << 3)) = v;
     }
   };
 
   // DEPTH tiles requested before the first one is staged; `pgn` holds the
   // pages of the next tile to be requested.
-  Tile ring[DEPTH];
+  Tile ring[kDma ? 1 : DEPTH];
   Pages pgn = page_of(0);
+  auto request_first = [&]() {
+    if constexpr (kDma) {
 #pragma unroll
-  for (int k = 0; k < DEPTH; ++k) {
-    load_tile(k, pgn, ring[k]);
-    pgn = page_of(k + 1);
-  }
+      for (int k = 0; k < 3; ++k) {
+        dma_tile(k, pgn, stg[k], k == 0);
+        pgn = page_of(k + 1);
+      }
+    } else {
+#pragma unroll
+      for (int k = 0; k < DEPTH; ++k) {
+        load_tile(k, pgn, ring[k]);
+        pgn = page_of(k + 1);
+      }
+    }
+  };
+  request_first();
 
   // ---- tree tables (fused verify split 0, pass B not in slot mode) ---------
   const bool drafts = (kVerify && split == 0 && !slot_mode) || (kDraft && !slot_mode);
@@ -408,12 +471,15 @@ rows_kernel(const AttnArgs a) {
   }
 
   auto kfrag = [&](const uint16_t* st, int kb, int ks) -> bf16x8 {
-    return *reinterpret_cast<const bf16x8*>(st + (kb * 16 + l16) * RS + (ks * 4 + g4) * 8);
+    const int key = kb * 16 + l16;
+    return *reinterpret_cast<const bf16x8*>(st + key * ROWE + (((ks * 4 + g4) ^ (key & 15)) << 3));
   };
   auto vt_frag = [&](const uint16_t* st, int db) -> bf16x8 {
-    const uint16_t* vb = st + 32 * RS + (4 * g4 + (l16 >> 2)) * RS + db * 16 + 4 * (l16 & 3);
+    const int row = 4 * g4 + (l16 >> 2);
+    const int c = 2 * db + ((l16 & 3) >> 1);
+    const uint16_t* vb = st + (32 + row) * ROWE + ((c ^ ((row & 3) << 1)) << 3) + 4 * (l16 & 1);
     const i16x4 lo = lds_read_tr16(vb);
-    const i16x4 hi = lds_read_tr16(vb + 16 * RS);
+    const i16x4 hi = lds_read_tr16(vb + 16 * ROWE);
     return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
   };
   // The lane's row's draft visibility (fused verify): request token, start of
@@ -545,6 +611,37 @@ rows_kernel(const AttnArgs a) {
   // then carries the same ring state as the entry, and each stage waits for
   // its own slot only.  Steps past the last tile stage zeros and compute
   // nothing.
+  // bf16: step t waits for this wave's copies of tile t (at most the two
+  // later tiles' eight copies still in flight), meets the other waves at the
+  // barrier, copies tile t+3 into the stage tile t-1 left, and computes tile
+  // t.  Whole rings of four steps; steps past the range copy nothing useful
+  // (zeros) and compute nothing.  The loop ends with every copy landed.
+  auto key_loop_dma = [&](auto kind_tag) {
+    constexpr int KIND = decltype(kind_tag)::value;
+    constexpr int kWait8 = 8 | (7 << 4) | (15 << 8);  // s_waitcnt vmcnt(8)
+    constexpr int kWait0 = 0 | (7 << 4) | (15 << 8);  // s_waitcnt vmcnt(0)
+    // Every load in flight lands first (the query rows and tables, and the
+    // first three tiles): the compiler, which cannot count the copies, then
+    // has no load of its own left to wait for inside the loop.
+    __builtin_amdgcn_s_waitcnt(kWait0);
+    for (int t0 = 0; t0 < nt; t0 += 4) {
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        const int t = t0 + k;
+        __builtin_amdgcn_s_waitcnt(kWait8);
+        __syncthreads();
+        dma_tile(t + 3, pgn, stg[(k + 3) & 3], false);
+        pgn = page_of(t + 4);
+        if (wave_rows && t < nt) {
+          const int tb = p0 + t * 32 - kshift;
+          const bool open = KIND == 1 && slot_mode && !tree && tb >= 0 && tb + 32 <= wave_tok + 1;
+          compute(stg[k], tb, open ? tb + 32 : kend, open ? 0 : KIND);
+        }
+      }
+    }
+    __builtin_amdgcn_s_waitcnt(kWait0);
+    __syncthreads();
+  };
   auto key_loop = [&](auto kind_tag) {
     constexpr int KIND = decltype(kind_tag)::value;
     {
@@ -575,7 +672,11 @@ rows_kernel(const AttnArgs a) {
       }
     }
   };
-  key_loop(KeyKind<kDraft ? 1 : 0>{});
+  if constexpr (kDma) {
+    key_loop_dma(KeyKind<kDraft ? 1 : 0>{});
+  } else {
+    key_loop(KeyKind<kDraft ? 1 : 0>{});
+  }
 
   // ---- fused verify, slot mode: the branch's draft keys as a second range ---
   if constexpr (kVerify) {
@@ -589,12 +690,12 @@ rows_kernel(const AttnArgs a) {
       kend = dhi;
       front = ds0;
       pgn = page_of(0);
-#pragma unroll
-      for (int j = 0; j < DEPTH; ++j) {
-        load_tile(j, pgn, ring[j]);
-        pgn = page_of(j + 1);
+      request_first();
+      if constexpr (kDma) {
+        key_loop_dma(KeyKind<1>{});
+      } else {
+        key_loop(KeyKind<1>{});
       }
-      key_loop(KeyKind<1>{});
     }
   }
 
