@@ -277,6 +277,13 @@ casc::AttnArgs make_args(const cascade_query* q, const cascade_paged_kv* kv, con
 // (64 requests, 48 to 512 rows per kv head, prefixes of 512 to 32768 keys)
 // 0.65 ms against 0.91 ms on the pair kernel in 48-row chunks.
 constexpr int64_t kRowKernelMinRows = 16 * kMaxRowBlocks + 1;
+// Rows per (request, kv head) from which the row-split kernel (bf16 pools)
+// runs three workgroups per CU with three copy stages instead of two with
+// four: many full 128-row items (prefix hit, fused: 2.52 -> 2.24 ms at
+// h = 0, 1.87 -> 1.69 ms at h = 0.5), while batches of short items that
+// stream from HBM (the ragged batch, at most 512 rows) keep the deeper copy
+// pipeline (0.59 against 0.60 ms).
+constexpr int64_t kRowThreeWaveRows = 1024;
 
 // Plan of the per-request launches (pass A, pass B, verify).  At head_dim 128,
 // pass A and the fused verify pass of requests with at most 16 * kMaxRowBlocks
@@ -457,8 +464,11 @@ hipError_t launch_row_modes(int mode, const cascade_paged_kv* kv,
     grid = (int64_t)t->batch_size * a.n_splits * a.n_chunks * kv->num_kv_heads;
   }
   if (grid <= 0) return hipSuccess;
+  // Launches of full items (at least kRowThreeWaveRows rows per pair: a
+  // prefix-hit suffix prefill) run three workgroups per CU.
+  const bool three_wave = (int64_t)t->max_request_rows * p.group >= kRowThreeWaveRows;
   return kv_fp8(kv) ? casc::launch_rows_d128_fp8(mode, a, (int)grid, s, e0, e1)
-                    : casc::launch_rows_d128(mode, a, (int)grid, s, e0, e1);
+                    : casc::launch_rows_d128(mode, three_wave, a, (int)grid, s, e0, e1);
 }
 
 // Kernel timing of cascade_verify_attn (per thread; see the header).

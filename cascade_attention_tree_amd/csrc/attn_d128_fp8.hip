@@ -12,7 +12,7 @@ hipError_t read_error_d128_fp8(int* v, int clear) { return read_error_word(v, cl
 
 hipError_t launch_rows_d128_fp8(int mode, const AttnArgs& a, int grid, hipStream_t s, hipEvent_t e0,
                                 hipEvent_t e1) {
-  return launch_rows<true>(mode, a, grid, s, e0, e1);
+  return launch_rows<true>(mode, false, a, grid, s, e0, e1);
 }
 
 }  // namespace casc

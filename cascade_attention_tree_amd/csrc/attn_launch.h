@@ -41,17 +41,28 @@ constexpr int kRowDepth = 4;
 // 16-row blocks per wave: each K and V fragment read out of LDS serves them all.
 constexpr int kRowBlocks = 2;
 
-template <bool KV8>
-static inline hipError_t launch_rows(int mode, const AttnArgs& a, int grid, hipStream_t s, hipEvent_t e0,
-                                     hipEvent_t e1) {
+template <bool KV8, int NS>
+static inline hipError_t launch_rows_ns(int mode, const AttnArgs& a, int grid, hipStream_t s, hipEvent_t e0,
+                                        hipEvent_t e1) {
   const dim3 g(grid), b(64 * kRowWaves);
   switch (mode) {
-    case kModePrefix: go(rows_kernel<kModePrefix, kRowDepth, kRowBlocks, KV8>, g, b, s, e0, e1, a); break;
-    case kModeVerify: go(rows_kernel<kModeVerify, kRowDepth, kRowBlocks, KV8>, g, b, s, e0, e1, a); break;
-    case kModeDraft: go(rows_kernel<kModeDraft, kRowDepth, kRowBlocks, KV8>, g, b, s, e0, e1, a); break;
+    case kModePrefix: go(rows_kernel<kModePrefix, kRowDepth, kRowBlocks, KV8, NS>, g, b, s, e0, e1, a); break;
+    case kModeVerify: go(rows_kernel<kModeVerify, kRowDepth, kRowBlocks, KV8, NS>, g, b, s, e0, e1, a); break;
+    case kModeDraft: go(rows_kernel<kModeDraft, kRowDepth, kRowBlocks, KV8, NS>, g, b, s, e0, e1, a); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
+}
+
+// three_wave: bf16 pools, three workgroups per CU (three copy stages);
+// otherwise two (four stages, or the FP8 register ring).
+template <bool KV8>
+static inline hipError_t launch_rows(int mode, bool three_wave, const AttnArgs& a, int grid, hipStream_t s,
+                                     hipEvent_t e0, hipEvent_t e1) {
+  if constexpr (!KV8) {
+    if (three_wave) return launch_rows_ns<KV8, 3>(mode, a, grid, s, e0, e1);
+  }
+  return launch_rows_ns<KV8, 4>(mode, a, grid, s, e0, e1);
 }
 
 // Pair kernel (head_dim 128): pass A or the fused verify pass over chunks of

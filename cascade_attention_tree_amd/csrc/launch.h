@@ -22,9 +22,10 @@ hipError_t launch_attn_d128_fp8(int mode, int rb, const AttnArgs& a, int grid, h
 
 // Row-split kernel for head_dim 128 (bf16 / FP8 pools), modes kModePrefix,
 // kModeVerify and kModeDraft: work items of at most kRowsPerItem query rows
-// (a.n_chunks counts chunks of that size).
-hipError_t launch_rows_d128(int mode, const AttnArgs& a, int grid, hipStream_t s, hipEvent_t ev_start,
-                            hipEvent_t ev_stop);
+// (a.n_chunks counts chunks of that size).  three_wave (bf16): three
+// workgroups per CU instead of two.
+hipError_t launch_rows_d128(int mode, bool three_wave, const AttnArgs& a, int grid, hipStream_t s,
+                            hipEvent_t ev_start, hipEvent_t ev_stop);
 hipError_t launch_rows_d128_fp8(int mode, const AttnArgs& a, int grid, hipStream_t s, hipEvent_t ev_start,
                                 hipEvent_t ev_stop);
 

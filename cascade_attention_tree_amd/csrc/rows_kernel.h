@@ -15,10 +15,10 @@
 // 32-key tiles in lock step:
 //   * bf16 pools: the tiles are copied from HBM straight into LDS (buffer
 //     loads into LDS, 16 bytes a lane; the 64 lanes of a wave fill four whole
-//     256-byte key rows of one page per copy) into four stages, three tiles
+//     256-byte key rows of one page per copy) into NS stages, NS - 1 tiles
 //     ahead; per step each wave waits for its own copies of the current tile,
 //     the workgroup meets at one barrier, the stage the previous tile left
-//     gets the tile three ahead, and the current tile is computed.  No
+//     gets the tile NS - 1 ahead, and the current tile is computed.  No
 //     register holds a tile in flight;
 //   * FP8 pools: each thread loads its 8-byte code chunks DEPTH tiles ahead
 //     into a ring of registers, and per step widens the next tile into one of
@@ -61,8 +61,15 @@ struct KeyKind {
   static constexpr int value = K;
 };
 
-template <int MODE, int DEPTH, int RBW, bool KV8>
-__global__ void __launch_bounds__(64 * kRowWaves) __attribute__((amdgpu_waves_per_eu(2, 2)))
+// NS: LDS stages of the bf16 copies (NS - 1 tiles in flight).  NS = 4: two
+// workgroups per CU (64 KB of stages each).  NS = 3: three workgroups per CU
+// -- 48 KB of stages, a 256-key draft table and at most 168 VGPRs (a few
+// values spill), so that every SIMD runs three waves: for launches with many
+// full 128-row items (a prefix-hit suffix prefill: 10-12 % faster), while
+// batches of short HBM-bound items keep the deeper copy pipeline.  FP8 pools
+// run the register ring at two workgroups per CU.
+template <int MODE, int DEPTH, int RBW, bool KV8, int NS>
+__global__ void __launch_bounds__(64 * kRowWaves) __attribute__((amdgpu_waves_per_eu(NS == 3 ? 3 : 2, NS == 3 ? 3 : 2)))
 rows_kernel(const AttnArgs a) {
   static_assert(MODE == kModePrefix || MODE == kModeVerify || MODE == kModeDraft, "pass A, verify, pass B");
   static_assert(DEPTH % 2 == 0, "the two LDS stages of the register ring alternate within the unrolled ring");
@@ -80,9 +87,11 @@ rows_kernel(const AttnArgs a) {
   constexpr int ROWE = D;             // bf16 elements per LDS row
   constexpr int STAGE = 64 * ROWE;    // bf16 elements of one stage: K tile, then V tile
   // bf16 pools are copied global -> LDS directly (buffer loads into LDS):
-  // four stages, three tiles in flight.  FP8 codes are widened in registers
+  // NS stages, NS - 1 tiles in flight.  FP8 codes are widened in registers
   // on the way (two stages, a register ring of DEPTH tiles).
   constexpr bool kDma = !KV8;
+  static_assert(NS == 3 || NS == 4, "three or four copy stages");
+  static_assert(!KV8 || NS == 4, "FP8 pools run the register ring");
   // Bytes per pool element; a chunk of 8 channels as loaded (16 bytes of
   // bf16, or 8 bytes of FP8 E4M3 codes widened to bf16 when staged).
   constexpr int EB = KV8 ? 1 : 2;
@@ -102,14 +111,14 @@ rows_kernel(const AttnArgs a) {
   constexpr bool kDraft = MODE == kModeDraft;
   constexpr bool kTables = kVerify || kDraft;
   constexpr int NBCAP = 128;   // branches of a request resolved in LDS
-  constexpr int KEYCAP = 512;  // draft keys of a chunk resolved in LDS
+  constexpr int KEYCAP = NS == 3 ? 256 : 512;  // draft keys of a chunk resolved in LDS
 
   // One LDS object per stage, so that the compiler can tell the stages apart
   // when it orders reads of one stage against copies into another.
   __shared__ __attribute__((aligned(16))) uint16_t stg0[STAGE];
   __shared__ __attribute__((aligned(16))) uint16_t stg1[STAGE];
   __shared__ __attribute__((aligned(16))) uint16_t stg2[kDma ? STAGE : 8];
-  __shared__ __attribute__((aligned(16))) uint16_t stg3[kDma ? STAGE : 8];
+  __shared__ __attribute__((aligned(16))) uint16_t stg3[kDma && NS > 3 ? STAGE : 8];
   uint16_t* const stg[4] = {stg0, stg1, stg2, stg3};
   __shared__ int64_t t_doff[kTables ? KEYCAP : 1];
   __shared__ int t_bnd[kTables ? NBCAP + 1 : 1];
@@ -376,7 +385,7 @@ rows_kernel(const AttnArgs a) {
   auto request_first = [&]() {
     if constexpr (kDma) {
 #pragma unroll
-      for (int k = 0; k < 3; ++k) {
+      for (int k = 0; k < NS - 1; ++k) {
         dma_tile(k, pgn, stg[k], k == 0);
         pgn = page_of(k + 1);
       }
@@ -394,7 +403,11 @@ rows_kernel(const AttnArgs a) {
   const bool drafts = (kVerify && split == 0 && !slot_mode) || (kDraft && !slot_mode);
   const bool lds_bnd = nb <= NBCAP;
   int dlo = 0;
-  Tile dt;  // the first draft tile, requested after the tables
+  // The first draft tile: requested right after the tables at two
+  // workgroups per CU; after the key loop at three (no registers held
+  // across the loop).
+  constexpr bool kEarlyDraft = NS == 4;
+  Tile dt;
   int dkeep = 0;
   auto branch_at = [&](int x) -> int {  // local branch of request token x
     if (lds_bnd) {
@@ -455,7 +468,7 @@ rows_kernel(const AttnArgs a) {
         t_doff[t] = draft_slot_offset(kv, a.draft_page_table + (int64_t)(jb + jl) * dstride, dstride, slot);
       }
       __syncthreads();
-      load_draft(dlo, dt, dkeep);
+      if constexpr (kEarlyDraft) load_draft(dlo, dt, dkeep);
     }
   }
 
@@ -611,27 +624,28 @@ rows_kernel(const AttnArgs a) {
   // then carries the same ring state as the entry, and each stage waits for
   // its own slot only.  Steps past the last tile stage zeros and compute
   // nothing.
-  // bf16: step t waits for this wave's copies of tile t (at most the two
-  // later tiles' eight copies still in flight), meets the other waves at the
-  // barrier, copies tile t+3 into the stage tile t-1 left, and computes tile
-  // t.  Whole rings of four steps; steps past the range copy nothing useful
-  // (zeros) and compute nothing.  The loop ends with every copy landed.
+  // bf16: step t waits for this wave's copies of tile t (at most the NS - 2
+  // later tiles' four copies each still in flight), meets the other waves at
+  // the barrier, copies tile t+NS-1 into the stage tile t-1 left, and
+  // computes tile t.  Whole rings of NS steps; steps past the range copy
+  // nothing useful (zeros) and compute nothing.  The loop ends with every
+  // copy landed.
   auto key_loop_dma = [&](auto kind_tag) {
     constexpr int KIND = decltype(kind_tag)::value;
-    constexpr int kWait8 = 8 | (7 << 4) | (15 << 8);  // s_waitcnt vmcnt(8)
+    constexpr int kWaitTile = 4 * (NS - 2) | (7 << 4) | (15 << 8);  // s_waitcnt vmcnt(4 (NS - 2))
     constexpr int kWait0 = 0 | (7 << 4) | (15 << 8);  // s_waitcnt vmcnt(0)
     // Every load in flight lands first (the query rows and tables, and the
-    // first three tiles): the compiler, which cannot count the copies, then
+    // first NS - 1 tiles): the compiler, which cannot count the copies, then
     // has no load of its own left to wait for inside the loop.
     __builtin_amdgcn_s_waitcnt(kWait0);
-    for (int t0 = 0; t0 < nt; t0 += 4) {
+    for (int t0 = 0; t0 < nt; t0 += NS) {
 #pragma unroll
-      for (int k = 0; k < 4; ++k) {
+      for (int k = 0; k < NS; ++k) {
         const int t = t0 + k;
-        __builtin_amdgcn_s_waitcnt(kWait8);
+        __builtin_amdgcn_s_waitcnt(kWaitTile);
         __syncthreads();
-        dma_tile(t + 3, pgn, stg[(k + 3) & 3], false);
-        pgn = page_of(t + 4);
+        dma_tile(t + NS - 1, pgn, stg[(k + NS - 1) % NS], false);
+        pgn = page_of(t + NS);
         if (wave_rows && t < nt) {
           const int tb = p0 + t * 32 - kshift;
           const bool open = KIND == 1 && slot_mode && !tree && tb >= 0 && tb + 32 <= wave_tok + 1;
@@ -709,7 +723,7 @@ rows_kernel(const AttnArgs a) {
           if (tree) ranc[rb] = a.draft_mask[(int64_t)(tok0 + rtok[rb]) * a.draft_mask_words];
         }
       for (int base = dlo; base < dhi; base += 32) {
-        if (base != dlo) load_draft(base, dt, dkeep);
+        if (!kEarlyDraft || base != dlo) load_draft(base, dt, dkeep);
         stage(dt, dkeep, stg[0]);
         __syncthreads();
         if (wave_rows) compute(stg[0], base, dhi, 1);

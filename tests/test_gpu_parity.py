@@ -130,6 +130,14 @@ def small_cases():
         # (1200 rows per kv head; 5-word masks), with a split prefix.
         "rows_wide_tree": lambda: W.attach_random_trees(
             W.build_workload("rows_wide_tree", [4500], [[300]], 8, 2, 128, 16, seed=67), 68),
+        # Row-split launches whose chunks see more draft keys than the LDS
+        # table of draft-key offsets holds (256 at three workgroups per CU,
+        # 512 at two): two branches per request, so no chunk streams its
+        # drafts; the keys past the table resolve through the block table.
+        "rows_long_branch": lambda: W.build_workload("rows_long_branch", [700], [[300, 10]], 16, 2, 128, 16,
+                                                     seed=72),
+        "rows_long_branch_g1": lambda: W.build_workload("rows_long_branch_g1", [300], [[600, 10]], 2, 2, 128, 16,
+                                                        seed=73),
         # A 600-token suffix (one branch continuing its prefix pages) at d = 64,
         # which the key-split kernel runs: row chunks near the end of the
         # suffix see more than 512 draft keys, past the LDS table of draft-key
