@@ -289,11 +289,11 @@ constexpr int64_t kRowThreeWaveRows = 1024;
 // pass A and the fused verify pass of requests with at most 16 * kMaxRowBlocks
 // rows per kv head run on the pair kernel (chunks of up to kPairRows rows,
 // two workgroups per CU, the chunks of a (request, kv head) sharing its
-// prefix stream through one L2) -- except bf16 pools whose (request, kv head)
+// prefix stream through one L2) -- except launches whose (request, kv head)
 // pairs already fill the device with one chunk each: there the key-split
-// kernel, one workgroup per CU holding all rows, measured faster (60.6 against
-// 64.5 us at 32 requests x 8 kv heads x 80 rows), while the pair kernel is
-// faster over FP8 pools.  With too few (request, kv head) pairs to fill the
+// kernel, one workgroup per CU holding all rows, measured faster (32 requests
+// x 8 kv heads x 80 rows: 60.6 against 64.5 us over bf16 pools, 53.3 against
+// 54.7 us over FP8 pools).  With too few (request, kv head) pairs to fill the
 // device, a request's rows are cut in more chunks before its prefix is split;
 // when even one 16-row block per chunk leaves at most a workgroup per CU (the
 // GQA configuration: 8 requests x 8 kv heads x 48 rows, 192 chunks), the
@@ -313,7 +313,7 @@ Plan plan_request(const cascade_query* q, const cascade_paged_kv* kv, const casc
     p.n_chunks = (int)cdiv(rows, 16);
   }
   p.items = pairs * p.n_chunks;
-  const bool one_chunk_fills = !kv_fp8(kv) && rows <= 16 * kMaxRowBlocks && pairs >= kTargetItems;
+  const bool one_chunk_fills = rows <= 16 * kMaxRowBlocks && pairs >= kTargetItems;
   p.pair = !thin && kv->head_dim == 128 && rows > 0 && rows < kRowKernelMinRows && !one_chunk_fills;
   p.rows_kernel = kv->head_dim == 128 && rows >= kRowKernelMinRows;
   if (p.rows_kernel) {

@@ -508,9 +508,9 @@ rows_kernel(const AttnArgs a) {
     for (int rb = 0; rb < RBW; ++rb)
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb) s[rb][kb] = f32x4{0.f, 0.f, 0.f, 0.f};
-    // The matrix phases run at raised wave priority: when the two waves of
-    // a SIMD (independent workgroups) both have work, the one with MFMAs to
-    // issue goes first and the other's softmax fills in behind it.
+    // The matrix phases run at raised wave priority: when the waves of a
+    // SIMD (independent workgroups) both have work, the one with MFMAs to
+    // issue goes first and the others' softmax fills in behind it.
     __builtin_amdgcn_s_setprio(1);
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
@@ -520,12 +520,19 @@ rows_kernel(const AttnArgs a) {
 #pragma unroll
         for (int rb = 0; rb < RBW; ++rb) s[rb][kb] = mfma16(kf, qf[rb][ks], s[rb][kb]);
       }
-#pragma unroll
-    for (int rb = 0; rb < RBW; ++rb)
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb) asm volatile("" : "+v"(s[rb][kb]));
     __builtin_amdgcn_s_setprio(0);
+    // At two workgroups per CU (registers to spare) each row block's P.V
+    // follows its own softmax, the tile's V fragments read out of the stage
+    // beforehand, so that the first block's P.V runs while the second block's
+    // weights are formed (ragged batch: 0.56 against 0.59 ms).  At three, the
+    // P.V of both blocks follows both softmaxes (held V fragments would spill).
+    constexpr bool kPvPerBlock = NS == 4 && !KV8;
     bf16x8 pf[RBW];
+    bf16x8 vfr[kPvPerBlock ? DB : 1];
+    if constexpr (kPvPerBlock) {
+#pragma unroll
+      for (int db = 0; db < DB; ++db) vfr[db] = vt_frag(st, db);
+    }
 #pragma unroll
     for (int rb = 0; rb < RBW; ++rb) {
       // One uniform branch per tile picks the rule (tree masks or chains).
@@ -593,15 +600,21 @@ rows_kernel(const AttnArgs a) {
       const u32x4 pk = {pack_bf16x2(p[0], p[1]), pack_bf16x2(p[2], p[3]), pack_bf16x2(p[4], p[5]),
                         pack_bf16x2(p[6], p[7])};
       pf[rb] = __builtin_bit_cast(bf16x8, pk);
-    }
-    __builtin_amdgcn_s_setprio(1);
+      if constexpr (kPvPerBlock) {
 #pragma unroll
-    for (int db = 0; db < DB; ++db) {
-      const bf16x8 vf = vt_frag(st, db);
-#pragma unroll
-      for (int rb = 0; rb < RBW; ++rb) o[rb][db] = mfma16(vf, pf[rb], o[rb][db]);
+        for (int db = 0; db < DB; ++db) o[rb][db] = mfma16(vfr[db], pf[rb], o[rb][db]);
+      }
     }
-    __builtin_amdgcn_s_setprio(0);
+    if constexpr (!kPvPerBlock) {
+      __builtin_amdgcn_s_setprio(1);
+#pragma unroll
+      for (int db = 0; db < DB; ++db) {
+        const bf16x8 vf = vt_frag(st, db);
+#pragma unroll
+        for (int rb = 0; rb < RBW; ++rb) o[rb][db] = mfma16(vf, pf[rb], o[rb][db]);
+      }
+      __builtin_amdgcn_s_setprio(0);
+    }
   };
 
   // Request token of the wave's first row (its rows' tokens are not smaller).
