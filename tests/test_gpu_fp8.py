@@ -147,6 +147,32 @@ def test_fp8_headline_all_rows(B, layout):
     assert B.cascade_device_error(clear=True) == 0
 
 
+@pytest.mark.parametrize("values", ["bf16", "fp8"])
+def test_full_pairs_split_prefix_sampled(B, values):
+    """32 requests x 8 kv heads (one key-split workgroup per pair holds all 80
+    rows) with 4500-key prefixes, past the 4096 keys one split may hold: the
+    fused verify launch splits every prefix in two and merges the partial
+    states.  The first, the last and four random rows of every request
+    against the oracle (over the dequantised pools for FP8)."""
+    wl = W.build_workload("split_full_pairs", [4500] * 32, [[5] * 4] * 32, 32, 8, 128, 16, seed=81)
+    if values == "fp8":
+        wl = W.with_fp8_kv(wl)
+    note(f"full pairs, split prefix, {values}")
+    x = B.to_device(wl, layout="HND")
+    assert B.workspace_for(x) is not None
+    o, l = B.cascade_verify_attn(x, out_dtype=torch.bfloat16)
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(5)
+    per = wl.total_rows // wl.batch_size
+    rows = []
+    for i in range(wl.batch_size):
+        rows += [i * per, i * per + per - 1] + list(i * per + rng.choice(per, 4, replace=False))
+    r, ro, rl = O.cascade_rows(O.dequantize_kv(wl) if values == "fp8" else wl, rows)
+    idx = torch.as_tensor(r, device=o.device)
+    cmp(o[idx], l[idx], ro, rl)
+    assert B.cascade_device_error(clear=True) == 0
+
+
 # Per-channel scales through each kernel: key-split (16-row chunks, d 128 and
 # d 64, split prefixes, trees), pair (one-block chunks), row-split.
 CHANNEL_CASES = ["gqa_ragged", "page64_d64", "long_split", "draft_tree", "pair_16row", "rows_split"]
