@@ -290,11 +290,12 @@ def ragged_timing(B, W, torch, flush, steps=10, warmup=3):
     return out
 
 
-def streaming_read_GBps(B, torch, steps=10):
+def streaming_read_GBps(B, torch, steps=10, nbytes=1 << 30, with_ms=False):
     """A plain streaming read on the same box (the library's reference read
-    kernel over a 1 GiB buffer, another 1 GiB read between runs to evict it),
-    median of the event-timed runs."""
-    a = torch.ones(1 << 28, dtype=torch.float32, device="cuda")
+    kernel over an nbytes buffer, 1 GiB by default, another 1 GiB read between
+    runs to evict it), median of the event-timed runs (with_ms: also that
+    median time in ms)."""
+    a = torch.ones(nbytes // 4, dtype=torch.float32, device="cuda")
     b = torch.ones(1 << 28, dtype=torch.float32, device="cuda")
     sink = torch.zeros(4, dtype=torch.int32, device="cuda")
     ts = []
@@ -309,7 +310,9 @@ def streaming_read_GBps(B, torch, steps=10):
             ts.append(e0.elapsed_time(e1))
     del a, b
     torch.cuda.empty_cache()
-    return (1 << 30) / (float(np.median(ts)) * 1e-3) / 1e9
+    t = float(np.median(ts))
+    gbs = nbytes / (t * 1e-3) / 1e9
+    return (gbs, t) if with_ms else gbs
 
 
 def graph_step_timing(B, torch, flush, wl, x0, n_layers=8, steps=10, warmup=3):
@@ -632,6 +635,12 @@ def main():
         sr = streaming_read_GBps(B, torch)
         line["streaming_read_GBps"] = sr
         line["pct_streaming_read"] = 100.0 * kv_gbs / sr
+        # The same read over exactly the step's algorithmic bytes, timed like
+        # the step (events around the call): what one launch that only reads
+        # those bytes costs on this machine.
+        gbs, t_read = streaming_read_GBps(B, torch, nbytes=compulsory, with_ms=True)
+        line["same_size_read"] = {"bytes": compulsory, "ms": t_read, "GBps": gbs,
+                                  "step_over_read": float(np.median(ms)) / t_read}
     if not args.only_verify:
         other = "NHD" if args.layout == "HND" else "HND"
         print(f"bench: timing the headline verify with {other} pages", file=sys.stderr, flush=True)
